@@ -1,0 +1,201 @@
+"""cpattn: one context-parallel rank's share of causal attention on MI355X (gfx950).
+
+Thin ctypes binding over ``libcpattn.so`` (C ABI declared in ``include/cpattn.h``).
+The Python functions carry the C names and only marshal arguments: torch tensors
+become device pointers, host tables become ctypes arrays, the current torch stream
+becomes the HIP stream.  Every step of the computation runs in the HIP kernels; if
+the library is missing this package fails to import.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+# ---- constants (match include/cpattn.h) -------------------------------------------------
+OK, ERR_ARG, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+BF16, F32 = 0, 1
+MASK_NONE, MASK_CAUSAL, MASK_CAUSAL_DOC = 0, 1, 2
+PART_ZIGZAG, PART_THD = 0, 1
+
+_c_i32, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_size_t)
+
+
+class cpattn_attn_desc(ctypes.Structure):
+    _fields_ = [("dtype", _c_i32), ("hq", _c_i32), ("hkv", _c_i32), ("d", _c_i32),
+                ("scale", _c_f32), ("mask", _c_i32)]
+
+
+class cpattn_q_block(ctypes.Structure):
+    _fields_ = [("q", _c_vp), ("pos", _c_vp), ("doc", _c_vp), ("len", _c_i64)]
+
+
+class cpattn_kv_seg(ctypes.Structure):
+    _fields_ = [("k", _c_vp), ("v", _c_vp), ("pos", _c_vp), ("doc", _c_vp), ("len", _c_i64)]
+
+
+_P = ctypes.POINTER
+lib.cpattn_strerror.argtypes = [_c_i32]
+lib.cpattn_strerror.restype = ctypes.c_char_p
+lib.cpattn_version.argtypes = []
+lib.cpattn_version.restype = _c_i32
+lib.cpattn_partition.argtypes = [_c_i32, _c_i64, _c_i32, _c_i32, _P(_c_i32), _c_vp, _c_i32, _c_vp,
+                                 _c_vp, _c_i32, _P(_c_vp), _P(_c_vp), _P(_c_i64), _c_vp]
+lib.cpattn_partition.restype = _c_i32
+lib.cpattn_tile_fwd.argtypes = [_P(cpattn_attn_desc), _c_i32, _P(cpattn_q_block), _P(cpattn_kv_seg),
+                                _P(_c_vp), _P(_c_vp), _c_vp]
+lib.cpattn_tile_fwd.restype = _c_i32
+lib.cpattn_merge.argtypes = [_c_i32, _P(_c_vp), _P(_c_vp), _c_i64, _c_i32, _c_i32, _c_i32, _c_vp,
+                             _c_vp, _c_vp]
+lib.cpattn_merge.restype = _c_i32
+lib.cpattn_stream_fwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
+                                  _P(cpattn_kv_seg), _c_vp, _c_vp, _c_vp]
+lib.cpattn_stream_fwd.restype = _c_i32
+lib.cpattn_bwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
+                           _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
+lib.cpattn_bwd.restype = _c_i32
+lib.cpattn_bwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _c_i64]
+lib.cpattn_bwd_workspace_bytes.restype = _c_sz
+
+EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
+            "cpattn_merge", "cpattn_stream_fwd", "cpattn_bwd", "cpattn_bwd_workspace_bytes")
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {cpattn_strerror(status)}")
+
+
+def cpattn_strerror(status: int) -> str:
+    return lib.cpattn_strerror(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise CpattnError(status, where)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to cpattn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+_DT = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def attn_desc(hq: int, hkv: int, d: int, dtype=torch.bfloat16, mask: int = MASK_CAUSAL,
+              scale: float = 0.0) -> cpattn_attn_desc:
+    return cpattn_attn_desc(_DT[dtype] if not isinstance(dtype, int) else dtype, hq, hkv, d,
+                            float(scale), mask)
+
+
+def q_block(q, pos, doc=None) -> cpattn_q_block:
+    n = 0 if q is None else q.shape[0]
+    return cpattn_q_block(_ptr(q) if n else None, _ptr(pos) if n else None,
+                          _ptr(doc) if (n and doc is not None) else None, n)
+
+
+def kv_seg(k, v, pos, doc=None) -> cpattn_kv_seg:
+    n = 0 if k is None else k.shape[0]
+    return cpattn_kv_seg(_ptr(k) if n else None, _ptr(v) if n else None,
+                         _ptr(pos) if n else None, _ptr(doc) if (n and doc is not None) else None, n)
+
+
+def _vp_array(ptrs):
+    return (_c_vp * max(1, len(ptrs)))(*ptrs)
+
+
+# ---- the five calls ---------------------------------------------------------------------
+def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out, doc_out=None,
+                     src=(), dst=(), cu_seqlens_host=None, cu_seqlens_dev=None, stream=None):
+    """Rows of rank ``cp_rank`` (zigzag or per-document) into ``idx_out`` (+ ``doc_out``),
+    and ``dst[g][i] = src[g][idx_out[i]]`` for every tensor pair."""
+    if len(src) != len(dst):
+        raise ValueError("src and dst must pair up")
+    row_bytes = [math.prod(s.shape[1:]) * s.element_size() for s in src]
+    cu_host = None
+    n_docs = 0
+    if mode == PART_THD:
+        vals = [int(x) for x in cu_seqlens_host]
+        n_docs = len(vals) - 1
+        cu_host = (_c_i32 * len(vals))(*vals)
+    st = lib.cpattn_partition(mode, total, cp_size, cp_rank, cu_host, _ptr(cu_seqlens_dev), n_docs,
+                              _ptr(idx_out), _ptr(doc_out), len(src),
+                              _vp_array([_ptr(s) for s in src]), _vp_array([_ptr(d) for d in dst]),
+                              (_c_i64 * max(1, len(src)))(*row_bytes), _stream(stream))
+    _check(st, "cpattn_partition")
+
+
+def cpattn_tile_fwd(desc: cpattn_attn_desc, q_blocks, segs, o_parts, lse_parts, stream=None):
+    """TileAttention for every (q_blocks[e], segs[e]) edge into (o_parts[e], lse_parts[e])."""
+    n = len(q_blocks)
+    if not (len(segs) == len(o_parts) == len(lse_parts) == n):
+        raise ValueError("one q block, segment, O and LSE buffer per edge")
+    qa = (cpattn_q_block * max(1, n))(*q_blocks)
+    sa = (cpattn_kv_seg * max(1, n))(*segs)
+    st = lib.cpattn_tile_fwd(ctypes.byref(desc), n, qa, sa, _vp_array([_ptr(o) for o in o_parts]),
+                             _vp_array([_ptr(x) for x in lse_parts]), _stream(stream))
+    _check(st, "cpattn_tile_fwd")
+
+
+def cpattn_merge(o_parts, lse_parts, o_out, lse_out, stream=None):
+    """Log-sum-exp merge of fp32 partial states into (o_out, lse_out)."""
+    n = len(o_parts)
+    rows, hq, d = o_out.shape
+    out_dtype = _DT[o_out.dtype]
+    st = lib.cpattn_merge(n, _vp_array([_ptr(o) for o in o_parts]),
+                          _vp_array([_ptr(x) for x in lse_parts]), rows, hq, d, out_dtype,
+                          _ptr(o_out), _ptr(lse_out), _stream(stream))
+    _check(st, "cpattn_merge")
+
+
+def cpattn_stream_fwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o_out, lse_out, stream=None):
+    """Streaming online-softmax attention of ``q`` over ``segs`` in arrival order."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    st = lib.cpattn_stream_fwd(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o_out),
+                               _ptr(lse_out), _stream(stream))
+    _check(st, "cpattn_stream_fwd")
+
+
+def cpattn_bwd_workspace_bytes(desc: cpattn_attn_desc, q_len: int) -> int:
+    return int(lib.cpattn_bwd_workspace_bytes(ctypes.byref(desc), q_len))
+
+
+def cpattn_bwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o, lse, dout, dq, dk, dv,
+               workspace, stream=None):
+    """LSE-replay backward: dQ for the local rows, per-segment summed dK/dV."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    st = lib.cpattn_bwd(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o), _ptr(lse),
+                        _ptr(dout), _ptr(dq), _vp_array([_ptr(x) for x in dk]),
+                        _vp_array([_ptr(x) for x in dv]), _ptr(workspace),
+                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                        _stream(stream))
+    _check(st, "cpattn_bwd")

@@ -1,0 +1,269 @@
+// C ABI of libcpattn.so: argument validation and kernel launches.
+//
+// Every check the host can make without touching device memory happens before any
+// work is enqueued; on error the call returns a status and enqueues nothing.
+// Calls are asynchronous on the given stream and keep no state between calls.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/cpattn.h"
+#include "common.h"
+
+using namespace cpattn;
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const cpattn_attn_desc* d) {
+  if (d == nullptr) return CPATTN_ERR_ARG;
+  if (d->hq < 1 || d->hkv < 1) return CPATTN_ERR_ARG;
+  if (!(std::isfinite(d->scale)) || d->scale < 0.0f) return CPATTN_ERR_ARG;
+  if (d->dtype != CPATTN_BF16 && d->dtype != CPATTN_F32) return CPATTN_ERR_UNSUPPORTED;
+  if (d->d != 64 && d->d != 128) return CPATTN_ERR_UNSUPPORTED;
+  if (d->hq % d->hkv != 0) return CPATTN_ERR_UNSUPPORTED;
+  if (d->mask < CPATTN_MASK_NONE || d->mask > CPATTN_MASK_CAUSAL_DOC) return CPATTN_ERR_UNSUPPORTED;
+  return CPATTN_OK;
+}
+
+int check_qblock(const cpattn_attn_desc* d, const cpattn_q_block* q) {
+  if (q == nullptr) return CPATTN_ERR_ARG;
+  if (q->len < 0 || q->len > kMaxRows) return CPATTN_ERR_ARG;
+  if (q->len == 0) return CPATTN_OK;
+  if (q->q == nullptr || q->pos == nullptr) return CPATTN_ERR_ARG;
+  if (d->mask == CPATTN_MASK_CAUSAL_DOC && q->doc == nullptr) return CPATTN_ERR_ARG;
+  if (!aligned16(q->q)) return CPATTN_ERR_ALIGN;
+  return CPATTN_OK;
+}
+
+int check_seg(const cpattn_attn_desc* d, const cpattn_kv_seg* s) {
+  if (s->len < 0 || s->len > kMaxRows) return CPATTN_ERR_ARG;
+  if (s->len == 0) return CPATTN_OK;
+  if (s->k == nullptr || s->v == nullptr || s->pos == nullptr) return CPATTN_ERR_ARG;
+  if (d->mask == CPATTN_MASK_CAUSAL_DOC && s->doc == nullptr) return CPATTN_ERR_ARG;
+  if (!aligned16(s->k) || !aligned16(s->v)) return CPATTN_ERR_ALIGN;
+  return CPATTN_OK;
+}
+
+float eff_scale(const cpattn_attn_desc* d) {
+  return d->scale > 0.0f ? d->scale : 1.0f / std::sqrt((float)d->d);
+}
+
+int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
+void fill_common(FwdArgs& a, const cpattn_attn_desc* d) {
+  a.hq = d->hq;
+  a.hkv = d->hkv;
+  a.group = d->hq / d->hkv;
+  a.heads_per_wg = heads_per_wg(a.group);
+  a.mask = d->mask;
+  a.scale_log2 = eff_scale(d) * kLog2e;
+}
+
+SegDesc to_seg(const cpattn_kv_seg& s) {
+  SegDesc r{};
+  r.k = s.k;
+  r.v = s.v;
+  r.pos = s.pos;
+  r.doc = s.doc;
+  r.len = (int32_t)s.len;
+  return r;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cpattn_strerror(int status) {
+  switch (status) {
+    case CPATTN_OK: return "ok";
+    case CPATTN_ERR_ARG: return "invalid argument (null pointer, negative or out-of-range size or rank)";
+    case CPATTN_ERR_ALIGN: return "alignment error (length not divisible by 2*cp, bad cu_seqlens, or pointer/row not 16-byte aligned)";
+    case CPATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, mask or head grouping)";
+    case CPATTN_ERR_HIP: return "HIP runtime or launch failure";
+    case CPATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int cpattn_version(void) { return 100; }
+
+int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                     const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, int32_t n_docs,
+                     int32_t* idx_out, int32_t* doc_out, int32_t n_gather, const void* const* src,
+                     void* const* dst, const int64_t* row_bytes, void* stream) {
+  if (mode != CPATTN_PART_ZIGZAG && mode != CPATTN_PART_THD) return CPATTN_ERR_ARG;
+  if (total < 0 || total > INT32_MAX || cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size)
+    return CPATTN_ERR_ARG;
+  if (n_gather < 0 || n_gather > 8) return CPATTN_ERR_ARG;
+  if (total % (2 * (int64_t)cp_size) != 0) return CPATTN_ERR_ALIGN;
+  if (mode == CPATTN_PART_THD) {
+    if (cu_seqlens_host == nullptr || cu_seqlens_dev == nullptr || n_docs < 1) return CPATTN_ERR_ARG;
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_docs] != total) return CPATTN_ERR_ALIGN;
+    for (int k = 0; k < n_docs; ++k) {
+      const int64_t len = (int64_t)cu_seqlens_host[k + 1] - cu_seqlens_host[k];
+      if (len < 0 || len % (2 * (int64_t)cp_size) != 0) return CPATTN_ERR_ALIGN;
+    }
+  }
+  if (total > 0 && idx_out == nullptr) return CPATTN_ERR_ARG;
+  if (n_gather > 0 && (src == nullptr || dst == nullptr || row_bytes == nullptr)) return CPATTN_ERR_ARG;
+  for (int g = 0; g < n_gather; ++g) {
+    if (row_bytes[g] <= 0 || row_bytes[g] > ((int64_t)1 << 24)) return CPATTN_ERR_ARG;
+    if (row_bytes[g] % 16 != 0) return CPATTN_ERR_ALIGN;
+    if (total > 0 && (src[g] == nullptr || dst[g] == nullptr)) return CPATTN_ERR_ARG;
+    if (!aligned16(src[g]) || !aligned16(dst[g])) return CPATTN_ERR_ALIGN;
+  }
+  if (total == 0) return CPATTN_OK;
+  return hip_status(launch_partition(mode, total, cp_size, cp_rank, cu_seqlens_dev, n_docs, idx_out,
+                                     doc_out, n_gather, src, dst, row_bytes,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cpattn_tile_fwd(const cpattn_attn_desc* desc, int32_t n_edges, const cpattn_q_block* q_blocks,
+                    const cpattn_kv_seg* segs, float* const* o_parts, float* const* lse_parts,
+                    void* stream) {
+  int st = check_desc(desc);
+  if (st != CPATTN_OK) return st;
+  if (n_edges < 0) return CPATTN_ERR_ARG;
+  if (n_edges == 0) return CPATTN_OK;
+  if (q_blocks == nullptr || segs == nullptr || o_parts == nullptr || lse_parts == nullptr)
+    return CPATTN_ERR_ARG;
+  for (int e = 0; e < n_edges; ++e) {
+    if ((st = check_qblock(desc, &q_blocks[e])) != CPATTN_OK) return st;
+    if ((st = check_seg(desc, &segs[e])) != CPATTN_OK) return st;
+    if (q_blocks[e].len > 0) {
+      if (o_parts[e] == nullptr || lse_parts[e] == nullptr) return CPATTN_ERR_ARG;
+      if (!aligned16(o_parts[e])) return CPATTN_ERR_ALIGN;
+    }
+  }
+  FwdArgs a{};
+  fill_common(a, desc);
+  int e = 0;
+  while (e < n_edges) {
+    a.n_jobs = 0;
+    for (; e < n_edges && a.n_jobs < kMaxJobs; ++e) {
+      if (q_blocks[e].len == 0) continue;
+      const int j = a.n_jobs++;
+      a.segs[j] = to_seg(segs[e]);
+      JobDesc& jb = a.jobs[j];
+      jb.q = q_blocks[e].q;
+      jb.pos = q_blocks[e].pos;
+      jb.doc = q_blocks[e].doc;
+      jb.o = o_parts[e];
+      jb.lse = lse_parts[e];
+      jb.len = (int32_t)q_blocks[e].len;
+      jb.seg_begin = j;
+      jb.seg_end = j + 1;
+    }
+    if (a.n_jobs == 0) continue;
+    st = hip_status(launch_fwd(a, desc->d, desc->dtype, true, reinterpret_cast<hipStream_t>(stream)));
+    if (st != CPATTN_OK) return st;
+  }
+  return CPATTN_OK;
+}
+
+int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* const* lse_parts,
+                 int64_t rows, int32_t hq, int32_t d, int32_t out_dtype, void* o_out, float* lse_out,
+                 void* stream) {
+  if (n_parts < 1 || n_parts > 64 || rows < 0 || rows > kMaxRows || hq < 1) return CPATTN_ERR_ARG;
+  if (d < 4 || d > 256 || d % 4 != 0) return CPATTN_ERR_UNSUPPORTED;
+  if (out_dtype != CPATTN_BF16 && out_dtype != CPATTN_F32) return CPATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return CPATTN_OK;
+  if (o_parts == nullptr || lse_parts == nullptr || o_out == nullptr || lse_out == nullptr)
+    return CPATTN_ERR_ARG;
+  for (int j = 0; j < n_parts; ++j) {
+    if (o_parts[j] == nullptr || lse_parts[j] == nullptr) return CPATTN_ERR_ARG;
+    if (!aligned16(o_parts[j])) return CPATTN_ERR_ALIGN;
+  }
+  if (!aligned16(o_out)) return CPATTN_ERR_ALIGN;
+  return hip_status(launch_merge(n_parts, o_parts, lse_parts, rows, hq, d, out_dtype, o_out, lse_out,
+                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* stream) {
+  int st = check_desc(desc);
+  if (st != CPATTN_OK) return st;
+  if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
+  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return CPATTN_ERR_ARG;
+  for (int s = 0; s < n_segs; ++s)
+    if ((st = check_seg(desc, &segs[s])) != CPATTN_OK) return st;
+  if (q->len == 0) return CPATTN_OK;
+  if (o_out == nullptr || lse_out == nullptr) return CPATTN_ERR_ARG;
+  if (!aligned16(o_out)) return CPATTN_ERR_ALIGN;
+  FwdArgs a{};
+  fill_common(a, desc);
+  for (int s = 0; s < n_segs; ++s) a.segs[s] = to_seg(segs[s]);
+  a.n_jobs = 1;
+  JobDesc& jb = a.jobs[0];
+  jb.q = q->q;
+  jb.pos = q->pos;
+  jb.doc = q->doc;
+  jb.o = o_out;
+  jb.lse = lse_out;
+  jb.len = (int32_t)q->len;
+  jb.seg_begin = 0;
+  jb.seg_end = n_segs;
+  return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, int64_t q_len) {
+  if (desc == nullptr || q_len < 0 || desc->hq < 1) return 0;
+  const size_t bytes = (size_t)q_len * (size_t)desc->hq * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+               const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout, float* dq,
+               float* const* dk, float* const* dv, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_desc(desc);
+  if (st != CPATTN_OK) return st;
+  if (desc->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
+  if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
+  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr || dk == nullptr || dv == nullptr)
+    return CPATTN_ERR_ARG;
+  for (int s = 0; s < n_segs; ++s) {
+    if ((st = check_seg(desc, &segs[s])) != CPATTN_OK) return st;
+    if (segs[s].len > 0) {
+      if (dk[s] == nullptr || dv[s] == nullptr) return CPATTN_ERR_ARG;
+      if (!aligned16(dk[s]) || !aligned16(dv[s])) return CPATTN_ERR_ALIGN;
+    }
+  }
+  if (q->len > 0) {
+    if (o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr) return CPATTN_ERR_ARG;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(dq)) return CPATTN_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < cpattn_bwd_workspace_bytes(desc, q->len))
+      return CPATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CPATTN_ERR_ALIGN;
+  }
+  BwdArgs a{};
+  for (int s = 0; s < n_segs; ++s) {
+    a.segs[s] = to_seg(segs[s]);
+    a.dk[s] = dk[s];
+    a.dv[s] = dv[s];
+  }
+  a.q = q->q;
+  a.qpos = q->pos;
+  a.qdoc = q->doc;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.delta = reinterpret_cast<float*>(workspace);
+  a.q_len = (int32_t)q->len;
+  a.n_segs = n_segs;
+  a.hq = desc->hq;
+  a.hkv = desc->hkv;
+  a.group = desc->hq / desc->hkv;
+  a.mask = desc->mask;
+  a.scale = eff_scale(desc);
+  a.scale_log2 = a.scale * kLog2e;
+  return hip_status(launch_bwd(a, desc->d, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

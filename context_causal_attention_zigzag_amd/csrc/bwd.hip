@@ -1,0 +1,424 @@
+// LSE-replay backward of one rank's share.
+//
+// "上下文并行：一条序列跨卡，仍算同一个目标", sections 01-02: each KV block is
+// replayed against the local queries; the block's probabilities are rebuilt from
+// the saved full-row log-sum-exp, P_ij = exp(S_ij - lambda_i); the softmax
+// derivative gives dS_ij = P_ij (dP_ij - D_i) with dP = G V^T and D_i = G_i . O_i;
+// then dQ_i += dS_ij K_j / sqrt(d), dK_j += dS_ij Q_i / sqrt(d), dV_j += P_ij G_i,
+// and the K/V gradients of every query are summed at the owner of the keys.
+//
+// Kernel layout (gfx950, v_mfma_f32_32x32x16_bf16):
+//  - preprocess: D_i = rowsum(dO * O) in fp32 into the workspace, dQ zeroed.
+//  - main: one work-group of 4 waves per (KV segment, 128-key tile, kv head); wave w
+//    keeps keys 32w..32w+31 (K and V rows) in registers as B operands and owns their
+//    dK/dV accumulators, so the per-owner sums over all local queries and all query
+//    heads of the group finish in registers and are stored once (no atomics).
+//    The work-group walks the visible 32-row query tiles: Q and dO are staged in LDS
+//    both row-major (A operands of S = Q K^T and dP = dO V^T) and transposed with the
+//    contraction order of a C-layout B operand (A operands of dV^T = dO^T P and
+//    dK^T = Q^T dS), so P and dS feed the matrix cores straight from the accumulators.
+//    dS goes through LDS once more for dQ = dS K, computed per 32-dim slice by each
+//    wave and added to the fp32 dQ with coalesced atomics (128-byte rows).
+//  - one barrier per query tile; the next tile's global loads overlap the current
+//    tile's matrix work.
+#include "common.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBKV = 128;  // keys per work-group (32 per wave)
+constexpr int kBQ = 32;    // query rows per step
+constexpr int kPosPad = 0x7fffffff;
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restrict__ o,
+                                                            const bf16* __restrict__ dout,
+                                                            float* __restrict__ delta,
+                                                            float* __restrict__ dq, int64_t pairs) {
+  constexpr int kTpp = D / 8;  // threads per (row, head), 8 elements each
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t pair = gid / kTpp;
+  const int c = (int)(gid % kTpp);
+  float s = 0.0f;
+  if (pair < pairs) {
+    const int64_t off = pair * D + c * 8;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + off);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(dq + off) = z;
+    *reinterpret_cast<f32x4*>(dq + off + 4) = z;
+  }
+#pragma unroll
+  for (int w = kTpp / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, kTpp);
+  if (pair < pairs && c == 0) delta[pair] = s;
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdSmem {
+  static constexpr int kRS = D + 8;     // row-major stride (Q, dO)
+  static constexpr int kTS = kBQ + 8;   // transposed stride (Q^T, dO^T)
+  static constexpr int kSS = kBKV + 8;  // dS and K^T stride
+  bf16 qs[2][kBQ * kRS];
+  bf16 dos[2][kBQ * kRS];
+  bf16 qt[2][D * kTS];
+  bf16 dot[2][D * kTS];
+  float lse2[2][kBQ];
+  float delta[2][kBQ];
+  int32_t qpos[2][kBQ];
+  int32_t qdoc[2][kBQ];
+  bf16 ds[2][kBQ * kSS];
+  bf16 kt[D * kSS];
+};
+
+struct QStageRegs {
+  u32x4 x[4];  // 4 rows x 8 dims of Q (threads 0..127) or dO (threads 128..255)
+  float lse2, delta;
+  int32_t pos, doc;
+};
+
+__device__ __forceinline__ void load_qstage(QStageRegs& r, const BwdArgs& a, int head, int r0, int D,
+                                            int tid) {
+  const int half = tid >> 7;       // 0: Q, 1: dO
+  const int u = tid & 127;
+  const int m = u & 7, dc = u >> 3;  // rows 4m..4m+3, dims dc*8..+7
+  if (dc < D / 8) {
+    const bf16* base = reinterpret_cast<const bf16*>(half ? a.dout : a.q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * m + i;
+      if (row < a.q_len)
+        r.x[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8);
+      else
+        r.x[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  if (tid < kBQ) {
+    const int row = r0 + tid;
+    if (row < a.q_len) {
+      const float l = a.lse[(int64_t)row * a.hq + head];
+      r.lse2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // a row with no key adds nothing
+      r.delta = a.delta[(int64_t)row * a.hq + head];
+      r.pos = a.qpos[row];
+      r.doc = a.mask == kMaskCausalDoc ? a.qdoc[row] : 0;
+    } else {
+      r.lse2 = __builtin_inff();
+      r.delta = 0.0f;
+      r.pos = -kPosPad - 1;  // sees nothing
+      r.doc = 0;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs& r, int tid) {
+  constexpr int kRS = BwdSmem<D>::kRS, kTS = BwdSmem<D>::kTS;
+  const int half = tid >> 7;
+  const int u = tid & 127;
+  const int m = u & 7, dc = u >> 3;
+  if (dc < D / 8) {
+    bf16* rowm = half ? sm.dos[buf] : sm.qs[buf];
+    bf16* trn = half ? sm.dot[buf] : sm.qt[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&rowm[(4 * m + i) * kRS + dc * 8]) = r.x[i];
+    const int col = perm16(4 * m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (r.x[0][w] >> sh) & 0xffffu, x1 = (r.x[1][w] >> sh) & 0xffffu;
+      const uint32_t x2 = (r.x[2][w] >> sh) & 0xffffu, x3 = (r.x[3][w] >> sh) & 0xffffu;
+      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
+      *reinterpret_cast<u32x2*>(&trn[(dc * 8 + e) * kTS + col]) = packed;
+    }
+  }
+  if (tid < kBQ) {
+    sm.lse2[buf][tid] = r.lse2;
+    sm.delta[buf][tid] = r.delta;
+    sm.qpos[buf][tid] = r.pos;
+    sm.qdoc[buf][tid] = r.doc;
+  }
+}
+
+struct QRef {
+  int hh;  // head within the kv group
+  int qt;  // query tile
+};
+
+// Next visible (head, query tile) at or after (hh, qt) for the key range [kmin, kmax].
+__device__ __forceinline__ QRef next_qtile(const BwdArgs& a, int hh, int qt, int n_qt, int kmin,
+                                           int kmax, int kdmin, int kdmax) {
+  for (; hh < a.group; ++hh, qt = 0) {
+    for (; qt < n_qt; ++qt) {
+      const int r0 = qt * kBQ, r1 = min(a.q_len, r0 + kBQ) - 1;
+      int qdmin = 0, qdmax = 0;
+      if (a.mask == kMaskCausalDoc) {
+        qdmin = a.qdoc[r0];
+        qdmax = a.qdoc[r1];
+      }
+      if (classify(a.mask, a.qpos[r0], a.qpos[r1], qdmin, qdmax, kmin, kmax, kdmin, kdmax) != kTileEmpty)
+        return {hh, qt};
+    }
+  }
+  return {-1, 0};
+}
+
+template <int D, bool MASKED>
+__device__ __forceinline__ void bwd_step(BwdSmem<D>& sm, int buf, const bf16x8 (&kf)[D / 16],
+                                         const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
+                                         f32x16 (&dv)[D / 32], int kpos, int kdoc, bool key_ok,
+                                         int mask, float scale, float scale_log2, int wave, int lane) {
+  constexpr int kRS = BwdSmem<D>::kRS, kTS = BwdSmem<D>::kTS, kSS = BwdSmem<D>::kSS;
+  const int r = lane & 31, h = lane >> 5;
+  f32x16 s = {}, dp = {};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qs[buf][r * kRS + ds * 16 + h * 8]);
+    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dos[buf][r * kRS + ds * 16 + h * 8]);
+    s = mfma32x32x16(aq, kf[ds], s);
+    dp = mfma32x32x16(ao, vf[ds], dp);
+  }
+  bf16x8 pf[2], dsf[2];
+  bf16* dsrow = sm.ds[buf];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int q0 = 8 * g + 4 * h;
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][q0]);
+    const f32x4 dl = *reinterpret_cast<const f32x4*>(&sm.delta[buf][q0]);
+    int4 qp = {0, 0, 0, 0}, qd = {0, 0, 0, 0};
+    if (MASKED) {
+      qp = *reinterpret_cast<const int4*>(&sm.qpos[buf][q0]);
+      if (mask == kMaskCausalDoc) qd = *reinterpret_cast<const int4*>(&sm.qdoc[buf][q0]);
+    }
+    const int qpa[4] = {qp.x, qp.y, qp.z, qp.w};
+    const int qda[4] = {qd.x, qd.y, qd.z, qd.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int a = 4 * g + e;
+      float p = fast_exp2(s[a] * scale_log2 - l2[e]);
+      if (MASKED) {
+        bool vis = key_ok;
+        if (mask != kMaskNone) vis = vis && kpos <= qpa[e];
+        if (mask == kMaskCausalDoc) vis = vis && kdoc == qda[e];
+        p = vis ? p : 0.0f;
+      }
+      const float dsv = p * (dp[a] - dl[e]) * scale;
+      pf[a >> 3][a & 7] = (bf16)p;
+      const bf16 dsb = (bf16)dsv;
+      dsf[a >> 3][a & 7] = dsb;
+      dsrow[(q0 + e) * kSS + wave * 32 + r] = dsb;
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dot[buf][(db * 32 + r) * kTS + sl * 16 + h * 8]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][(db * 32 + r) * kTS + sl * 16 + h * 8]);
+      dv[db] = mfma32x32x16(ao, pf[sl], dv[db]);
+      dk[db] = mfma32x32x16(aq, dsf[sl], dk[db]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
+  __shared__ BwdSmem<D> sm;
+  constexpr int kSS = BwdSmem<D>::kSS;
+  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
+  if (logical >= a.total_wgs) return;
+  int s = 0;
+  while (s + 1 < a.n_segs && a.seg_wg_begin[s + 1] <= logical) ++s;
+  const SegDesc& sg = a.segs[s];
+  const int n_kt = (sg.len + kBKV - 1) / kBKV;
+  const int local = logical - a.seg_wg_begin[s];
+  const int kvh = local / n_kt;
+  const int kt = local - kvh * n_kt;
+  const int k0 = kt * kBKV, k1 = min(sg.len, k0 + kBKV);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, h = lane >> 5;
+  const int mask = a.mask;
+  const bf16* kb = reinterpret_cast<const bf16*>(sg.k);
+  const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
+
+  // this wave's keys as B operands (lane: key 32*wave + r, dims 16*ds + 8*h .. +7)
+  const int mykey = k0 + wave * 32 + r;
+  const bool key_ok = mykey < k1;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    if (key_ok) {
+      const int64_t off = ((int64_t)mykey * a.hkv + kvh) * D + ds * 16 + h * 8;
+      kf[ds] = *reinterpret_cast<const bf16x8*>(kb + off);
+      vf[ds] = *reinterpret_cast<const bf16x8*>(vb + off);
+    } else {
+      kf[ds] = bf16x8{};
+      vf[ds] = bf16x8{};
+    }
+  }
+  const int kpos = key_ok ? sg.pos[mykey] : kPosPad;
+  const int kdoc = (key_ok && mask == kMaskCausalDoc) ? sg.doc[mykey] : 0;
+
+  // K^T of the whole work-group tile in LDS (natural key order), for dQ = dS K
+  for (int u = tid; u < (kBKV / 4) * (D / 8); u += kThreads) {
+    const int m = u % (kBKV / 4), dc = u / (kBKV / 4);
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = k0 + 4 * m + i;
+      u32x4 x = {0, 0, 0, 0};
+      if (key < k1) x = *reinterpret_cast<const u32x4*>(kb + ((int64_t)key * a.hkv + kvh) * D + dc * 8);
+      w[i][0] = x[0];
+      w[i][1] = x[1];
+      w[i][2] = x[2];
+      w[i][3] = x[3];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wi = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (w[0][wi] >> sh) & 0xffffu, x1 = (w[1][wi] >> sh) & 0xffffu;
+      const uint32_t x2 = (w[2][wi] >> sh) & 0xffffu, x3 = (w[3][wi] >> sh) & 0xffffu;
+      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
+      *reinterpret_cast<u32x2*>(&sm.kt[(dc * 8 + e) * kSS + 4 * m]) = packed;
+    }
+  }
+
+  // key ranges of the work-group and of this wave (non-decreasing positions)
+  const int kmin = sg.pos[k0], kmax = sg.pos[k1 - 1];
+  int kdmin = 0, kdmax = 0;
+  if (mask == kMaskCausalDoc) {
+    kdmin = sg.doc[k0];
+    kdmax = sg.doc[k1 - 1];
+  }
+  const int wk0 = k0 + wave * 32, wk1 = min(k1, wk0 + 32);
+  const bool wave_keys = wk0 < wk1;
+  int wkmin = 0, wkmax = 0, wkdmin = 0, wkdmax = 0;
+  if (wave_keys) {
+    wkmin = sg.pos[wk0];
+    wkmax = sg.pos[wk1 - 1];
+    if (mask == kMaskCausalDoc) {
+      wkdmin = sg.doc[wk0];
+      wkdmax = sg.doc[wk1 - 1];
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int n_qt = (a.q_len + kBQ - 1) / kBQ;
+  QRef cur = next_qtile(a, 0, 0, n_qt, kmin, kmax, kdmin, kdmax);
+  if (cur.hh >= 0) {
+    QStageRegs qr;
+    load_qstage(qr, a, kvh * a.group + cur.hh, cur.qt * kBQ, D, tid);
+    store_qstage<D>(sm, 0, qr, tid);
+    __syncthreads();
+    int buf = 0;
+    while (true) {
+      QRef nxt = next_qtile(a, cur.hh, cur.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
+      if (nxt.hh >= 0) load_qstage(qr, a, kvh * a.group + nxt.hh, nxt.qt * kBQ, D, tid);
+      const int head = kvh * a.group + cur.hh;
+      const int r0 = cur.qt * kBQ, r1 = min(a.q_len, r0 + kBQ);
+      // wave-level class of (query tile, this wave's keys)
+      int wcls = kTileEmpty;
+      if (wave_keys) {
+        int qdmin = 0, qdmax = 0;
+        if (mask == kMaskCausalDoc) {
+          qdmin = a.qdoc[r0];
+          qdmax = a.qdoc[r1 - 1];
+        }
+        wcls = classify(mask, a.qpos[r0], a.qpos[r1 - 1], qdmin, qdmax, wkmin, wkmax, wkdmin, wkdmax);
+        if (wcls == kTileFull && (wk1 - wk0 < 32 || r1 - r0 < kBQ)) wcls = kTilePartial;
+      }
+      if (wcls == kTileFull)
+        bwd_step<D, false>(sm, buf, kf, vf, dk, dv, kpos, kdoc, key_ok, mask, a.scale, a.scale_log2, wave, lane);
+      else if (wcls == kTilePartial)
+        bwd_step<D, true>(sm, buf, kf, vf, dk, dv, kpos, kdoc, key_ok, mask, a.scale, a.scale_log2, wave, lane);
+      else {
+        bf16* dsrow = sm.ds[buf];
+#pragma unroll
+        for (int q = 0; q < kBQ / 2; ++q) dsrow[(2 * q + h) * kSS + wave * 32 + r] = (bf16)0.0f;
+      }
+      if (nxt.hh >= 0) store_qstage<D>(sm, buf ^ 1, qr, tid);
+      __syncthreads();
+      // dQ[q][32*wave .. +31] += dS[q][:] K[:][...]  (scale already folded into dS)
+      if (wave * 32 < D) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < kBKV / 16; ++ks) {
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sm.ds[buf][r * kSS + ks * 16 + h * 8]);
+          const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.kt[(wave * 32 + r) * kSS + ks * 16 + h * 8]);
+          acc = mfma32x32x16(ad, bk, acc);
+        }
+#pragma unroll
+        for (int aa = 0; aa < 16; ++aa) {
+          const int row = r0 + 8 * (aa >> 2) + 4 * h + (aa & 3);
+          if (row < r1)
+            unsafeAtomicAdd(&a.dq[((int64_t)row * a.hq + head) * D + wave * 32 + r], acc[aa]);
+        }
+      }
+      if (nxt.hh < 0) break;
+      buf ^= 1;
+      cur = nxt;
+    }
+  }
+
+  // per-owner sums: this wave's 32 keys, all local queries and all heads of the group
+  if (key_ok) {
+    float* dkp = a.dk[s];
+    float* dvp = a.dv[s];
+    const int64_t rowoff = ((int64_t)mykey * a.hkv + kvh) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * h;
+        const f32x4 vk = {dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+        const f32x4 vv = {dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dkp + rowoff + d0) = vk;
+        *reinterpret_cast<f32x4*>(dvp + rowoff + d0) = vv;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(BwdArgs& a, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.q_len * a.hq;
+  if (pairs > 0) {
+    const int64_t threads = pairs * (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(a.o),
+                       reinterpret_cast<const bf16*>(a.dout), a.delta, a.dq, pairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int total = 0;
+  for (int s = 0; s < a.n_segs; ++s) {
+    a.seg_wg_begin[s] = total;
+    total += ((a.segs[s].len + kBKV - 1) / kBKV) * a.hkv;
+  }
+  a.seg_wg_begin[a.n_segs] = total;
+  a.total_wgs = total;
+  a.padded_wgs = (total + 7) & ~7;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& args, int d, hipStream_t stream) {
+  BwdArgs a = args;
+  if (d == 64) return launch_bwd_d<64>(a, stream);
+  return launch_bwd_d<128>(a, stream);
+}
+
+}  // namespace cpattn

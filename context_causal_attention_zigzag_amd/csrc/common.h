@@ -1,0 +1,161 @@
+// Device-side building blocks shared by the cpattn kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, one wave64):
+//   A (32 x 16): lane l holds row (l % 32), contraction elements 8*(l / 32) .. +7
+//   B (16 x 32): lane l holds column (l % 32), contraction elements 8*(l / 32) .. +7
+//   C (32 x 32): lane l holds column (l % 32); accumulator a holds row
+//                8*(a / 4) + 4*(l / 32) + (a % 4),  a = 0..15
+// A C-layout matrix therefore already sits in B-operand form for a product that
+// contracts over its rows, provided the other operand enumerates the contraction
+// index in the same order: within each 16-row slice, lane half h and element e
+// name row  perm16(h, e) = 8*(e / 4) + 4*h + (e % 4).  Operands staged in LDS for
+// such products are stored with that permutation (swap of index bits 2 and 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kWave = 64;
+
+// Mask kinds (values match the public CPATTN_MASK_* constants).
+constexpr int kMaskNone = 0;
+constexpr int kMaskCausal = 1;
+constexpr int kMaskCausalDoc = 2;
+
+// Tile classes for one (query tile, key tile) pair.
+constexpr int kTileEmpty = 0;
+constexpr int kTileFull = 1;
+constexpr int kTilePartial = 2;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
+
+// Swap of bits 2 and 3 inside each group of 16 (the contraction order of a C-layout
+// B operand, see the header comment).
+__device__ __forceinline__ int perm16(int k) {
+  return (k & ~15) | ((k >> 2) & 1) << 3 | ((k >> 3) & 1) << 2 | (k & 3);
+}
+
+// Classification of a query tile [qmin, qmax] (document range [qdmin, qdmax])
+// against a key tile [kmin, kmax] ([kdmin, kdmax]); positions and documents are
+// non-decreasing inside tiles, so the extremes are the first and last entries.
+__device__ __forceinline__ int classify(int mask, int qmin, int qmax, int qdmin, int qdmax,
+                                        int kmin, int kmax, int kdmin, int kdmax) {
+  if (mask == kMaskNone) return kTileFull;
+  if (kmin > qmax) return kTileEmpty;
+  if (mask == kMaskCausalDoc) {
+    if (kdmax < qdmin || kdmin > qdmax) return kTileEmpty;
+    if (kmax <= qmin && qdmin == qdmax && kdmin == kdmax && qdmin == kdmin) return kTileFull;
+    return kTilePartial;
+  }
+  return kmax <= qmin ? kTileFull : kTilePartial;
+}
+
+// Work-group order remap: the dispatcher hands consecutive work-groups to the 8
+// XCDs in turn, so logical work item (x * per + i) runs on XCD x; neighbours in
+// logical order (same heads, adjacent query tiles) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int padded_n) {
+  const int per = padded_n >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel-argument tables (passed by value).
+constexpr int kMaxSegs = 32;
+constexpr int kMaxJobs = 24;
+
+struct SegDesc {
+  const void* k;
+  const void* v;
+  const int32_t* pos;
+  const int32_t* doc;
+  int32_t len;
+  int32_t pad_;
+};
+
+struct JobDesc {
+  const void* q;
+  const int32_t* pos;
+  const int32_t* doc;
+  void* o;        // final output (input dtype) or fp32 partial output
+  float* lse;     // [len, hq]
+  int32_t len;
+  int32_t seg_begin;
+  int32_t seg_end;
+  int32_t wg_begin;  // first logical work-group of this job
+};
+
+struct FwdArgs {
+  SegDesc segs[kMaxSegs];
+  JobDesc jobs[kMaxJobs];
+  int32_t n_jobs;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;         // hq / hkv
+  int32_t heads_per_wg;  // query heads sharing one work-group (divides group)
+  int32_t mask;
+  float scale_log2;      // softmax scale times log2(e)
+  int32_t total_wgs;     // logical work-groups
+  int32_t padded_wgs;    // grid size (multiple of 8)
+};
+
+struct BwdArgs {
+  SegDesc segs[kMaxSegs];
+  const void* q;
+  const int32_t* qpos;
+  const int32_t* qdoc;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk[kMaxSegs];
+  float* dv[kMaxSegs];
+  float* delta;          // workspace [q_len, hq]: rowsum(dO * O)
+  int32_t q_len;
+  int32_t n_segs;
+  int32_t seg_wg_begin[kMaxSegs + 1];
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  int32_t mask;
+  float scale;
+  float scale_log2;
+  int32_t total_wgs;
+  int32_t padded_wgs;
+};
+
+// Host-side launchers (defined in the .hip files).
+hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int32_t* cu_dev,
+                            int n_docs, int32_t* idx, int32_t* doc, int n_gather,
+                            const void* const* src, void* const* dst, const int64_t* row_bytes,
+                            hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool partial_out, hipStream_t stream);
+hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                        int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
+                        hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,493 @@
+// Forward attention kernels: TileAttention over task-graph edges and the
+// streaming online-softmax form over KV segments in arrival order.
+//
+// Both forms run the same per-query-tile loop: for every KV tile (64 keys) that the
+// query tile can see, the running row state (m, l, a) is updated as written in
+// "上下文并行：一条序列跨卡，仍算同一个目标", section 02 (m' = max(m, max S),
+// c = e^{m-m'}, l' = c l + sum e^{S-m'}, a' = c a + sum e^{S-m'} V), and at the end
+// O = a / l and LSE = m + log l.  A job is either one edge of the Q-KV task graph
+// ("Context Parallelism (CP)", section 2.1: output normalised inside its segment,
+// fp32 O_ij and L_ij for a later merge) or one query block with its list of segments
+// in ring arrival order (ring-attention page, section 2: final O in the input dtype).
+//
+// bf16 kernel (gfx950 matrix cores), per work-group of 4 waves, 32 query rows per wave:
+//  - S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A operand and the
+//    wave's queries, held in registers for the whole loop, the B operand.  Each lane
+//    then owns one query row (column of S^T), so row max / row sum are in-lane plus
+//    one exchange between the two lane halves.
+//  - P^T (bf16, converted in place from the accumulators) is directly the B operand
+//    of O^T += V^T P^T; V^T is staged in LDS with the contraction order that layout
+//    implies (common.h), so every operand read is one 16-byte LDS load.
+//  - The scale is applied to the fp32 scores (folded with log2 e into exp2).
+//  - The running maximum is only moved when a new score exceeds it by more than
+//    2^8 (probabilities stay <= 256, exact in fp32 and bf16 range), so the O rescale
+//    is skipped on almost every tile.
+//  - Tiles are classified per work-group (skip empty tiles entirely) and per wave
+//    (fully visible tiles run without mask arithmetic).
+//  - K/V tiles are double-buffered in LDS; the next visible tile's global loads are
+//    in flight while the current tile computes; one barrier per tile.
+//
+// fp32 kernel: a plain VALU kernel, one thread per (query row, head), used for fp32
+// inputs (exact fp32 arithmetic, no bf16 rounding anywhere).
+#include "common.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kBK = 64;         // keys per KV tile
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kRowsPerWave = 32;
+constexpr float kTau = 8.0f;    // lazy-rescale threshold (log2 units)
+constexpr int kPosPad = 0x7fffffff;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int kKS = D + 8;     // K row stride (elements), 16-byte pad
+  static constexpr int kVS = kBK + 8;   // V^T row stride (elements), 16-byte pad
+  bf16 k[2][kBK * kKS];
+  bf16 vt[2][D * kVS];
+  int32_t kpos[2][kBK];
+  int32_t kdoc[2][kBK];
+};
+
+struct TileRef {
+  int seg;
+  int tile;
+};
+
+// Next KV tile at or after (s, t) that the query range can see; seg = -1 if none.
+__device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int s, int t, int qmin,
+                                             int qmax, int qdmin, int qdmax) {
+  for (; s < seg_end; ++s, t = 0) {
+    const SegDesc& sg = a.segs[s];
+    const int nt = (sg.len + kBK - 1) / kBK;
+    for (; t < nt; ++t) {
+      const int k0 = t * kBK;
+      const int k1 = min(sg.len, k0 + kBK) - 1;
+      int kdmin = 0, kdmax = 0;
+      if (a.mask == kMaskCausalDoc) {
+        kdmin = sg.doc[k0];
+        kdmax = sg.doc[k1];
+      }
+      const int cls = classify(a.mask, qmin, qmax, qdmin, qdmax, sg.pos[k0], sg.pos[k1], kdmin, kdmax);
+      if (cls != kTileEmpty) return {s, t};
+    }
+  }
+  return {-1, 0};
+}
+
+template <int D>
+struct TileRegs {
+  static constexpr int kKChunks = kBK * D / 8 / kThreads;  // 16-byte K chunks per thread
+  u32x4 k[kKChunks];
+  u32x4 v[4];
+  int32_t pos;
+  int32_t doc;
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const SegDesc& sg, int tile, int kvh,
+                                          int hkv, int mask, int tid) {
+  const int k0 = tile * kBK;
+  const int klen = min(kBK, sg.len - k0);
+  const bf16* kb = reinterpret_cast<const bf16*>(sg.k);
+  const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
+  constexpr int kCPK = D / 8;  // chunks per key row
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kKChunks; ++i) {
+    const int c = tid + i * kThreads;
+    const int key = c / kCPK, dc = c % kCPK;
+    if (key < klen)
+      r.k[i] = *reinterpret_cast<const u32x4*>(kb + ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8);
+    else
+      r.k[i] = u32x4{0, 0, 0, 0};
+  }
+  // V: unit = (group of 4 consecutive keys, 8 consecutive dims)
+  const int m = tid & 15, dc = tid >> 4;
+  if (dc < D / 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 4 * m + i;
+      if (key < klen)
+        r.v[i] = *reinterpret_cast<const u32x4*>(vb + ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8);
+      else
+        r.v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  if (tid < kBK) {
+    r.pos = tid < klen ? sg.pos[k0 + tid] : kPosPad;
+    r.doc = (mask == kMaskCausalDoc && tid < klen) ? sg.doc[k0 + tid] : 0;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(FwdSmem<D>& sm, int buf, const TileRegs<D>& r, int tid) {
+  constexpr int kCPK = D / 8;
+  constexpr int kKS = FwdSmem<D>::kKS, kVS = FwdSmem<D>::kVS;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kKChunks; ++i) {
+    const int c = tid + i * kThreads;
+    const int key = c / kCPK, dc = c % kCPK;
+    *reinterpret_cast<u32x4*>(&sm.k[buf][key * kKS + dc * 8]) = r.k[i];
+  }
+  const int m = tid & 15, dc = tid >> 4;
+  if (dc < D / 8) {
+    const int col = perm16(4 * m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // dim dc*8+e of keys 4m..4m+3 -> four consecutive V^T columns
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (r.v[0][w] >> sh) & 0xffffu, x1 = (r.v[1][w] >> sh) & 0xffffu;
+      const uint32_t x2 = (r.v[2][w] >> sh) & 0xffffu, x3 = (r.v[3][w] >> sh) & 0xffffu;
+      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * kVS + col]) = packed;
+    }
+  }
+  if (tid < kBK) {
+    sm.kpos[buf][tid] = r.pos;
+    sm.kdoc[buf][tid] = r.doc;
+  }
+}
+
+// One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
+template <int D, bool MASKED>
+__device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf16* __restrict__ vt,
+                                          const int32_t* kpos, const int32_t* kdoc, int klen,
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                          float& m, float& l, int qpos, int qdoc, int mask,
+                                          float scale_log2, int lane) {
+  constexpr int kKS = FwdSmem<D>::kKS, kVS = FwdSmem<D>::kVS;
+  const int r = lane & 31, h = lane >> 5;
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + r * kKS + ds * 16 + h * 8);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + (32 + r) * kKS + ds * 16 + h * 8);
+    s0 = mfma32x32x16(a0, qf[ds], s0);
+    s1 = mfma32x32x16(a1, qf[ds], s1);
+  }
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = s0[i] * scale_log2;
+    x[16 + i] = s1[i] * scale_log2;
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int base = kb * 32 + 8 * g + 4 * h;
+        const int4 kp = *reinterpret_cast<const int4*>(kpos + base);
+        int4 kd = {0, 0, 0, 0};
+        if (mask == kMaskCausalDoc) kd = *reinterpret_cast<const int4*>(kdoc + base);
+        const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
+        const int kda[4] = {kd.x, kd.y, kd.z, kd.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bool vis = base + e < klen;
+          if (mask != kMaskNone) vis = vis && kpa[e] <= qpos;
+          if (mask == kMaskCausalDoc) vis = vis && kda[e] == qdoc;
+          if (!vis) x[kb * 16 + g * 4 + e] = neg_inf();
+        }
+      }
+    }
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
+  mt = fmaxf(mt, swap_halves(mt));
+  const float m_new = fmaxf(m, mt);
+  const bool need = m_new > m + kTau;
+  if (__any(need)) {
+    const float c = need ? fast_exp2(m - m_new) : 1.0f;
+    if (need) m = m_new;
+    l *= c;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= c;
+  }
+  const float mu = (m == neg_inf()) ? 0.0f : m;
+  float rs = 0.0f;
+  bf16x8 pf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(x[j * 8 + e] - mu);
+      rs += p;
+      pf[j][e] = (bf16)p;
+    }
+  }
+  l += rs;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (db * 32 + r) * kVS + j * 16 + h * 8);
+      o[db] = mfma32x32x16(a, pf[j], o[db]);
+    }
+  }
+}
+
+template <int D, bool PARTIAL_OUT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+  __shared__ FwdSmem<D> sm;
+  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
+  if (logical >= a.total_wgs) return;
+  int j = 0;
+  while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
+  const JobDesc& job = a.jobs[j];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hpw = a.heads_per_wg;
+  const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
+  const int n_qt = (job.len + qt_rows - 1) / qt_rows;
+  const int local = logical - job.wg_begin;
+  const int hg = local / n_qt;
+  const int qt = n_qt - 1 - (local - hg * n_qt);  // heaviest (latest) query tiles first
+  const int r0 = qt * qt_rows, r1 = min(job.len, r0 + qt_rows);
+  const int head = hg * hpw + wave % hpw;
+  const int kvh = (hg * hpw) / a.group;
+  const int wr0 = r0 + (wave / hpw) * kRowsPerWave;
+  const int wr1 = min(r1, wr0 + kRowsPerWave);
+  const bool wave_rows = wr0 < wr1;
+  const int myrow = wr0 + (lane & 31);
+  const bool row_ok = myrow < wr1;
+  const int mask = a.mask;
+
+  // work-group and wave query ranges (positions / documents are non-decreasing)
+  const int qmin = job.pos[r0], qmax = job.pos[r1 - 1];
+  int qdmin = 0, qdmax = 0, wqdmin = 0, wqdmax = 0;
+  if (mask == kMaskCausalDoc) {
+    qdmin = job.doc[r0];
+    qdmax = job.doc[r1 - 1];
+  }
+  int wqmin = 0, wqmax = -1;
+  if (wave_rows) {
+    wqmin = job.pos[wr0];
+    wqmax = job.pos[wr1 - 1];
+    if (mask == kMaskCausalDoc) {
+      wqdmin = job.doc[wr0];
+      wqdmax = job.doc[wr1 - 1];
+    }
+  }
+
+  bf16x8 qf[D / 16];
+  int qpos = kPosPad, qdoc = 0;
+  {
+    const bf16* qb = reinterpret_cast<const bf16*>(job.q) + ((int64_t)myrow * a.hq + head) * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      if (row_ok)
+        qf[ds] = *reinterpret_cast<const bf16x8*>(qb + ds * 16);
+      else
+        qf[ds] = bf16x8{};
+    }
+    if (row_ok) {
+      qpos = job.pos[myrow];
+      if (mask == kMaskCausalDoc) qdoc = job.doc[myrow];
+    }
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m = neg_inf(), l = 0.0f;
+
+  TileRef cur = next_tile(a, job.seg_end, job.seg_begin, 0, qmin, qmax, qdmin, qdmax);
+  if (cur.seg >= 0) {
+    TileRegs<D> tr;
+    load_tile<D>(tr, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, tid);
+    store_tile<D>(sm, 0, tr, tid);
+    __syncthreads();
+    int buf = 0;
+    while (true) {
+      const TileRef nxt = next_tile(a, job.seg_end, cur.seg, cur.tile + 1, qmin, qmax, qdmin, qdmax);
+      if (nxt.seg >= 0) load_tile<D>(tr, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, tid);
+      if (wave_rows) {
+        const int klen = min(kBK, a.segs[cur.seg].len - cur.tile * kBK);
+        const int32_t* kp = sm.kpos[buf];
+        const int32_t* kd = sm.kdoc[buf];
+        int wcls = classify(mask, wqmin, wqmax, wqdmin, wqdmax, kp[0], kp[klen - 1],
+                            mask == kMaskCausalDoc ? kd[0] : 0,
+                            mask == kMaskCausalDoc ? kd[klen - 1] : 0);
+        if (wcls == kTileFull && klen < kBK) wcls = kTilePartial;
+        if (wcls == kTileFull)
+          tile_step<D, false>(sm.k[buf], sm.vt[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
+                              a.scale_log2, lane);
+        else if (wcls == kTilePartial)
+          tile_step<D, true>(sm.k[buf], sm.vt[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
+                             a.scale_log2, lane);
+      }
+      if (nxt.seg < 0) break;
+      store_tile<D>(sm, buf ^ 1, tr, tid);
+      __syncthreads();
+      buf ^= 1;
+      cur = nxt;
+    }
+  }
+
+  // finalize: combine the two lane halves' partial sums, normalise, store
+  const float lt = l + swap_halves(l);
+  const bool live = lt > 0.0f;
+  const float inv = live ? 1.0f / lt : 0.0f;
+  const float lse = live ? (m + fast_log2(lt)) * kLn2 : neg_inf();
+  if (row_ok) {
+    const int h = lane >> 5;
+    const int64_t rowoff = ((int64_t)myrow * a.hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + g * 8 + h * 4;
+        f32x4 v = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                   o[db][4 * g + 3] * inv};
+        if (PARTIAL_OUT) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(job.o) + rowoff + d0) = v;
+        } else {
+          bf16x4 b;
+          b[0] = (bf16)v[0];
+          b[1] = (bf16)v[1];
+          b[2] = (bf16)v[2];
+          b[3] = (bf16)v[3];
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(job.o) + rowoff + d0) = b;
+        }
+      }
+    }
+    if (h == 0) job.lse[(int64_t)myrow * a.hq + head] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: one thread per (query row, head), 64 rows of one head per block.
+constexpr int kF32Rows = 64;
+constexpr int kF32Keys = 32;
+
+template <int D, bool PARTIAL_OUT>
+__global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdArgs a) {
+  __shared__ float ks[kF32Keys][D + 1];
+  __shared__ float vs[kF32Keys][D + 1];
+  __shared__ int32_t kpos[kF32Keys];
+  __shared__ int32_t kdoc[kF32Keys];
+  const int logical = blockIdx.x;
+  if (logical >= a.total_wgs) return;
+  int j = 0;
+  while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
+  const JobDesc& job = a.jobs[j];
+  const int n_qt = (job.len + kF32Rows - 1) / kF32Rows;
+  const int local = logical - job.wg_begin;
+  const int head = local / n_qt;
+  const int qt = local - head * n_qt;
+  const int r0 = qt * kF32Rows, r1 = min(job.len, r0 + kF32Rows);
+  const int tid = threadIdx.x;
+  const int row = r0 + tid;
+  const bool row_ok = row < r1;
+  const int kvh = head / a.group;
+  const int mask = a.mask;
+  const float* qp = reinterpret_cast<const float*>(job.q) + ((int64_t)(row_ok ? row : r0) * a.hq + head) * D;
+  float q[D], acc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    q[i] = row_ok ? qp[i] : 0.0f;
+    acc[i] = 0.0f;
+  }
+  const int qpos = row_ok ? job.pos[row] : 0;
+  const int qdoc = (row_ok && mask == kMaskCausalDoc) ? job.doc[row] : 0;
+  const int qmin = job.pos[r0], qmax = job.pos[r1 - 1];
+  const int qdmin = mask == kMaskCausalDoc ? job.doc[r0] : 0;
+  const int qdmax = mask == kMaskCausalDoc ? job.doc[r1 - 1] : 0;
+  const float scale = a.scale_log2 * kLn2;
+  float m = neg_inf(), l = 0.0f;
+  for (int s = job.seg_begin; s < job.seg_end; ++s) {
+    const SegDesc& sg = a.segs[s];
+    const float* kb = reinterpret_cast<const float*>(sg.k);
+    const float* vb = reinterpret_cast<const float*>(sg.v);
+    for (int k0 = 0; k0 < sg.len; k0 += kF32Keys) {
+      const int klen = min(kF32Keys, sg.len - k0);
+      const int kdmin = mask == kMaskCausalDoc ? sg.doc[k0] : 0;
+      const int kdmax = mask == kMaskCausalDoc ? sg.doc[k0 + klen - 1] : 0;
+      if (classify(mask, qmin, qmax, qdmin, qdmax, sg.pos[k0], sg.pos[k0 + klen - 1], kdmin, kdmax) ==
+          kTileEmpty)
+        continue;
+      __syncthreads();
+      for (int i = tid; i < klen * D; i += kF32Rows) {
+        const int key = i / D, dd = i % D;
+        ks[key][dd] = kb[((int64_t)(k0 + key) * a.hkv + kvh) * D + dd];
+        vs[key][dd] = vb[((int64_t)(k0 + key) * a.hkv + kvh) * D + dd];
+      }
+      if (tid < klen) {
+        kpos[tid] = sg.pos[k0 + tid];
+        kdoc[tid] = mask == kMaskCausalDoc ? sg.doc[k0 + tid] : 0;
+      }
+      __syncthreads();
+      for (int key = 0; key < klen; ++key) {
+        bool vis = true;
+        if (mask != kMaskNone) vis = kpos[key] <= qpos;
+        if (mask == kMaskCausalDoc) vis = vis && kdoc[key] == qdoc;
+        if (!vis) continue;
+        float sc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) sc = fmaf(q[i], ks[key][i], sc);
+        sc *= scale;
+        const float m_new = fmaxf(m, sc);
+        const float c = expf(m - m_new);
+        const float p = expf(sc - m_new);
+        l = l * c + p;
+#pragma unroll
+        for (int i = 0; i < D; ++i) acc[i] = fmaf(p, vs[key][i], acc[i] * c);
+        m = m_new;
+      }
+    }
+  }
+  if (!row_ok) return;
+  const bool live = l > 0.0f;
+  const float inv = live ? 1.0f / l : 0.0f;
+  const int64_t off = ((int64_t)row * a.hq + head) * D;
+  float* out = reinterpret_cast<float*>(job.o) + off;  // fp32 in both modes
+#pragma unroll
+  for (int i = 0; i < D; ++i) out[i] = acc[i] * inv;
+  job.lse[(int64_t)row * a.hq + head] = live ? m + logf(l) : neg_inf();
+}
+
+template <int D>
+hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t stream) {
+  if (dtype == 0) {
+    const int hpw = a.heads_per_wg;
+    const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
+    int total = 0;
+    for (int j = 0; j < a.n_jobs; ++j) {
+      a.jobs[j].wg_begin = total;
+      const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+      total += n_qt * (a.hq / hpw);
+    }
+    a.total_wgs = total;
+    a.padded_wgs = (total + 7) & ~7;
+    if (total == 0) return hipSuccess;
+    if (partial_out)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+  } else {
+    int total = 0;
+    for (int j = 0; j < a.n_jobs; ++j) {
+      a.jobs[j].wg_begin = total;
+      total += ((a.jobs[j].len + kF32Rows - 1) / kF32Rows) * a.hq;
+    }
+    a.total_wgs = total;
+    a.padded_wgs = total;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3(total), dim3(kF32Rows), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& args, int d, int dtype, bool partial_out, hipStream_t stream) {
+  FwdArgs a = args;
+  if (d == 64) return launch_fwd_d<64>(a, dtype, partial_out, stream);
+  return launch_fwd_d<128>(a, dtype, partial_out, stream);
+}
+
+}  // namespace cpattn

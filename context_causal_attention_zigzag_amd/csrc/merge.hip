@@ -1,0 +1,93 @@
+// Merge kernel: the associative log-sum-exp merge of partial attention states.
+//
+// "Context Parallelism (CP)", section 2.2: for one query row,
+//   L = log sum_j exp(L_j),   O = sum_j exp(L_j - L) O_j,
+// valid in any order and grouping.  Parts with L_j = -inf (no visible key) carry no
+// weight and their O_j is not read; a row whose parts are all -inf becomes (0, -inf).
+//
+// Bandwidth-bound: each (row, head) pair is handled by d/4 threads that each own a
+// 16-byte slice of the head vector, so the n partial outputs stream through in
+// fully coalesced 16-byte loads and the result leaves in one store per thread.
+#include "common.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kMaxParts = 64;
+constexpr int kThreads = 256;
+
+struct MergeArgs {
+  const float* o[kMaxParts];
+  const float* lse[kMaxParts];
+  void* o_out;
+  float* lse_out;
+  int64_t pairs;  // rows * hq
+  int32_t n;
+  int32_t d;
+};
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  const int tpp = a.d >> 2;  // threads per (row, head) pair
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t pair = gid / tpp;
+  const int c = (int)(gid - pair * tpp);
+  if (pair >= a.pairs) return;
+
+  float mx = neg_inf();
+  for (int j = 0; j < a.n; ++j) mx = fmaxf(mx, a.lse[j][pair]);
+  const int64_t off = pair * a.d + 4 * c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse = neg_inf();
+  if (mx != neg_inf()) {
+    float sum = 0.f;
+    for (int j = 0; j < a.n; ++j) sum += fast_exp2((a.lse[j][pair] - mx) * kLog2e);
+    lse = mx + fast_log2(sum) * kLn2;
+    for (int j = 0; j < a.n; ++j) {
+      const float lj = a.lse[j][pair];
+      if (lj == neg_inf()) continue;
+      const float w = fast_exp2((lj - lse) * kLog2e);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.o[j] + off);
+      acc += w * v;
+    }
+  }
+  if (OUT_BF16) {
+    bf16x4 r;
+    r[0] = (bf16)acc[0];
+    r[1] = (bf16)acc[1];
+    r[2] = (bf16)acc[2];
+    r[3] = (bf16)acc[3];
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o_out) + off) = r;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o_out) + off) = acc;
+  }
+  if (c == 0) a.lse_out[pair] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                        int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
+                        hipStream_t stream) {
+  MergeArgs a{};
+  for (int j = 0; j < n_parts; ++j) {
+    a.o[j] = o_parts[j];
+    a.lse[j] = lse_parts[j];
+  }
+  a.o_out = o_out;
+  a.lse_out = lse_out;
+  a.pairs = rows * hq;
+  a.n = n_parts;
+  a.d = d;
+  const int64_t threads = a.pairs * (d / 4);
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  if (out_dtype == 0)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

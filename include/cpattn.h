@@ -1,0 +1,221 @@
+/*
+ * cpattn — one context-parallel rank's share of causal attention on MI355X (gfx950).
+ *
+ * C ABI of libcpattn.so.  Plain C types only: device buffers are passed as raw
+ * device pointers, host tables as host pointers, the stream as an opaque
+ * hipStream_t handle (void*, NULL = the null stream).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are token-major and contiguous: Q/O/dO/dQ are [T, Hq, D], K/V/dK/dV are
+ *    [T, Hkv, D] (D fastest), log-sum-exp values are [T, Hq] fp32 in natural log.
+ *    Positions and document ids are int32 [T].
+ *  - Positions are GLOBAL token indices (the partition output); the causal rule is
+ *    "key visible iff pos_k <= pos_q" (diagonal visible), plus "doc_k == doc_q" for
+ *    packed documents.  Local numbering is storage only.
+ *    Source: "上下文并行：一条序列跨卡，仍算同一个目标", section 01 (global j <= i);
+ *    "Context Parallelism (CP)", section 5 (block-diagonal mask of packed documents).
+ *  - Precondition for speed, not safety: inside each Q block and each KV segment,
+ *    positions (and document ids) are non-decreasing — every partition output is.
+ *    Tiles are classified empty / fully visible / partial from their first and last
+ *    entries; a violated precondition gives wrong masks but never an out-of-bounds
+ *    access.
+ *  - Grouped queries: q head h reads kv head h / (Hq / Hkv).
+ *  - The library keeps no global state and allocates no device memory.  All
+ *    device buffers belong to the caller; host arrays are read only during the
+ *    call.  Work is enqueued asynchronously on `stream`; every argument the host
+ *    can see is validated first, and on any error nothing is enqueued.
+ *  - Outputs are overwritten, never accumulated across calls.
+ *  - A row that sees no key at all gets O = 0 and LSE = -inf (never NaN).
+ *  - Status codes below; cpattn_strerror() names them.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------- */
+#define CPATTN_OK 0
+#define CPATTN_ERR_ARG 1          /* null pointer, negative / out-of-range size or rank */
+#define CPATTN_ERR_ALIGN 2        /* length not divisible by 2*cp, cu_seqlens not monotone
+                                     or not ending at total, pointer / row not 16-B aligned */
+#define CPATTN_ERR_UNSUPPORTED 3  /* head dim, dtype, mask or head grouping not supported */
+#define CPATTN_ERR_HIP 4          /* a HIP launch or runtime call failed */
+#define CPATTN_ERR_WORKSPACE 5    /* workspace missing or smaller than required */
+
+/* ---- enums ------------------------------------------------------------------- */
+#define CPATTN_BF16 0             /* bfloat16 inputs, fp32 accumulation */
+#define CPATTN_F32 1              /* float32 inputs, fp32 arithmetic throughout */
+
+#define CPATTN_MASK_NONE 0        /* every key visible */
+#define CPATTN_MASK_CAUSAL 1      /* pos_k <= pos_q */
+#define CPATTN_MASK_CAUSAL_DOC 2  /* pos_k <= pos_q and doc_k == doc_q (packed documents) */
+
+#define CPATTN_PART_ZIGZAG 0      /* one causal sequence cut into 2*cp chunks */
+#define CPATTN_PART_THD 1         /* packed documents, zigzag inside every document */
+
+/* Attention problem description shared by the attention calls. */
+typedef struct {
+  int32_t dtype;   /* CPATTN_BF16 or CPATTN_F32 (inputs Q, K, V, O, dO) */
+  int32_t hq;      /* query heads (>= 1) */
+  int32_t hkv;     /* key/value heads, hq % hkv == 0 */
+  int32_t d;       /* head dim: 64 or 128 */
+  float scale;     /* multiplies the fp32 scores; 0 means 1/sqrt(d) */
+  int32_t mask;    /* CPATTN_MASK_* */
+} cpattn_attn_desc;
+
+/* A block of local queries (device pointers). */
+typedef struct {
+  const void* q;        /* [len, hq, d] in desc.dtype */
+  const int32_t* pos;   /* [len] global positions */
+  const int32_t* doc;   /* [len] document ids; may be NULL unless CPATTN_MASK_CAUSAL_DOC */
+  int64_t len;          /* rows, >= 0 */
+} cpattn_q_block;
+
+/* A KV segment, e.g. one owner rank's keys/values (device pointers). */
+typedef struct {
+  const void* k;        /* [len, hkv, d] in desc.dtype */
+  const void* v;        /* [len, hkv, d] */
+  const int32_t* pos;   /* [len] global positions */
+  const int32_t* doc;   /* [len] document ids; may be NULL unless CPATTN_MASK_CAUSAL_DOC */
+  int64_t len;          /* rows, >= 0 */
+} cpattn_kv_seg;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* cpattn_strerror(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int cpattn_version(void);
+
+/*
+ * cpattn_partition — the rows one context-parallel rank holds, and their gather.
+ *
+ * Source: "04 · Megatron-LM 实现" (Megatron CP integration), section 1.1 (zigzag:
+ * the sequence is viewed as 2*cp chunks, rank r keeps chunk r then chunk 2cp-1-r)
+ * and section 1.2 with section 5 (packed THD: the same split inside every
+ * document: for a document of length L at offset c, seg = L/(2cp), rows
+ * c+[r*seg, (r+1)*seg) then c+[L-(r+1)*seg, L-r*seg); documents in order).
+ *
+ *  mode             CPATTN_PART_ZIGZAG (cu_seqlens ignored, one document [0,total))
+ *                   or CPATTN_PART_THD.
+ *  total            tokens of the full (packed) sequence; total % (2*cp) == 0.
+ *  cp_size, cp_rank 1 <= cp_size, 0 <= cp_rank < cp_size.
+ *  cu_seqlens_host  THD: host int32 [n_docs+1], 0 = cu[0] <= cu[1] <= ... = total,
+ *                   every difference divisible by 2*cp (validated on the host).
+ *  cu_seqlens_dev   THD: the same values in device memory (read by the kernel).
+ *  n_docs           THD: number of documents (>= 1).
+ *  idx_out          device int32 [total/cp]: global row index of each local row,
+ *                   ascending; doubles as the rows' global positions.
+ *  doc_out          device int32 [total/cp] document id of each local row, or NULL.
+ *  n_gather         number of row tensors to gather (0..8).
+ *  src, dst         host arrays of n_gather device pointers: src[g] is [total, row],
+ *                   dst[g] is [total/cp, row]; dst[g][i] = src[g][idx_out[i]].
+ *  row_bytes        host array of n_gather row sizes in bytes, multiples of 16;
+ *                   src/dst pointers must be 16-byte aligned.
+ * Errors: ARG, ALIGN (see above), HIP.  Output is bit-exact (integer work and
+ * byte copies).
+ */
+int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                     const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                     int32_t n_docs, int32_t* idx_out, int32_t* doc_out, int32_t n_gather,
+                     const void* const* src, void* const* dst, const int64_t* row_bytes,
+                     void* stream);
+
+/*
+ * cpattn_tile_fwd — TileAttention over a batch of independent (Q block, KV segment)
+ * edges of the Q-KV task graph.
+ *
+ * Source: "Context Parallelism (CP)", section 2.1: each edge (i, j) is an
+ * independent task producing the partial state A_ij = (O_ij, L_ij), where L_ij is
+ * the per-row log-sum-exp of the masked, scaled scores Q_i K_j^T and O_ij is the
+ * output normalised inside segment j only.
+ *
+ *  n_edges          number of edges (0 is a no-op).
+ *  q_blocks, segs   host arrays [n_edges]: the edge's queries and its KV segment.
+ *  o_parts          host array [n_edges] of device fp32 [q.len, hq, d] outputs O_ij.
+ *  lse_parts        host array [n_edges] of device fp32 [q.len, hq] outputs L_ij.
+ * Rows of a block that see nothing of the segment get (0, -inf).
+ * Errors: ARG, UNSUPPORTED (d not 64/128, hq % hkv, dtype, mask), HIP.
+ */
+int cpattn_tile_fwd(const cpattn_attn_desc* desc, int32_t n_edges,
+                    const cpattn_q_block* q_blocks, const cpattn_kv_seg* segs,
+                    float* const* o_parts, float* const* lse_parts, void* stream);
+
+/*
+ * cpattn_merge — the associative log-sum-exp merge of partial states.
+ *
+ * Source: "Context Parallelism (CP)", section 2.2: L_i = log sum_j exp(L_ij) and
+ * O_i = sum_j exp(L_ij - L_i) O_ij; any order and grouping gives the same result
+ * up to rounding.  Parts whose L is -inf contribute nothing; a row whose parts are
+ * all -inf becomes (0, -inf).
+ *
+ *  n_parts          1..64.
+ *  o_parts          host array [n_parts] of device fp32 [rows, hq, d].
+ *  lse_parts        host array [n_parts] of device fp32 [rows, hq].
+ *  out_dtype        CPATTN_BF16 (round to nearest even) or CPATTN_F32 for o_out.
+ *  o_out            device [rows, hq, d]; lse_out device fp32 [rows, hq].
+ * Errors: ARG, UNSUPPORTED (d not a multiple of 4 up to 256), HIP.
+ */
+int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* const* lse_parts,
+                 int64_t rows, int32_t hq, int32_t d, int32_t out_dtype, void* o_out,
+                 float* lse_out, void* stream);
+
+/*
+ * cpattn_stream_fwd — the streaming online-softmax form over KV segments in
+ * arrival order (the ring loop of one rank, with the other ranks' segments given
+ * as local buffers).
+ *
+ * Source: "上下文并行：一条序列跨卡，仍算同一个目标", section 02 (per row:
+ * m' = max(m, max_B S), c = e^{m-m'}, l' = c l + sum_B e^{S-m'},
+ * a' = c a + sum_B e^{S-m'} V, O = a / l, lambda = m + log l) and
+ * "推理系统基础设施（二）：Sequence Parallelism + Ring Attention", section 2
+ * (Q stays, KV blocks arrive one by one, the running max/sum/output are updated).
+ *
+ *  q                the local query block.
+ *  n_segs, segs     host array of KV segments in arrival order (1..32).
+ *  o_out            device [q.len, hq, d] in desc.dtype (final output O).
+ *  lse_out          device fp32 [q.len, hq] (lambda, natural log).
+ * Errors: ARG, UNSUPPORTED, HIP.
+ */
+int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* stream);
+
+/*
+ * cpattn_bwd — LSE-replay backward of one rank's share.
+ *
+ * Source: "上下文并行：一条序列跨卡，仍算同一个目标", sections 01-02: the local
+ * probabilities are rebuilt from the full-row LSE and output, P_ij = exp(S_ij -
+ * lambda_i); then dQ, dK, dV of every block follow from the softmax derivative,
+ * dK_j = sum_i dS_ij Q_i / sqrt(d), dV_j = sum_i P_ij G_i, and the K/V gradient
+ * contributions of all local queries are summed per owner (per segment here).
+ *
+ *  q, segs          as for cpattn_stream_fwd (bf16 only in this version).
+ *  o                device [q.len, hq, d] forward output (desc.dtype).
+ *  lse              device fp32 [q.len, hq] forward log-sum-exp.
+ *  dout             device [q.len, hq, d] upstream gradient G (desc.dtype).
+ *  dq               device fp32 [q.len, hq, d] output.
+ *  dk, dv           host arrays [n_segs] of device fp32 [segs[s].len, hkv, d] outputs:
+ *                   the summed contribution of all local queries (and all query
+ *                   heads of a group) to segment s's keys and values.
+ *  workspace        device buffer of at least cpattn_bwd_workspace_bytes() bytes,
+ *                   256-byte aligned; contents on entry are ignored.
+ * Errors: ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+               const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout,
+               float* dq, float* const* dk, float* const* dv, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace cpattn_bwd needs for `q_len` local rows (0 on bad args). */
+size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, int64_t q_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports what include/cpattn.h declares, and rejects bad
+arguments on the host before touching a GPU (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import context_causal_attention_zigzag_amd as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("cpattn_partition", "cpattn_tile_fwd", "cpattn_merge", "cpattn_stream_fwd", "cpattn_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (cpattn_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(C.lib, n)
+    assert set(C.EXPORTED) == set(declared_functions())
+
+
+def test_strerror_names_every_status():
+    for st in range(6):
+        assert C.cpattn_strerror(st) and "unknown" not in C.cpattn_strerror(st)
+    assert "unknown" in C.cpattn_strerror(99)
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def part(mode, total, cp, rank, cu=None, n_gather=0, row_bytes=(16,)):
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu) if cu else None
+    n_docs = len(cu) - 1 if cu else 0
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    rb = (ctypes.c_int64 * 1)(*row_bytes)
+    return C.lib.cpattn_partition(mode, total, cp, rank, cu_arr, FAKE if cu else None, n_docs, FAKE, None,
+                                  n_gather, ptrs, ptrs, rb, None)
+
+
+def test_partition_validation():
+    assert part(C.PART_ZIGZAG, 100, 4, 0) == C.ERR_ALIGN          # 100 % 8
+    assert part(C.PART_ZIGZAG, 64, 4, 4) == C.ERR_ARG             # rank out of range
+    assert part(C.PART_ZIGZAG, 64, 0, 0) == C.ERR_ARG
+    assert part(C.PART_ZIGZAG, -8, 2, 0) == C.ERR_ARG
+    assert part(7, 64, 2, 0) == C.ERR_ARG
+    assert part(C.PART_THD, 64, 2, 0, cu=[0, 32, 60]) == C.ERR_ALIGN   # does not end at total
+    assert part(C.PART_THD, 64, 2, 0, cu=[0, 30, 64]) == C.ERR_ALIGN   # 30 % 4
+    assert part(C.PART_THD, 64, 2, 0, cu=[0, 40, 32, 64]) == C.ERR_ALIGN  # not monotone
+    assert part(C.PART_THD, 64, 2, 0, cu=[1, 32, 64]) == C.ERR_ALIGN
+    assert part(C.PART_ZIGZAG, 64, 2, 0, n_gather=1, row_bytes=(24,)) == C.ERR_ALIGN
+    assert part(C.PART_ZIGZAG, 64, 2, 0, n_gather=1, row_bytes=(0,)) == C.ERR_ARG
+    assert part(C.PART_ZIGZAG, 64, 2, 0, n_gather=9) == C.ERR_ARG
+
+
+def desc(**kw):
+    base = dict(dtype=C.BF16, hq=8, hkv=8, d=128, scale=0.0, mask=C.MASK_CAUSAL)
+    base.update(kw)
+    return C.cpattn_attn_desc(**base)
+
+
+def qb(n=64, q=FAKE):
+    return C.cpattn_q_block(q, FAKE, None, n)
+
+
+def sg(n=64):
+    return C.cpattn_kv_seg(FAKE, FAKE, FAKE, None, n)
+
+
+def stream_call(d, q=None, segs=None):
+    q = q or qb()
+    segs = segs if segs is not None else [sg()]
+    arr = (C.cpattn_kv_seg * max(1, len(segs)))(*segs)
+    return C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), len(segs), arr, FAKE, FAKE, None)
+
+
+def test_attention_validation():
+    assert stream_call(desc(d=96)) == C.ERR_UNSUPPORTED
+    assert stream_call(desc(hq=6, hkv=4)) == C.ERR_UNSUPPORTED
+    assert stream_call(desc(mask=5)) == C.ERR_UNSUPPORTED
+    assert stream_call(desc(dtype=7)) == C.ERR_UNSUPPORTED
+    assert stream_call(desc(hkv=0)) == C.ERR_ARG
+    assert stream_call(desc(scale=float("nan"))) == C.ERR_ARG
+    assert stream_call(desc(), segs=[]) == C.ERR_ARG
+    assert stream_call(desc(), segs=[sg()] * 33) == C.ERR_ARG
+    assert stream_call(desc(), q=qb(q=FAKE + 8)) == C.ERR_ALIGN
+    assert stream_call(desc(), q=C.cpattn_q_block(FAKE, None, None, 64)) == C.ERR_ARG
+    assert stream_call(desc(mask=C.MASK_CAUSAL_DOC)) == C.ERR_ARG     # doc ids required
+    assert stream_call(desc(), segs=[C.cpattn_kv_seg(FAKE, FAKE, FAKE, None, -1)]) == C.ERR_ARG
+
+
+def test_tile_and_merge_validation():
+    d = desc(d=64)
+    q = (C.cpattn_q_block * 1)(qb())
+    s = (C.cpattn_kv_seg * 1)(sg())
+    nul = (ctypes.c_void_p * 1)(None)
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 1, q, s, nul, nul, None) == C.ERR_ARG
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), -1, q, s, nul, nul, None) == C.ERR_ARG
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 0, q, s, nul, nul, None) == C.OK   # no-op
+    p = (ctypes.c_void_p * 1)(FAKE)
+    assert C.lib.cpattn_merge(0, p, p, 10, 8, 128, C.BF16, FAKE, FAKE, None) == C.ERR_ARG
+    assert C.lib.cpattn_merge(65, p, p, 10, 8, 128, C.BF16, FAKE, FAKE, None) == C.ERR_ARG
+    assert C.lib.cpattn_merge(1, p, p, 10, 8, 6, C.BF16, FAKE, FAKE, None) == C.ERR_UNSUPPORTED
+    assert C.lib.cpattn_merge(1, p, p, 10, 8, 128, 9, FAKE, FAKE, None) == C.ERR_UNSUPPORTED
+    assert C.lib.cpattn_merge(1, p, p, 0, 8, 128, C.BF16, FAKE, FAKE, None) == C.OK   # no-op
+
+
+def test_bwd_validation_and_workspace():
+    d = desc()
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), 2048) == 2048 * 8 * 4
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), 3) == 256
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), -1) == 0
+    q = qb(2048)
+    s = (C.cpattn_kv_seg * 1)(sg())
+    p = (ctypes.c_void_p * 1)(FAKE)
+    f32 = desc(dtype=C.F32)
+    assert C.lib.cpattn_bwd(ctypes.byref(f32), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
+                            FAKE, 1 << 20, None) == C.ERR_UNSUPPORTED
+    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
+                            FAKE, 100, None) == C.ERR_WORKSPACE
+    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
+                            None, 1 << 20, None) == C.ERR_WORKSPACE
+    nul = (ctypes.c_void_p * 1)(None)
+    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, nul, p,
+                            FAKE, 1 << 20, None) == C.ERR_ARG

@@ -1,0 +1,108 @@
+"""Backward parity: dQ and the per-owner dK/dV sums vs the oracle's float64 gradients."""
+import numpy as np
+import pytest
+import torch
+
+from context_causal_attention_zigzag_amd.rank_share import build_rank_share, ring_order
+import oracle
+from oracle import attention as OA
+import workloads
+from gpu_common import DEV, TOL_BF16, assert_close, rank_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bwd(q, k, v, g_full, cp, rank, cu=None):
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), cp, rank, cu)
+    rows, qdoc = rank_rows(q.shape[0], cp, rank, cu)
+    g = g_full[torch.as_tensor(rows)]
+    o, lse = rs.stream_fwd("owner")
+    dq, dk, dv = rs.bwd(o, lse, g.to(DEV))
+    torch.cuda.synchronize()
+    return rs, rows, g, dq, dk, dv
+
+
+def check_bwd(name, q, k, v, g_full, cp, rank, cu=None):
+    say(f"{name} bwd rank={rank}")
+    rs, rows, g, dq, dk, dv = run_bwd(q, k, v, g_full, cp, rank, cu)
+    seq = q.shape[0]
+    kw = {}
+    if cu is not None:
+        kw = dict(q_doc=oracle.thd_doc_ids(cu, rows), k_doc=oracle.thd_doc_ids(cu, np.arange(seq)),
+                  mask=OA.MASK_CAUSAL_DOC)
+    dq_r, dk_r, dv_r = OA.attention_bwd(q[torch.as_tensor(rows)], k, v, g, rows, np.arange(seq), **kw)
+    assert_close(dq, dq_r, TOL_BF16, f"{name} r{rank} dQ")
+    for (o_idx, owner) in enumerate(ring_order(cp, rank)):
+        orow = rs.owners[owner].idx.cpu().numpy()
+        assert_close(dk[o_idx], dk_r[orow], TOL_BF16, f"{name} r{rank} dK owner {owner}")
+        assert_close(dv[o_idx], dv_r[orow], TOL_BF16, f"{name} r{rank} dV owner {owner}")
+    return rs, dk, dv
+
+
+@pytest.fixture(scope="module")
+def bwd8k():
+    w = workloads.WORKLOADS["bwd8k"]
+    q, k, v = workloads.full_qkv(w)
+    g = workloads.randn((w.seq, w.hq, w.d), w.grad_seed, w.dtype, 3)
+    return w, q, k, v, g
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_bwd8k_rank(bwd8k, rank):
+    w, q, k, v, g = bwd8k
+    check_bwd("bwd8k", q, k, v, g, w.cp, rank)
+
+
+@pytest.mark.parametrize("seq,cp,hq,hkv,d", [(800, 4, 4, 2, 128), (512, 2, 8, 1, 64), (384, 2, 12, 4, 128)])
+def test_bwd_small_shapes_and_owner_sums(seq, cp, hq, hkv, d):
+    q = workloads.randn((seq, hq, d), 21, "bf16", 0)
+    k = workloads.randn((seq, hkv, d), 21, "bf16", 1)
+    v = workloads.randn((seq, hkv, d), 21, "bf16", 2)
+    g = workloads.randn((seq, hq, d), 21, "bf16", 3)
+    dk_sum = torch.zeros((seq, hkv, d), dtype=torch.float64)
+    dv_sum = torch.zeros((seq, hkv, d), dtype=torch.float64)
+    for r in range(cp):
+        rs, dk, dv = check_bwd(f"bwd{seq}", q, k, v, g, cp, r)
+        for o_idx, owner in enumerate(ring_order(cp, r)):
+            orow = torch.as_tensor(rs.owners[owner].idx.cpu().numpy().astype(np.int64))
+            dk_sum[orow] += dk[o_idx].cpu().double()
+            dv_sum[orow] += dv[o_idx].cpu().double()
+    # contributions of all emulated ranks summed at their owners = full-sequence gradients
+    _, dk_f, dv_f = OA.attention_bwd(q, k, v, g)
+    assert_close(dk_sum, dk_f, TOL_BF16, f"bwd{seq} owner-summed dK")
+    assert_close(dv_sum, dv_f, TOL_BF16, f"bwd{seq} owner-summed dV")
+
+
+def test_bwd_packed_small():
+    lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520]
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    q = workloads.randn((total, 4, 128), 22, "bf16", 0)
+    k = workloads.randn((total, 2, 128), 22, "bf16", 1)
+    v = workloads.randn((total, 2, 128), 22, "bf16", 2)
+    g = workloads.randn((total, 4, 128), 22, "bf16", 3)
+    for r in range(2):
+        check_bwd("bwd-packed", q, k, v, g, 2, r, cu)
+
+
+def test_bwd_fully_masked_rows_give_zero_gradients():
+    import context_causal_attention_zigzag_amd as C
+    tq, tk, h, d = 40, 64, 2, 128
+    q = workloads.randn((tq, h, d), 23, "bf16", 0).to(DEV)
+    k = workloads.randn((tk, h, d), 23, "bf16", 1).to(DEV)
+    v = workloads.randn((tk, h, d), 23, "bf16", 2).to(DEV)
+    g = workloads.randn((tq, h, d), 23, "bf16", 3).to(DEV)
+    qpos = torch.arange(tq, dtype=torch.int32, device=DEV)
+    kpos = torch.arange(tk, dtype=torch.int32, device=DEV) + 100
+    desc = C.attn_desc(h, h, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((tq, h), dtype=torch.float32, device=DEV)
+    say("bwd fully masked")
+    C.cpattn_stream_fwd(desc, C.q_block(q, qpos), [C.kv_seg(k, v, kpos)], o, lse)
+    dq = torch.full((tq, h, d), 7.0, device=DEV)
+    dk = torch.full((tk, h, d), 7.0, device=DEV)
+    dv = torch.full((tk, h, d), 7.0, device=DEV)
+    ws = torch.empty(C.cpattn_bwd_workspace_bytes(desc, tq), dtype=torch.uint8, device=DEV)
+    C.cpattn_bwd(desc, C.q_block(q, qpos), [C.kv_seg(k, v, kpos)], o, lse, g, dq, [dk], [dv], ws)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)

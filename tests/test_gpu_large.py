@@ -1,0 +1,79 @@
+"""Full-size workloads in the launch configuration the benchmark times, checked on
+sampled rows against the oracle (which evaluates those rows against every key), and
+the two forward forms checked against each other on every row."""
+import numpy as np
+import pytest
+import torch
+
+from context_causal_attention_zigzag_amd.rank_share import build_rank_share
+import oracle
+import workloads
+from gpu_common import (DEV, TOL_BF16, TOL_LSE_BF16, assert_close, oracle_fwd_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_local_rows(n, extra, seed):
+    base = [0, 1, 31, 32, 63, 64, 127, 128, n // 2 - 1, n // 2, n // 2 + 1, n - 2, n - 1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([base, rng.integers(0, n, extra)]))
+
+
+def test_s128k_rank0_sampled():
+    w = workloads.WORKLOADS["s128k"]
+    say("s128k: generating inputs")
+    q, k, v = workloads.full_qkv(w)
+    say("s128k: partition + stream")
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), w.cp, 0)
+    o, lse = rs.stream_fwd("chunk")
+    torch.cuda.synchronize()
+    say("s128k: tile + merge")
+    edges, parts = rs.alloc_tile_buffers("chunk")
+    assert len(edges) == 2 * w.cp + 1
+    rs.tile_fwd(edges, parts)
+    o2, l2 = rs.merge(edges, parts)
+    torch.cuda.synchronize()
+    del parts
+    local = sample_local_rows(rs.q.shape[0], 19, 3)
+    rows = rs.q_idx.cpu().numpy()[local]
+    assert np.array_equal(rows, oracle.zigzag_indices(w.seq, w.cp, 0)[local])
+    say(f"s128k: oracle on {len(local)} rows")
+    o_ref, l_ref = oracle_fwd_rows(q, k, v, rows)
+    li = torch.as_tensor(local, device=DEV)
+    assert_close(o[li], o_ref, TOL_BF16, "s128k stream O (sampled)")
+    assert_close(lse[li], l_ref, TOL_LSE_BF16, "s128k stream LSE (sampled)")
+    assert_close(o2[li], o_ref, TOL_BF16, "s128k tile O (sampled)")
+    assert_close(l2[li], l_ref, TOL_LSE_BF16, "s128k tile LSE (sampled)")
+    # every row: the two forward forms agree
+    assert_close(o2, o.float(), TOL_BF16, "s128k tile vs stream O (all rows)")
+    assert_close(l2, lse, TOL_LSE_BF16, "s128k tile vs stream LSE (all rows)")
+
+
+def test_thd64k_rank1_sampled():
+    w = workloads.WORKLOADS["thd64k"]
+    cu = workloads.cu_seqlens_from_lengths(workloads.thd_lengths(w.seed))
+    q, k, v = workloads.full_qkv(w)
+    say("thd64k: partition + stream")
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), w.cp, 1, cu)
+    o, lse = rs.stream_fwd("owner")
+    edges, parts = rs.alloc_tile_buffers("owner")
+    rs.tile_fwd(edges, parts)
+    o2, l2 = rs.merge(edges, parts)
+    torch.cuda.synchronize()
+    rows_all = oracle.thd_indices(cu, w.cp, 1)
+    assert np.array_equal(rs.q_idx.cpu().numpy(), rows_all)
+    assert np.array_equal(rs.q_doc.cpu().numpy(), oracle.thd_doc_ids(cu, rows_all))
+    # sampled rows: both ends of every document's two slices plus random rows
+    docs = oracle.thd_doc_ids(cu, rows_all)
+    ends = np.flatnonzero(np.diff(docs)) 
+    local = np.unique(np.concatenate([sample_local_rows(len(rows_all), 16, 4), ends, ends + 1]))
+    rows = rows_all[local]
+    say(f"thd64k: oracle on {len(local)} rows")
+    all_docs = oracle.thd_doc_ids(cu, np.arange(w.seq))
+    o_ref, l_ref = oracle_fwd_rows(q, k, v, rows, cu, all_docs)
+    li = torch.as_tensor(local, device=DEV)
+    assert_close(o[li], o_ref, TOL_BF16, "thd64k stream O (sampled)")
+    assert_close(lse[li], l_ref, TOL_LSE_BF16, "thd64k stream LSE (sampled)")
+    assert_close(o2[li], o_ref, TOL_BF16, "thd64k tile O (sampled)")
+    assert_close(o2, o.float(), TOL_BF16, "thd64k tile vs stream O (all rows)")
+    assert_close(l2, lse, TOL_LSE_BF16, "thd64k tile vs stream LSE (all rows)")

@@ -1,0 +1,58 @@
+"""Partition kernel vs the oracle: indices and document ids bit-exact, gathers are
+exact row copies."""
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_zigzag_amd as C
+from context_causal_attention_zigzag_amd.rank_share import partition_shard
+import oracle
+import workloads
+from gpu_common import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("seq,cp", [(512, 2), (8192, 4), (800, 4), (131072, 8), (64, 1), (48, 3)])
+def test_zigzag_indices_and_gather(seq, cp):
+    src = torch.arange(seq * 24, dtype=torch.int32).reshape(seq, 3, 8)   # 96-byte rows
+    src2 = torch.randn(seq, 4, dtype=torch.float32)                        # 16-byte rows
+    g_src, g_src2 = src.to(DEV), src2.to(DEV)
+    for r in range(cp):
+        say(f"partition zigzag seq={seq} cp={cp} rank={r}")
+        sh = partition_shard(C.PART_ZIGZAG, seq, cp, r, [g_src, g_src2])
+        torch.cuda.synchronize()
+        want = oracle.zigzag_indices(seq, cp, r)
+        assert np.array_equal(sh.idx.cpu().numpy(), want)
+        assert torch.equal(sh.tensors[0].cpu(), src[torch.as_tensor(want)])
+        assert torch.equal(sh.tensors[1].cpu(), src2[torch.as_tensor(want)])
+
+
+@pytest.mark.parametrize("lengths,cp", [
+    (None, 4),                                      # the thd64k mix (seed 4)
+    ([8, 64, 136, 0, 16, 256, 8, 32], 2),           # short, ragged, one empty document
+    ([4096], 4),                                    # one document = zigzag
+])
+def test_thd_indices_docs_and_gather(lengths, cp):
+    if lengths is None:
+        lengths = workloads.thd_lengths(4)
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    cu_dev = torch.as_tensor(cu, dtype=torch.int32, device=DEV)
+    src = torch.randn(total, 2, 64).to(torch.bfloat16)
+    g_src = src.to(DEV)
+    for r in range(cp):
+        say(f"partition thd docs={len(lengths)} total={total} cp={cp} rank={r}")
+        sh = partition_shard(C.PART_THD, total, cp, r, [g_src], cu.tolist(), cu_dev, with_doc=True)
+        torch.cuda.synchronize()
+        want = oracle.thd_indices(cu, cp, r)
+        assert np.array_equal(sh.idx.cpu().numpy(), want)
+        assert np.array_equal(sh.doc.cpu().numpy(), oracle.thd_doc_ids(cu, want))
+        assert torch.equal(sh.tensors[0].cpu().view(torch.int16), src[torch.as_tensor(want)].view(torch.int16))
+
+
+def test_empty_partition_is_noop():
+    say("partition total=0")
+    idx = torch.empty(0, dtype=torch.int32, device=DEV)
+    C.cpattn_partition(C.PART_ZIGZAG, 0, 4, 1, idx)
+    torch.cuda.synchronize()
