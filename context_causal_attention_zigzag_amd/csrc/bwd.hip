@@ -13,12 +13,13 @@
 //    keeps keys 32w..32w+31 (K and V rows) in registers as B operands and owns their
 //    dK/dV accumulators, so the per-owner sums over all local queries and all query
 //    heads of the group finish in registers and are stored once (no atomics).
-//    The work-group walks the visible 32-row query tiles: Q and dO are staged in LDS
-//    both row-major (A operands of S = Q K^T and dP = dO V^T) and transposed with the
-//    contraction order of a C-layout B operand (A operands of dV^T = dO^T P and
-//    dK^T = Q^T dS), so P and dS feed the matrix cores straight from the accumulators.
-//    dS goes through LDS once more for dQ = dS K, computed per 32-dim slice by each
-//    wave and added to the fp32 dQ with coalesced atomics (128-byte rows).
+//    The work-group walks the visible 32-row query tiles: Q and dO are staged row-major
+//    in LDS; they are the A operands of S = Q K^T and dP = dO V^T as plain row reads,
+//    and of dV^T = dO^T P and dK^T = Q^T dS through transposing LDS reads addressed in
+//    the contraction order of the accumulator layout, so P and dS feed the matrix
+//    cores straight from the accumulators.  dS goes through LDS once more for
+//    dQ = dS K (K^T slices read transposed from a row-major K tile), computed per
+//    32-dim slice by each wave and added to the fp32 dQ with coalesced atomics.
 //  - one barrier per query tile; the next tile's global loads overlap the current
 //    tile's matrix work.
 #include "common.h"
@@ -61,42 +62,41 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdSmem {
-  static constexpr int kRS = D + 8;     // row-major stride (Q, dO)
-  static constexpr int kTS = kBQ + 8;   // transposed stride (Q^T, dO^T)
-  static constexpr int kSS = kBKV + 8;  // dS and K^T stride
+  static constexpr int kRS = D + 8;     // Q / dO row stride (row reads and transposing reads)
+  static constexpr int kKS = D + 16;    // K row stride (transposing reads only)
+  static constexpr int kSS = kBKV + 8;  // dS row stride (row reads)
   bf16 qs[2][kBQ * kRS];
   bf16 dos[2][kBQ * kRS];
-  bf16 qt[2][D * kTS];
-  bf16 dot[2][D * kTS];
   float lse2[2][kBQ];
   float delta[2][kBQ];
   int32_t qpos[2][kBQ];
   int32_t qdoc[2][kBQ];
   bf16 ds[2][kBQ * kSS];
-  bf16 kt[D * kSS];
+  bf16 ks[kBKV * kKS];
 };
 
+template <int D>
 struct QStageRegs {
-  u32x4 x[4];  // 4 rows x 8 dims of Q (threads 0..127) or dO (threads 128..255)
+  static constexpr int kChunks = kBQ * D / 8 / 128;  // 16-byte chunks per thread
+  u32x4 x[kChunks];  // rows of Q (threads 0..127) or of dO (threads 128..255)
   float lse2, delta;
   int32_t pos, doc;
 };
 
-__device__ __forceinline__ void load_qstage(QStageRegs& r, const BwdArgs& a, int head, int r0, int D,
-                                            int tid) {
-  const int half = tid >> 7;       // 0: Q, 1: dO
+template <int D>
+__device__ __forceinline__ void load_qstage(QStageRegs<D>& r, const BwdArgs& a, int head, int r0, int tid) {
+  constexpr int kCPR = D / 8;
+  const int half = tid >> 7;  // 0: Q, 1: dO
   const int u = tid & 127;
-  const int m = u & 7, dc = u >> 3;  // rows 4m..4m+3, dims dc*8..+7
-  if (dc < D / 8) {
-    const bf16* base = reinterpret_cast<const bf16*>(half ? a.dout : a.q);
+  const bf16* base = reinterpret_cast<const bf16*>(half ? a.dout : a.q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * m + i;
-      if (row < a.q_len)
-        r.x[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8);
-      else
-        r.x[i] = u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
+    const int c = u + 128 * i;
+    const int row = r0 + c / kCPR, dc = c % kCPR;
+    if (row < a.q_len)
+      r.x[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8);
+    else
+      r.x[i] = u32x4{0, 0, 0, 0};
   }
   if (tid < kBQ) {
     const int row = r0 + tid;
@@ -116,25 +116,15 @@ __device__ __forceinline__ void load_qstage(QStageRegs& r, const BwdArgs& a, int
 }
 
 template <int D>
-__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs& r, int tid) {
-  constexpr int kRS = BwdSmem<D>::kRS, kTS = BwdSmem<D>::kTS;
+__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs<D>& r, int tid) {
+  constexpr int kCPR = D / 8, kRS = BwdSmem<D>::kRS;
   const int half = tid >> 7;
   const int u = tid & 127;
-  const int m = u & 7, dc = u >> 3;
-  if (dc < D / 8) {
-    bf16* rowm = half ? sm.dos[buf] : sm.qs[buf];
-    bf16* trn = half ? sm.dot[buf] : sm.qt[buf];
+  bf16* dst = half ? sm.dos[buf] : sm.qs[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&rowm[(4 * m + i) * kRS + dc * 8]) = r.x[i];
-    const int col = perm16(4 * m);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (r.x[0][w] >> sh) & 0xffffu, x1 = (r.x[1][w] >> sh) & 0xffffu;
-      const uint32_t x2 = (r.x[2][w] >> sh) & 0xffffu, x3 = (r.x[3][w] >> sh) & 0xffffu;
-      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
-      *reinterpret_cast<u32x2*>(&trn[(dc * 8 + e) * kTS + col]) = packed;
-    }
+  for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
+    const int c = u + 128 * i;
+    *reinterpret_cast<u32x4*>(&dst[(c / kCPR) * kRS + (c % kCPR) * 8]) = r.x[i];
   }
   if (tid < kBQ) {
     sm.lse2[buf][tid] = r.lse2;
@@ -167,23 +157,29 @@ __device__ __forceinline__ QRef next_qtile(const BwdArgs& a, int hh, int qt, int
   return {-1, 0};
 }
 
+// One (32-row query tile, this wave's 32 keys) block: S = Q K^T and dP = dO V^T from
+// row-major LDS rows and register-resident K/V; P and dS in the accumulator layout;
+// dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by transposing
+// LDS reads in the accumulators' contraction order; dS also goes to LDS for dQ.
 template <int D, bool MASKED>
 __device__ __forceinline__ void bwd_step(BwdSmem<D>& sm, int buf, const bf16x8 (&kf)[D / 16],
                                          const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
                                          f32x16 (&dv)[D / 32], int kpos, int kdoc, bool key_ok,
                                          int mask, float scale, float scale_log2, int wave, int lane) {
-  constexpr int kRS = BwdSmem<D>::kRS, kTS = BwdSmem<D>::kTS, kSS = BwdSmem<D>::kSS;
+  constexpr int kRS = BwdSmem<D>::kRS, kSS = BwdSmem<D>::kSS;
   const int r = lane & 31, h = lane >> 5;
   f32x16 s = {}, dp = {};
+  const bf16* qrow = sm.qs[buf] + r * kRS + h * 8;
+  const bf16* orow = sm.dos[buf] + r * kRS + h * 8;
 #pragma unroll
   for (int ds = 0; ds < D / 16; ++ds) {
-    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qs[buf][r * kRS + ds * 16 + h * 8]);
-    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dos[buf][r * kRS + ds * 16 + h * 8]);
+    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
+    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(orow + ds * 16);
     s = mfma32x32x16(aq, kf[ds], s);
     dp = mfma32x32x16(ao, vf[ds], dp);
   }
   bf16x8 pf[2], dsf[2];
-  bf16* dsrow = sm.ds[buf];
+  bf16* dsw = sm.ds[buf] + 4 * h * kSS + wave * 32 + r;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int q0 = 8 * g + 4 * h;
@@ -199,7 +195,7 @@ __device__ __forceinline__ void bwd_step(BwdSmem<D>& sm, int buf, const bf16x8 (
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int a = 4 * g + e;
-      float p = fast_exp2(s[a] * scale_log2 - l2[e]);
+      float p = fast_exp2(fmaf(s[a], scale_log2, -l2[e]));
       if (MASKED) {
         bool vis = key_ok;
         if (mask != kMaskNone) vis = vis && kpos <= qpa[e];
@@ -210,15 +206,18 @@ __device__ __forceinline__ void bwd_step(BwdSmem<D>& sm, int buf, const bf16x8 (
       pf[a >> 3][a & 7] = (bf16)p;
       const bf16 dsb = (bf16)dsv;
       dsf[a >> 3][a & 7] = dsb;
-      dsrow[(q0 + e) * kSS + wave * 32 + r] = dsb;
+      dsw[(8 * g + e) * kSS] = dsb;
     }
   }
+  const bf16* qtr = sm.qs[buf] + tr_lane_offset<4>(lane, kRS);
+  const bf16* otr = sm.dos[buf] + tr_lane_offset<4>(lane, kRS);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
-      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sm.dot[buf][(db * 32 + r) * kTS + sl * 16 + h * 8]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][(db * 32 + r) * kTS + sl * 16 + h * 8]);
+      const int off = sl * 16 * kRS + db * 32;
+      const bf16x8 ao = concat(lds_read_tr4(otr + off), lds_read_tr4(otr + off + 8 * kRS));
+      const bf16x8 aq = concat(lds_read_tr4(qtr + off), lds_read_tr4(qtr + off + 8 * kRS));
       dv[db] = mfma32x32x16(ao, pf[sl], dv[db]);
       dk[db] = mfma32x32x16(aq, dsf[sl], dk[db]);
     }
@@ -228,7 +227,7 @@ __device__ __forceinline__ void bwd_step(BwdSmem<D>& sm, int buf, const bf16x8 (
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   __shared__ BwdSmem<D> sm;
-  constexpr int kSS = BwdSmem<D>::kSS;
+  constexpr int kSS = BwdSmem<D>::kSS, kKS = BwdSmem<D>::kKS;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
   if (logical >= a.total_wgs) return;
   int s = 0;
@@ -263,28 +262,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int kpos = key_ok ? sg.pos[mykey] : kPosPad;
   const int kdoc = (key_ok && mask == kMaskCausalDoc) ? sg.doc[mykey] : 0;
 
-  // K^T of the whole work-group tile in LDS (natural key order), for dQ = dS K
-  for (int u = tid; u < (kBKV / 4) * (D / 8); u += kThreads) {
-    const int m = u % (kBKV / 4), dc = u / (kBKV / 4);
-    uint32_t w[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k0 + 4 * m + i;
-      u32x4 x = {0, 0, 0, 0};
-      if (key < k1) x = *reinterpret_cast<const u32x4*>(kb + ((int64_t)key * a.hkv + kvh) * D + dc * 8);
-      w[i][0] = x[0];
-      w[i][1] = x[1];
-      w[i][2] = x[2];
-      w[i][3] = x[3];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (w[0][wi] >> sh) & 0xffffu, x1 = (w[1][wi] >> sh) & 0xffffu;
-      const uint32_t x2 = (w[2][wi] >> sh) & 0xffffu, x3 = (w[3][wi] >> sh) & 0xffffu;
-      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
-      *reinterpret_cast<u32x2*>(&sm.kt[(dc * 8 + e) * kSS + 4 * m]) = packed;
-    }
+  // the work-group's K tile, row-major in LDS (operand of dQ = dS K)
+  for (int c = tid; c < kBKV * (D / 8); c += kThreads) {
+    const int key = c / (D / 8), dc = c % (D / 8);
+    u32x4 x = {0, 0, 0, 0};
+    if (k0 + key < k1) x = *reinterpret_cast<const u32x4*>(kb + ((int64_t)(k0 + key) * a.hkv + kvh) * D + dc * 8);
+    *reinterpret_cast<u32x4*>(&sm.ks[key * kKS + dc * 8]) = x;
   }
 
   // key ranges of the work-group and of this wave (non-decreasing positions)
@@ -313,17 +296,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
+  // dQ operand: K^T slice of this wave's 32 dims via transposing reads, natural key order
+  const bf16* ktr = sm.ks + tr_lane_offset<8>(lane, kKS) + wave * 32;
   const int n_qt = (a.q_len + kBQ - 1) / kBQ;
   QRef cur = next_qtile(a, 0, 0, n_qt, kmin, kmax, kdmin, kdmax);
   if (cur.hh >= 0) {
-    QStageRegs qr;
-    load_qstage(qr, a, kvh * a.group + cur.hh, cur.qt * kBQ, D, tid);
+    QStageRegs<D> qr;
+    load_qstage<D>(qr, a, kvh * a.group + cur.hh, cur.qt * kBQ, tid);
     store_qstage<D>(sm, 0, qr, tid);
     __syncthreads();
     int buf = 0;
     while (true) {
       QRef nxt = next_qtile(a, cur.hh, cur.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
-      if (nxt.hh >= 0) load_qstage(qr, a, kvh * a.group + nxt.hh, nxt.qt * kBQ, D, tid);
+      if (nxt.hh >= 0) load_qstage<D>(qr, a, kvh * a.group + nxt.hh, nxt.qt * kBQ, tid);
       const int head = kvh * a.group + cur.hh;
       const int r0 = cur.qt * kBQ, r1 = min(a.q_len, r0 + kBQ);
       // wave-level class of (query tile, this wave's keys)
@@ -342,26 +327,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       else if (wcls == kTilePartial)
         bwd_step<D, true>(sm, buf, kf, vf, dk, dv, kpos, kdoc, key_ok, mask, a.scale, a.scale_log2, wave, lane);
       else {
-        bf16* dsrow = sm.ds[buf];
+        bf16* dsw = sm.ds[buf] + wave * 32 + r;
 #pragma unroll
-        for (int q = 0; q < kBQ / 2; ++q) dsrow[(2 * q + h) * kSS + wave * 32 + r] = (bf16)0.0f;
+        for (int q = 0; q < kBQ / 2; ++q) dsw[(2 * q + h) * kSS] = (bf16)0.0f;
       }
       if (nxt.hh >= 0) store_qstage<D>(sm, buf ^ 1, qr, tid);
       __syncthreads();
       // dQ[q][32*wave .. +31] += dS[q][:] K[:][...]  (scale already folded into dS)
       if (wave * 32 < D) {
         f32x16 acc = {};
+        const bf16* dsr = sm.ds[buf] + r * kSS + h * 8;
 #pragma unroll
         for (int ks = 0; ks < kBKV / 16; ++ks) {
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sm.ds[buf][r * kSS + ks * 16 + h * 8]);
-          const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.kt[(wave * 32 + r) * kSS + ks * 16 + h * 8]);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dsr + ks * 16);
+          const bf16* p = ktr + ks * 16 * kKS;
+          const bf16x8 bk = concat(lds_read_tr4(p), lds_read_tr4(p + 4 * kKS));
           acc = mfma32x32x16(ad, bk, acc);
         }
+        float* dqp = a.dq + ((int64_t)r0 * a.hq + head) * D + wave * 32 + r;
+        const int64_t rs = (int64_t)a.hq * D;
+        if (r1 - r0 == kBQ) {
 #pragma unroll
-        for (int aa = 0; aa < 16; ++aa) {
-          const int row = r0 + 8 * (aa >> 2) + 4 * h + (aa & 3);
-          if (row < r1)
-            unsafeAtomicAdd(&a.dq[((int64_t)row * a.hq + head) * D + wave * 32 + r], acc[aa]);
+          for (int aa = 0; aa < 16; ++aa)
+            unsafeAtomicAdd(dqp + (8 * (aa >> 2) + 4 * h + (aa & 3)) * rs, acc[aa]);
+        } else {
+#pragma unroll
+          for (int aa = 0; aa < 16; ++aa) {
+            const int q = 8 * (aa >> 2) + 4 * h + (aa & 3);
+            if (r0 + q < r1) unsafeAtomicAdd(dqp + q * rs, acc[aa]);
+          }
         }
       }
       if (nxt.hh < 0) break;

@@ -50,6 +50,37 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Lanes act in groups of 16: lane r of a
+// group supplies the address of four consecutive 16-bit elements, and lane i of the
+// group receives element (i % 4) of the quads supplied by lanes i/4, i/4+4, i/4+8 and
+// i/4+12.  On a row-major [k][n] tile where lane r addresses row k0 + r/4, columns
+// n0 + 4*(r%4) .. +3, lane i therefore receives column n0 + i, rows k0 .. k0+3 — four
+// consecutive contraction elements of one operand column/row, as the matrix cores
+// expect.  Offsets for that addressing: tr_lane_offset().
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Element offset, within a row-major tile of row stride `stride`, that lane `lane`
+// addresses for lds_read_tr4 when the wave reads an operand whose lanes l % 32 own
+// columns n0 + l % 32 and whose lane half h = lane / 32 owns the four contraction rows
+// k0 + half_step*h .. +3: row half_step*h + (i / 4), column 16*(g % 2) + 4*(i % 4), with
+// g = lane / 16, i = lane % 16.  half_step = 4 gives the contraction order of a C-layout
+// B operand (two reads at k0 and k0 + 8 cover one 16-row slice), half_step = 8 the
+// natural order (two reads at k0 and k0 + 4).
+template <int kHalfStep>
+__device__ __forceinline__ int tr_lane_offset(int lane, int stride) {
+  const int g = lane >> 4, i = lane & 15;
+  return (kHalfStep * (g >> 1) + (i >> 2)) * stride + 16 * (g & 1) + 4 * (i & 3);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
 

@@ -16,8 +16,9 @@
 //    then owns one query row (column of S^T), so row max / row sum are in-lane plus
 //    one exchange between the two lane halves.
 //  - P^T (bf16, converted in place from the accumulators) is directly the B operand
-//    of O^T += V^T P^T; V^T is staged in LDS with the contraction order that layout
-//    implies (common.h), so every operand read is one 16-byte LDS load.
+//    of O^T += V^T P^T.  V stays row-major in LDS; its transposed operand comes from
+//    two transposing LDS reads (ds_read_b64_tr_b16) per product, addressed in the
+//    contraction order the accumulator layout implies (common.h).
 //  - The scale is applied to the fp32 scores (folded with log2 e into exp2).
 //  - The running maximum is only moved when a new score exceeds it by more than
 //    2^8 (probabilities stay <= 256, exact in fp32 and bf16 range), so the O rescale
@@ -43,10 +44,10 @@ constexpr int kPosPad = 0x7fffffff;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int kKS = D + 8;     // K row stride (elements), 16-byte pad
-  static constexpr int kVS = kBK + 8;   // V^T row stride (elements), 16-byte pad
+  static constexpr int kKS = D + 8;    // K row stride: 16-byte pad, row reads conflict-free
+  static constexpr int kVS = D + 16;   // V row stride: 32-byte pad, transposing reads conflict-free
   bf16 k[2][kBK * kKS];
-  bf16 vt[2][D * kVS];
+  bf16 v[2][kBK * kVS];
   int32_t kpos[2][kBK];
   int32_t kdoc[2][kBK];
 };
@@ -59,19 +60,26 @@ struct TileRef {
 // Next KV tile at or after (s, t) that the query range can see; seg = -1 if none.
 __device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int s, int t, int qmin,
                                              int qmax, int qdmin, int qdmax) {
+  const int mask = a.mask;
   for (; s < seg_end; ++s, t = 0) {
-    const SegDesc& sg = a.segs[s];
-    const int nt = (sg.len + kBK - 1) / kBK;
+    const int len = a.segs[s].len;
+    const int32_t* pos = a.segs[s].pos;
+    const int32_t* doc = a.segs[s].doc;
+    const int nt = (len + kBK - 1) / kBK;
     for (; t < nt; ++t) {
       const int k0 = t * kBK;
-      const int k1 = min(sg.len, k0 + kBK) - 1;
+      const int k1 = min(len, k0 + kBK) - 1;
+      if (mask == kMaskNone) return {s, t};
+      const int kmin = pos[k0];
+      // positions ascend inside a segment: once a tile starts after the last query,
+      // no later tile of that segment is visible either
+      if (kmin > qmax) break;
       int kdmin = 0, kdmax = 0;
-      if (a.mask == kMaskCausalDoc) {
-        kdmin = sg.doc[k0];
-        kdmax = sg.doc[k1];
+      if (mask == kMaskCausalDoc) {
+        kdmin = doc[k0];
+        kdmax = doc[k1];
       }
-      const int cls = classify(a.mask, qmin, qmax, qdmin, qdmax, sg.pos[k0], sg.pos[k1], kdmin, kdmax);
-      if (cls != kTileEmpty) return {s, t};
+      if (classify(mask, qmin, qmax, qdmin, qdmax, kmin, pos[k1], kdmin, kdmax) != kTileEmpty) return {s, t};
     }
   }
   return {-1, 0};
@@ -79,9 +87,9 @@ __device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int 
 
 template <int D>
 struct TileRegs {
-  static constexpr int kKChunks = kBK * D / 8 / kThreads;  // 16-byte K chunks per thread
-  u32x4 k[kKChunks];
-  u32x4 v[4];
+  static constexpr int kChunks = kBK * D / 8 / kThreads;  // 16-byte chunks per thread (K and V)
+  u32x4 k[kChunks];
+  u32x4 v[kChunks];
   int32_t pos;
   int32_t doc;
 };
@@ -95,24 +103,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const SegDesc& sg, int
   const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
   constexpr int kCPK = D / 8;  // chunks per key row
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKChunks; ++i) {
+  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
     const int c = tid + i * kThreads;
     const int key = c / kCPK, dc = c % kCPK;
-    if (key < klen)
-      r.k[i] = *reinterpret_cast<const u32x4*>(kb + ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8);
-    else
+    if (key < klen) {
+      const int64_t off = ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8;
+      r.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
+    } else {
       r.k[i] = u32x4{0, 0, 0, 0};
-  }
-  // V: unit = (group of 4 consecutive keys, 8 consecutive dims)
-  const int m = tid & 15, dc = tid >> 4;
-  if (dc < D / 8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 4 * m + i;
-      if (key < klen)
-        r.v[i] = *reinterpret_cast<const u32x4*>(vb + ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8);
-      else
-        r.v[i] = u32x4{0, 0, 0, 0};
+      r.v[i] = u32x4{0, 0, 0, 0};
     }
   }
   if (tid < kBK) {
@@ -126,23 +126,11 @@ __device__ __forceinline__ void store_tile(FwdSmem<D>& sm, int buf, const TileRe
   constexpr int kCPK = D / 8;
   constexpr int kKS = FwdSmem<D>::kKS, kVS = FwdSmem<D>::kVS;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKChunks; ++i) {
+  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
     const int c = tid + i * kThreads;
     const int key = c / kCPK, dc = c % kCPK;
     *reinterpret_cast<u32x4*>(&sm.k[buf][key * kKS + dc * 8]) = r.k[i];
-  }
-  const int m = tid & 15, dc = tid >> 4;
-  if (dc < D / 8) {
-    const int col = perm16(4 * m);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // dim dc*8+e of keys 4m..4m+3 -> four consecutive V^T columns
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (r.v[0][w] >> sh) & 0xffffu, x1 = (r.v[1][w] >> sh) & 0xffffu;
-      const uint32_t x2 = (r.v[2][w] >> sh) & 0xffffu, x3 = (r.v[3][w] >> sh) & 0xffffu;
-      u32x2 packed = {x0 | (x1 << 16), x2 | (x3 << 16)};
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + e) * kVS + col]) = packed;
-    }
+    *reinterpret_cast<u32x4*>(&sm.v[buf][key * kVS + dc * 8]) = r.v[i];
   }
   if (tid < kBK) {
     sm.kpos[buf][tid] = r.pos;
@@ -152,7 +140,7 @@ __device__ __forceinline__ void store_tile(FwdSmem<D>& sm, int buf, const TileRe
 
 // One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
 template <int D, bool MASKED>
-__device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf16* __restrict__ vt,
+__device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf16* __restrict__ vs,
                                           const int32_t* kpos, const int32_t* kdoc, int klen,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           float& m, float& l, int qpos, int qdoc, int mask,
@@ -167,11 +155,12 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
     s0 = mfma32x32x16(a0, qf[ds], s0);
     s1 = mfma32x32x16(a1, qf[ds], s1);
   }
+  // raw scores; the softmax scale (times log2 e) is applied inside the exp argument
   float x[32];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    x[i] = s0[i] * scale_log2;
-    x[16 + i] = s1[i] * scale_log2;
+    x[i] = s0[i];
+    x[16 + i] = s1[i];
   }
   if (MASKED) {
 #pragma unroll
@@ -189,7 +178,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
           bool vis = base + e < klen;
           if (mask != kMaskNone) vis = vis && kpa[e] <= qpos;
           if (mask == kMaskCausalDoc) vis = vis && kda[e] == qdoc;
-          if (!vis) x[kb * 16 + g * 4 + e] = neg_inf();
+          x[kb * 16 + g * 4 + e] = vis ? x[kb * 16 + g * 4 + e] : neg_inf();
         }
       }
     }
@@ -197,7 +186,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   float mt = x[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-  mt = fmaxf(mt, swap_halves(mt));
+  mt = fmaxf(mt, swap_halves(mt)) * scale_log2;  // -inf stays -inf (scale > 0)
   const float m_new = fmaxf(m, mt);
   const bool need = m_new > m + kTau;
   if (__any(need)) {
@@ -214,17 +203,21 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(x[j * 8 + e] - mu);
+      const float p = fast_exp2(fmaf(x[j * 8 + e], scale_log2, -mu));
       rs += p;
       pf[j][e] = (bf16)p;
     }
   }
   l += rs;
+  // O^T += V^T P^T: the V^T operand of key slice j (keys 16j..16j+15, in the order
+  // of P^T's rows) for dims 32db..32db+31 is two transposing reads of row-major V.
+  const bf16* vl = vs + tr_lane_offset<4>(lane, kVS);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (db * 32 + r) * kVS + j * 16 + h * 8);
+      const bf16* p = vl + j * 16 * kVS + db * 32;
+      const bf16x8 a = concat(lds_read_tr4(p), lds_read_tr4(p + 8 * kVS));
       o[db] = mfma32x32x16(a, pf[j], o[db]);
     }
   }
@@ -314,10 +307,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                             mask == kMaskCausalDoc ? kd[klen - 1] : 0);
         if (wcls == kTileFull && klen < kBK) wcls = kTilePartial;
         if (wcls == kTileFull)
-          tile_step<D, false>(sm.k[buf], sm.vt[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
+          tile_step<D, false>(sm.k[buf], sm.v[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
                               a.scale_log2, lane);
         else if (wcls == kTilePartial)
-          tile_step<D, true>(sm.k[buf], sm.vt[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
+          tile_step<D, true>(sm.k[buf], sm.v[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
                              a.scale_log2, lane);
       }
       if (nxt.seg < 0) break;

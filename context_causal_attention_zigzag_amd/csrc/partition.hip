@@ -15,19 +15,19 @@ namespace cpattn {
 
 namespace {
 
-constexpr int kRowsPerBlock = 64;
 constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;
 constexpr int kMaxGather = 8;
 
 struct PartArgs {
   const void* src[kMaxGather];
   void* dst[kMaxGather];
-  int64_t row_bytes[kMaxGather];
-  const int32_t* cu;   // device cu_seqlens (THD) or null (zigzag)
+  int32_t vpr[kMaxGather];  // 16-byte vectors per row of each tensor
+  const int32_t* cu;        // device cu_seqlens (THD) or null (zigzag)
   int32_t* idx;
   int32_t* doc;
   int64_t total;
-  int64_t local;       // total / cp
+  int64_t local;            // total / cp
   int32_t n_docs;
   int32_t cp;
   int32_t rank;
@@ -39,8 +39,8 @@ __device__ __forceinline__ void local_to_global(const PartArgs& a, int64_t t, in
   int64_t start = 0, len = a.total;
   int lo = 0;
   if (a.cu != nullptr) {
-    // largest k with cu[k]/cp <= t
-    int hi = a.n_docs;  // cu[n_docs]/cp == local > t
+    // largest k with cu[k]/cp <= t (cu[n_docs]/cp == local > t)
+    int hi = a.n_docs;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if ((int64_t)a.cu[mid] / a.cp <= t) lo = mid; else hi = mid;
@@ -55,34 +55,58 @@ __device__ __forceinline__ void local_to_global(const PartArgs& a, int64_t t, in
   docid = lo;
 }
 
+// grid.y selects the tensor (or, with no tensors, only the index output); every
+// thread moves kVecPerThread 16-byte vectors of one destination row segment.
 __global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
-  __shared__ int64_t rows[kRowsPerBlock];
-  const int64_t t0 = (int64_t)blockIdx.x * kRowsPerBlock;
-  const int tid = threadIdx.x;
-  if (tid < kRowsPerBlock) {
-    const int64_t t = t0 + tid;
-    if (t < a.local) {
-      int64_t row;
-      int32_t d;
+  const int g = blockIdx.y;
+  const int vpr = a.n_gather > 0 ? a.vpr[g] : 1;
+  const int64_t nvec = a.local * vpr;
+  const int64_t v0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVecPerThread;
+  if (v0 >= nvec) return;
+  int64_t row;
+  int32_t d;
+  if (a.n_gather == 0) {  // indices only: one row per vector
+    for (int i = 0; i < kVecPerThread && v0 + i < nvec; ++i) {
+      local_to_global(a, v0 + i, row, d);
+      a.idx[v0 + i] = (int32_t)row;
+      if (a.doc) a.doc[v0 + i] = d;
+    }
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.src[g]);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.dst[g]);
+  int64_t t = v0 / vpr;
+  int c = (int)(v0 - t * vpr);
+  local_to_global(a, t, row, d);
+  if (g == 0 && c == 0) {
+    a.idx[t] = (int32_t)row;
+    if (a.doc) a.doc[t] = d;
+  }
+  u32x4 buf[kVecPerThread];
+  int64_t drow[kVecPerThread];
+  int cc[kVecPerThread];
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i) {
+    if (v0 + i >= nvec) break;
+    if (c == vpr) {  // next destination row
+      ++t;
+      c = 0;
       local_to_global(a, t, row, d);
-      rows[tid] = row;
-      a.idx[t] = (int32_t)row;
-      if (a.doc) a.doc[t] = d;
+      if (g == 0) {
+        a.idx[t] = (int32_t)row;
+        if (a.doc) a.doc[t] = d;
+      }
     }
+    drow[i] = t;
+    cc[i] = c;
+    buf[i] = __builtin_nontemporal_load(&src[row * vpr + c]);
+    ++c;
+    ++n;
   }
-  __syncthreads();
-  const int nrows = (int)min((int64_t)kRowsPerBlock, a.local - t0);
-  for (int g = 0; g < a.n_gather; ++g) {
-    const int vpr = (int)(a.row_bytes[g] >> 4);  // 16-byte vectors per row
-    const int nvec = vpr * nrows;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.src[g]);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.dst[g]);
-    for (int i = tid; i < nvec; i += kThreads) {
-      const int r = i / vpr;
-      const int c = i - r * vpr;
-      dst[(t0 + r) * vpr + c] = __builtin_nontemporal_load(&src[rows[r] * vpr + c]);
-    }
-  }
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i)
+    if (i < n) dst[drow[i] * vpr + cc[i]] = buf[i];
 }
 
 }  // namespace
@@ -92,23 +116,28 @@ hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int
                             const void* const* src, void* const* dst, const int64_t* row_bytes,
                             hipStream_t stream) {
   PartArgs a{};
+  int64_t max_vec = 0;
+  a.local = total / cp;
   for (int g = 0; g < n_gather; ++g) {
     a.src[g] = src[g];
     a.dst[g] = dst[g];
-    a.row_bytes[g] = row_bytes[g];
+    a.vpr[g] = (int32_t)(row_bytes[g] / 16);
+    max_vec = max_vec > a.local * a.vpr[g] ? max_vec : a.local * a.vpr[g];
   }
+  if (n_gather == 0) max_vec = a.local;
   a.cu = mode == 1 ? cu_dev : nullptr;
   a.idx = idx;
   a.doc = doc;
   a.total = total;
-  a.local = total / cp;
   a.n_docs = mode == 1 ? n_docs : 1;
   a.cp = cp;
   a.rank = rank;
   a.n_gather = n_gather;
   if (a.local == 0) return hipSuccess;
-  const int64_t blocks = (a.local + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  const int64_t per_block = (int64_t)kThreads * kVecPerThread;
+  const int64_t blocks = (max_vec + per_block - 1) / per_block;
+  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)blocks, n_gather > 0 ? n_gather : 1), dim3(kThreads),
+                     0, stream, a);
   return hipGetLastError();
 }
 
