@@ -62,9 +62,12 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdSmem {
-  static constexpr int kRS = D + 8;     // Q / dO row stride (row reads and transposing reads)
-  static constexpr int kKS = D + 16;    // K row stride (transposing reads only)
-  static constexpr int kSS = kBKV + 8;  // dS row stride (row reads)
+  // Row strides for gfx950's 64-bank LDS: transposing reads are conflict-free at 16
+  // (mod 64) dwords, 16-byte row reads at 4 (mod 16) dwords.  Q and dO serve both
+  // (twice as many transposing reads), K only transposing reads, dS only row reads.
+  static constexpr int kRS = D + 32;    // Q / dO
+  static constexpr int kKS = D + 32;    // K
+  static constexpr int kSS = kBKV + 8;  // dS
   bf16 qs[2][kBQ * kRS];
   bf16 dos[2][kBQ * kRS];
   float lse2[2][kBQ];

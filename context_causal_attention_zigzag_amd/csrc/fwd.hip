@@ -44,8 +44,10 @@ constexpr int kPosPad = 0x7fffffff;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int kKS = D + 8;    // K row stride: 16-byte pad, row reads conflict-free
-  static constexpr int kVS = D + 16;   // V row stride: 32-byte pad, transposing reads conflict-free
+  // Row strides measured conflict-free on gfx950's 64-bank LDS: 16-byte row reads
+  // need a stride of 4 (mod 16) dwords, transposing reads 16 (mod 64) dwords.
+  static constexpr int kKS = D + 8;    // K: row reads
+  static constexpr int kVS = D + 32;   // V: transposing reads
   bf16 k[2][kBK * kKS];
   bf16 v[2][kBK * kVS];
   int32_t kpos[2][kBK];
