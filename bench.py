@@ -66,6 +66,8 @@ def main():
     o_s = torch.empty_like(rs.q)
     l_s = torch.empty_like(l_t)
     bwd_bufs = rs.alloc_bwd_buffers(gran)
+    ws_tile = rs.tile_workspace(edges)
+    ws_stream = rs.stream_workspace(gran)
     # partition outputs of this rank (Q and its own K/V shard), rewritten every step
     p_idx = torch.empty(n_local, dtype=torch.int32, device=dev)
     p_out = [torch.empty((n_local,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in (gq, gk, gv)]
@@ -85,11 +87,11 @@ def main():
         mark()
         C.cpattn_partition(C.PART_ZIGZAG, w.seq, w.cp, r, p_idx, None, [gq, gk, gv], p_out)
         mark()
-        rs.tile_fwd(edges, parts)
+        rs.tile_fwd(edges, parts, workspace=ws_tile)
         mark()
         rs.merge(edges, parts, o_t, l_t)
         mark()
-        rs.stream_fwd(gran, o_s, l_s)
+        rs.stream_fwd(gran, o_s, l_s, workspace=ws_stream)
         mark()
         rs.bwd(o_s, l_s, g, bwd_bufs, gran)
         mark()

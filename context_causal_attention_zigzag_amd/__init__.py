@@ -56,14 +56,20 @@ lib.cpattn_partition.argtypes = [_c_i32, _c_i64, _c_i32, _c_i32, _P(_c_i32), _c_
                                  _c_vp, _c_i32, _P(_c_vp), _P(_c_vp), _P(_c_i64), _c_vp]
 lib.cpattn_partition.restype = _c_i32
 lib.cpattn_tile_fwd.argtypes = [_P(cpattn_attn_desc), _c_i32, _P(cpattn_q_block), _P(cpattn_kv_seg),
-                                _P(_c_vp), _P(_c_vp), _c_vp]
+                                _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
 lib.cpattn_tile_fwd.restype = _c_i32
+lib.cpattn_tile_fwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _c_i32, _P(cpattn_q_block),
+                                                _P(cpattn_kv_seg)]
+lib.cpattn_tile_fwd_workspace_bytes.restype = _c_sz
 lib.cpattn_merge.argtypes = [_c_i32, _P(_c_vp), _P(_c_vp), _c_i64, _c_i32, _c_i32, _c_i32, _c_vp,
                              _c_vp, _c_vp]
 lib.cpattn_merge.restype = _c_i32
 lib.cpattn_stream_fwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
-                                  _P(cpattn_kv_seg), _c_vp, _c_vp, _c_vp]
+                                  _P(cpattn_kv_seg), _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
 lib.cpattn_stream_fwd.restype = _c_i32
+lib.cpattn_stream_fwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
+                                                  _P(cpattn_kv_seg)]
+lib.cpattn_stream_fwd_workspace_bytes.restype = _c_sz
 lib.cpattn_bwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
                            _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
 lib.cpattn_bwd.restype = _c_i32
@@ -71,7 +77,8 @@ lib.cpattn_bwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _c_i64]
 lib.cpattn_bwd_workspace_bytes.restype = _c_sz
 
 EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
-            "cpattn_merge", "cpattn_stream_fwd", "cpattn_bwd", "cpattn_bwd_workspace_bytes")
+            "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
+            "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes")
 
 
 class CpattnError(RuntimeError):
@@ -154,15 +161,42 @@ def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out,
     _check(st, "cpattn_partition")
 
 
-def cpattn_tile_fwd(desc: cpattn_attn_desc, q_blocks, segs, o_parts, lse_parts, stream=None):
-    """TileAttention for every (q_blocks[e], segs[e]) edge into (o_parts[e], lse_parts[e])."""
+def _workspace(nbytes, like):
+    """A device buffer of ``nbytes`` (None for 0), allocated through torch."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def cpattn_tile_fwd_workspace_bytes(desc: cpattn_attn_desc, q_blocks, segs) -> int:
+    n = len(q_blocks)
+    qa = (cpattn_q_block * max(1, n))(*q_blocks)
+    sa = (cpattn_kv_seg * max(1, n))(*segs)
+    return int(lib.cpattn_tile_fwd_workspace_bytes(ctypes.byref(desc), n, qa, sa))
+
+
+def cpattn_tile_fwd(desc: cpattn_attn_desc, q_blocks, segs, o_parts, lse_parts, workspace="auto",
+                    stream=None):
+    """TileAttention for every (q_blocks[e], segs[e]) edge into (o_parts[e], lse_parts[e]).
+
+    ``workspace``: a uint8 device tensor, None (no KV split), or "auto" (sized with
+    cpattn_tile_fwd_workspace_bytes and allocated here)."""
     n = len(q_blocks)
     if not (len(segs) == len(o_parts) == len(lse_parts) == n):
         raise ValueError("one q block, segment, O and LSE buffer per edge")
+    if isinstance(workspace, str):
+        workspace = _workspace(cpattn_tile_fwd_workspace_bytes(desc, q_blocks, segs), o_parts[0]) if n else None
     qa = (cpattn_q_block * max(1, n))(*q_blocks)
     sa = (cpattn_kv_seg * max(1, n))(*segs)
+    wp, wb = _ws_args(workspace)
     st = lib.cpattn_tile_fwd(ctypes.byref(desc), n, qa, sa, _vp_array([_ptr(o) for o in o_parts]),
-                             _vp_array([_ptr(x) for x in lse_parts]), _stream(stream))
+                             _vp_array([_ptr(x) for x in lse_parts]), wp, wb, _stream(stream))
     _check(st, "cpattn_tile_fwd")
 
 
@@ -177,11 +211,22 @@ def cpattn_merge(o_parts, lse_parts, o_out, lse_out, stream=None):
     _check(st, "cpattn_merge")
 
 
-def cpattn_stream_fwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o_out, lse_out, stream=None):
-    """Streaming online-softmax attention of ``q`` over ``segs`` in arrival order."""
+def cpattn_stream_fwd_workspace_bytes(desc: cpattn_attn_desc, q: cpattn_q_block, segs) -> int:
     sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    return int(lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(q), len(segs), sa))
+
+
+def cpattn_stream_fwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o_out, lse_out, workspace="auto",
+                      stream=None):
+    """Streaming online-softmax attention of ``q`` over ``segs`` in arrival order.
+
+    ``workspace`` as for cpattn_tile_fwd (cpattn_stream_fwd_workspace_bytes)."""
+    if isinstance(workspace, str):
+        workspace = _workspace(cpattn_stream_fwd_workspace_bytes(desc, q, segs), o_out) if o_out is not None else None
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    wp, wb = _ws_args(workspace)
     st = lib.cpattn_stream_fwd(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o_out),
-                               _ptr(lse_out), _stream(stream))
+                               _ptr(lse_out), wp, wb, _stream(stream))
     _check(st, "cpattn_stream_fwd")
 
 

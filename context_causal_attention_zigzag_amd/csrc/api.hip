@@ -74,6 +74,66 @@ SegDesc to_seg(const cpattn_kv_seg& s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_ERR_HIP; }
 
+// Compute units of the current device (256 when no device is visible, for planning).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+int check_tile_args(const cpattn_attn_desc* desc, int32_t n_edges, const cpattn_q_block* q_blocks,
+                    const cpattn_kv_seg* segs) {
+  int st = check_desc(desc);
+  if (st != CPATTN_OK) return st;
+  if (n_edges < 0) return CPATTN_ERR_ARG;
+  if (n_edges == 0) return CPATTN_OK;
+  if (q_blocks == nullptr || segs == nullptr) return CPATTN_ERR_ARG;
+  for (int e = 0; e < n_edges; ++e) {
+    if ((st = check_qblock(desc, &q_blocks[e])) != CPATTN_OK) return st;
+    if ((st = check_seg(desc, &segs[e])) != CPATTN_OK) return st;
+  }
+  return CPATTN_OK;
+}
+
+// Fills one launch's worth of edges starting at *e; returns false when none are left.
+bool next_edge_batch(FwdArgs& a, int32_t n_edges, const cpattn_q_block* q_blocks, const cpattn_kv_seg* segs,
+                     float* const* o_parts, float* const* lse_parts, int& e) {
+  a.n_jobs = 0;
+  for (; e < n_edges && a.n_jobs < kMaxJobs; ++e) {
+    if (q_blocks[e].len == 0) continue;
+    const int j = a.n_jobs++;
+    a.segs[j] = to_seg(segs[e]);
+    JobDesc& jb = a.jobs[j];
+    jb = JobDesc{};
+    jb.q = q_blocks[e].q;
+    jb.pos = q_blocks[e].pos;
+    jb.doc = q_blocks[e].doc;
+    jb.o = o_parts ? o_parts[e] : nullptr;
+    jb.lse = lse_parts ? lse_parts[e] : nullptr;
+    jb.len = (int32_t)q_blocks[e].len;
+    jb.seg_begin = j;
+    jb.seg_end = j + 1;
+  }
+  return a.n_jobs > 0;
+}
+
+void fill_stream_job(FwdArgs& a, const cpattn_q_block* q, int32_t n_segs, const cpattn_kv_seg* segs,
+                     void* o_out, float* lse_out) {
+  for (int s = 0; s < n_segs; ++s) a.segs[s] = to_seg(segs[s]);
+  a.n_jobs = 1;
+  JobDesc& jb = a.jobs[0];
+  jb = JobDesc{};
+  jb.q = q->q;
+  jb.pos = q->pos;
+  jb.doc = q->doc;
+  jb.o = o_out;
+  jb.lse = lse_out;
+  jb.len = (int32_t)q->len;
+  jb.seg_begin = 0;
+  jb.seg_end = n_segs;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,43 +183,42 @@ int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_ra
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t cpattn_tile_fwd_workspace_bytes(const cpattn_attn_desc* desc, int32_t n_edges,
+                                       const cpattn_q_block* q_blocks, const cpattn_kv_seg* segs) {
+  if (check_tile_args(desc, n_edges, q_blocks, segs) != CPATTN_OK) return 0;
+  FwdArgs a{};
+  fill_common(a, desc);
+  const int cus = device_cus();
+  size_t need = 0;
+  int e = 0;
+  while (next_edge_batch(a, n_edges, q_blocks, segs, nullptr, nullptr, e)) {
+    const size_t b = plan_fwd(a, desc->d, desc->dtype, cus, true);
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
 int cpattn_tile_fwd(const cpattn_attn_desc* desc, int32_t n_edges, const cpattn_q_block* q_blocks,
                     const cpattn_kv_seg* segs, float* const* o_parts, float* const* lse_parts,
-                    void* stream) {
-  int st = check_desc(desc);
-  if (st != CPATTN_OK) return st;
-  if (n_edges < 0) return CPATTN_ERR_ARG;
-  if (n_edges == 0) return CPATTN_OK;
-  if (q_blocks == nullptr || segs == nullptr || o_parts == nullptr || lse_parts == nullptr)
-    return CPATTN_ERR_ARG;
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_tile_args(desc, n_edges, q_blocks, segs);
+  if (st != CPATTN_OK || n_edges == 0) return st;
+  if (o_parts == nullptr || lse_parts == nullptr) return CPATTN_ERR_ARG;
   for (int e = 0; e < n_edges; ++e) {
-    if ((st = check_qblock(desc, &q_blocks[e])) != CPATTN_OK) return st;
-    if ((st = check_seg(desc, &segs[e])) != CPATTN_OK) return st;
     if (q_blocks[e].len > 0) {
       if (o_parts[e] == nullptr || lse_parts[e] == nullptr) return CPATTN_ERR_ARG;
       if (!aligned16(o_parts[e])) return CPATTN_ERR_ALIGN;
     }
   }
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
   FwdArgs a{};
   fill_common(a, desc);
+  const int cus = device_cus();
   int e = 0;
-  while (e < n_edges) {
-    a.n_jobs = 0;
-    for (; e < n_edges && a.n_jobs < kMaxJobs; ++e) {
-      if (q_blocks[e].len == 0) continue;
-      const int j = a.n_jobs++;
-      a.segs[j] = to_seg(segs[e]);
-      JobDesc& jb = a.jobs[j];
-      jb.q = q_blocks[e].q;
-      jb.pos = q_blocks[e].pos;
-      jb.doc = q_blocks[e].doc;
-      jb.o = o_parts[e];
-      jb.lse = lse_parts[e];
-      jb.len = (int32_t)q_blocks[e].len;
-      jb.seg_begin = j;
-      jb.seg_end = j + 1;
-    }
-    if (a.n_jobs == 0) continue;
+  while (next_edge_batch(a, n_edges, q_blocks, segs, o_parts, lse_parts, e)) {
+    size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr);
+    if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false);  // too small: no split
+    if (need > 0) assign_fwd_workspace(a, desc->d, workspace);
     st = hip_status(launch_fwd(a, desc->d, desc->dtype, true, reinterpret_cast<hipStream_t>(stream)));
     if (st != CPATTN_OK) return st;
   }
@@ -184,8 +243,21 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
+                                         int32_t n_segs, const cpattn_kv_seg* segs) {
+  if (check_desc(desc) != CPATTN_OK || check_qblock(desc, q) != CPATTN_OK) return 0;
+  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr || q->len == 0) return 0;
+  for (int s = 0; s < n_segs; ++s)
+    if (check_seg(desc, &segs[s]) != CPATTN_OK) return 0;
+  FwdArgs a{};
+  fill_common(a, desc);
+  fill_stream_job(a, q, n_segs, segs, nullptr, nullptr);
+  return plan_fwd(a, desc->d, desc->dtype, device_cus(), true);
+}
+
 int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
-                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* stream) {
+                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int st = check_desc(desc);
   if (st != CPATTN_OK) return st;
   if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
@@ -195,19 +267,14 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   if (q->len == 0) return CPATTN_OK;
   if (o_out == nullptr || lse_out == nullptr) return CPATTN_ERR_ARG;
   if (!aligned16(o_out)) return CPATTN_ERR_ALIGN;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
   FwdArgs a{};
   fill_common(a, desc);
-  for (int s = 0; s < n_segs; ++s) a.segs[s] = to_seg(segs[s]);
-  a.n_jobs = 1;
-  JobDesc& jb = a.jobs[0];
-  jb.q = q->q;
-  jb.pos = q->pos;
-  jb.doc = q->doc;
-  jb.o = o_out;
-  jb.lse = lse_out;
-  jb.len = (int32_t)q->len;
-  jb.seg_begin = 0;
-  jb.seg_end = n_segs;
+  fill_stream_job(a, q, n_segs, segs, o_out, lse_out);
+  const int cus = device_cus();
+  size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr);
+  if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false);  // too small: no split
+  if (need > 0) assign_fwd_workspace(a, desc->d, workspace);
   return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -225,6 +292,7 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   if (st != CPATTN_OK) return st;
   if (desc->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
   if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
+  if (q->len > bwd_max_rows()) return CPATTN_ERR_UNSUPPORTED;
   if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr || dk == nullptr || dv == nullptr)
     return CPATTN_ERR_ARG;
   for (int s = 0; s < n_segs; ++s) {
@@ -249,7 +317,7 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   }
   a.q = q->q;
   a.qpos = q->pos;
-  a.qdoc = q->doc;
+  a.qdoc = q->doc != nullptr ? q->doc : q->pos;  // always a readable array (read, unused)
   a.o = o;
   a.lse = lse;
   a.dout = dout;

@@ -20,8 +20,8 @@
 //    cores straight from the accumulators.  dS goes through LDS once more for
 //    dQ = dS K (K^T slices read transposed from a row-major K tile), computed per
 //    32-dim slice by each wave and added to the fp32 dQ with coalesced atomics.
-//  - one barrier per query tile; the next tile's global loads overlap the current
-//    tile's matrix work.
+//  - one LDS-only barrier per query tile; query tiles are staged two ahead so the
+//    staging loads never wait behind the dQ atomics (see the main loop).
 #include "common.h"
 
 namespace cpattn {
@@ -32,6 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per work-group (32 per wave)
 constexpr int kBQ = 32;    // query rows per step
 constexpr int kPosPad = 0x7fffffff;
+constexpr int kMaxQTiles = 2048;  // query tiles of the LDS range table (65536 local rows)
 
 // ---------------------------------------------------------------------------
 template <int D>
@@ -76,50 +77,49 @@ struct BwdSmem {
   int32_t qdoc[2][kBQ];
   bf16 ds[2][kBQ * kSS];
   bf16 ks[kBKV * kKS];
+  // first/last position and document of every query tile, so the per-tile
+  // classification reads LDS instead of global memory (a vector load there would
+  // wait behind the outstanding dQ atomics)
+  int32_t qtab[4][kMaxQTiles];
 };
 
 template <int D>
 struct QStageRegs {
   static constexpr int kChunks = kBQ * D / 8 / 128;  // 16-byte chunks per thread
-  u32x4 x[kChunks];  // rows of Q (threads 0..127) or of dO (threads 128..255)
-  float lse2, delta;
+  u32x4 x[kChunks];  // rows of Q (threads 0..127) or of dO (threads 128..255), raw
+  float lse, delta;  // raw values of row r0 + (tid % 32), clamped to the last row
   int32_t pos, doc;
+  int32_t r0;        // first row of the staged tile
 };
 
+// Every lane issues the same loads on every call (rows past the end are clamped):
+// the number of vector-memory operations between these loads and their use is then
+// the same on every path, so the wait at the LDS store leaves the younger dQ atomics
+// in flight.  Nothing here touches the loaded values; store_qstage() zeroes the rows
+// past the end and converts the LSE.
 template <int D>
-__device__ __forceinline__ void load_qstage(QStageRegs<D>& r, const BwdArgs& a, int head, int r0, int tid) {
+__device__ __forceinline__ void load_qstage(QStageRegs<D>& r, const BwdArgs& a, const bf16* base, int head,
+                                            int r0, int tid) {
   constexpr int kCPR = D / 8;
-  const int half = tid >> 7;  // 0: Q, 1: dO
   const int u = tid & 127;
-  const bf16* base = reinterpret_cast<const bf16*>(half ? a.dout : a.q);
+  const int last = a.q_len - 1;
 #pragma unroll
   for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
     const int c = u + 128 * i;
-    const int row = r0 + c / kCPR, dc = c % kCPR;
-    if (row < a.q_len)
-      r.x[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8);
-    else
-      r.x[i] = u32x4{0, 0, 0, 0};
+    const int row = min(r0 + c / kCPR, last), dc = c % kCPR;
+    r.x[i] = *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8);
   }
-  if (tid < kBQ) {
-    const int row = r0 + tid;
-    if (row < a.q_len) {
-      const float l = a.lse[(int64_t)row * a.hq + head];
-      r.lse2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // a row with no key adds nothing
-      r.delta = a.delta[(int64_t)row * a.hq + head];
-      r.pos = a.qpos[row];
-      r.doc = a.mask == kMaskCausalDoc ? a.qdoc[row] : 0;
-    } else {
-      r.lse2 = __builtin_inff();
-      r.delta = 0.0f;
-      r.pos = -kPosPad - 1;  // sees nothing
-      r.doc = 0;
-    }
-  }
+  const int64_t rr = min(r0 + (tid & (kBQ - 1)), last);
+  r.lse = a.lse[rr * a.hq + head];
+  r.delta = a.delta[rr * a.hq + head];
+  r.pos = a.qpos[rr];
+  r.doc = a.qdoc[rr];  // a valid array for every mask (the host passes positions when unused)
+  r.r0 = r0;
 }
 
 template <int D>
-__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs<D>& r, int tid) {
+__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs<D>& r, int q_len,
+                                             int mask, int tid) {
   constexpr int kCPR = D / 8, kRS = BwdSmem<D>::kRS;
   const int half = tid >> 7;
   const int u = tid & 127;
@@ -127,13 +127,18 @@ __device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QSta
 #pragma unroll
   for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
     const int c = u + 128 * i;
-    *reinterpret_cast<u32x4*>(&dst[(c / kCPR) * kRS + (c % kCPR) * 8]) = r.x[i];
+    const bool ok = r.r0 + c / kCPR < q_len;
+    const u32x4 x = r.x[i];
+    *reinterpret_cast<u32x4*>(&dst[(c / kCPR) * kRS + (c % kCPR) * 8]) =
+        u32x4{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
   }
   if (tid < kBQ) {
-    sm.lse2[buf][tid] = r.lse2;
-    sm.delta[buf][tid] = r.delta;
-    sm.qpos[buf][tid] = r.pos;
-    sm.qdoc[buf][tid] = r.doc;
+    const bool ok = r.r0 + tid < q_len;
+    // a row past the end, or one with no visible key, contributes nothing
+    sm.lse2[buf][tid] = (ok && r.lse != neg_inf()) ? r.lse * kLog2e : __builtin_inff();
+    sm.delta[buf][tid] = ok ? r.delta : 0.0f;
+    sm.qpos[buf][tid] = ok ? r.pos : -kPosPad - 1;
+    sm.qdoc[buf][tid] = mask == kMaskCausalDoc ? r.doc : 0;
   }
 }
 
@@ -142,18 +147,24 @@ struct QRef {
   int qt;  // query tile
 };
 
+// Position / document range of query tile t (LDS table).
+struct QRange {
+  int pmin, pmax, dmin, dmax;
+};
+
+template <int D>
+__device__ __forceinline__ QRange qrange(const BwdSmem<D>& sm, int t) {
+  return {sm.qtab[0][t], sm.qtab[1][t], sm.qtab[2][t], sm.qtab[3][t]};
+}
+
 // Next visible (head, query tile) at or after (hh, qt) for the key range [kmin, kmax].
-__device__ __forceinline__ QRef next_qtile(const BwdArgs& a, int hh, int qt, int n_qt, int kmin,
-                                           int kmax, int kdmin, int kdmax) {
+template <int D>
+__device__ __forceinline__ QRef next_qtile(const BwdSmem<D>& sm, const BwdArgs& a, int hh, int qt,
+                                           int n_qt, int kmin, int kmax, int kdmin, int kdmax) {
   for (; hh < a.group; ++hh, qt = 0) {
     for (; qt < n_qt; ++qt) {
-      const int r0 = qt * kBQ, r1 = min(a.q_len, r0 + kBQ) - 1;
-      int qdmin = 0, qdmax = 0;
-      if (a.mask == kMaskCausalDoc) {
-        qdmin = a.qdoc[r0];
-        qdmax = a.qdoc[r1];
-      }
-      if (classify(a.mask, a.qpos[r0], a.qpos[r1], qdmin, qdmax, kmin, kmax, kdmin, kdmax) != kTileEmpty)
+      const QRange q = qrange(sm, qt);
+      if (classify(a.mask, q.pmin, q.pmax, q.dmin, q.dmax, kmin, kmax, kdmin, kdmax) != kTileEmpty)
         return {hh, qt};
     }
   }
@@ -241,11 +252,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int kvh = local / n_kt;
   const int kt = local - kvh * n_kt;
   const int k0 = kt * kBKV, k1 = min(sg.len, k0 + kBKV);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r = lane & 31, h = lane >> 5;
   const int mask = a.mask;
   const bf16* kb = reinterpret_cast<const bf16*>(sg.k);
   const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
+  // staging source of this wave: Q for waves 0-1, dO for waves 2-3 (a value select,
+  // never a per-lane load of the argument block inside the loop)
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q);
+  const bf16* ob = reinterpret_cast<const bf16*>(a.dout);
+  const bf16* stage_base = wave >= 2 ? ob : qb;
 
   // this wave's keys as B operands (lane: key 32*wave + r, dims 16*ds + 8*h .. +7)
   const int mykey = k0 + wave * 32 + r;
@@ -302,27 +319,42 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // dQ operand: K^T slice of this wave's 32 dims via transposing reads, natural key order
   const bf16* ktr = sm.ks + tr_lane_offset<8>(lane, kKS) + wave * 32;
   const int n_qt = (a.q_len + kBQ - 1) / kBQ;
-  QRef cur = next_qtile(a, 0, 0, n_qt, kmin, kmax, kdmin, kdmax);
+  // n_qt <= kMaxQTiles is checked on the host
+  for (int t = tid; t < n_qt; t += kThreads) {
+    const int r0 = t * kBQ, r1 = min(a.q_len, r0 + kBQ) - 1;
+    sm.qtab[0][t] = a.qpos[r0];
+    sm.qtab[1][t] = a.qpos[r1];
+    sm.qtab[2][t] = mask == kMaskCausalDoc ? a.qdoc[r0] : 0;
+    sm.qtab[3][t] = mask == kMaskCausalDoc ? a.qdoc[r1] : 0;
+  }
+  lds_barrier();
+  // Prefetch order matters: vmcnt is one in-order counter for loads, stores and
+  // atomics.  Tiles 0 and 1 are staged before the loop; inside it, the staging loads
+  // of tile t+2 are issued after the barrier of tile t and before tile t's dQ atomics,
+  // and stored to LDS during tile t+1.  Every path from those loads to their use
+  // crosses exactly the 16 atomics of one tile, so the wait before the LDS store
+  // leaves them in flight instead of waiting for their round trip.
+  QRef cur = next_qtile(sm, a, 0, 0, n_qt, kmin, kmax, kdmin, kdmax);
   if (cur.hh >= 0) {
     QStageRegs<D> qr;
-    load_qstage<D>(qr, a, kvh * a.group + cur.hh, cur.qt * kBQ, tid);
-    store_qstage<D>(sm, 0, qr, tid);
-    __syncthreads();
+    load_qstage<D>(qr, a, stage_base, kvh * a.group + cur.hh, cur.qt * kBQ, tid);
+    store_qstage<D>(sm, 0, qr, a.q_len, mask, tid);
+    QRef nxt = next_qtile(sm, a, cur.hh, cur.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
+    if (nxt.hh >= 0) {
+      load_qstage<D>(qr, a, stage_base, kvh * a.group + nxt.hh, nxt.qt * kBQ, tid);
+      store_qstage<D>(sm, 1, qr, a.q_len, mask, tid);
+    }
+    lds_barrier();
     int buf = 0;
+    bool staged_next = true;  // the next tile's stage is already in LDS
     while (true) {
-      QRef nxt = next_qtile(a, cur.hh, cur.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
-      if (nxt.hh >= 0) load_qstage<D>(qr, a, kvh * a.group + nxt.hh, nxt.qt * kBQ, tid);
       const int head = kvh * a.group + cur.hh;
       const int r0 = cur.qt * kBQ, r1 = min(a.q_len, r0 + kBQ);
       // wave-level class of (query tile, this wave's keys)
       int wcls = kTileEmpty;
       if (wave_keys) {
-        int qdmin = 0, qdmax = 0;
-        if (mask == kMaskCausalDoc) {
-          qdmin = a.qdoc[r0];
-          qdmax = a.qdoc[r1 - 1];
-        }
-        wcls = classify(mask, a.qpos[r0], a.qpos[r1 - 1], qdmin, qdmax, wkmin, wkmax, wkdmin, wkdmax);
+        const QRange q = qrange(sm, cur.qt);
+        wcls = classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, wkmin, wkmax, wkdmin, wkdmax);
         if (wcls == kTileFull && (wk1 - wk0 < 32 || r1 - r0 < kBQ)) wcls = kTilePartial;
       }
       if (wcls == kTileFull)
@@ -334,10 +366,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < kBQ / 2; ++q) dsw[(2 * q + h) * kSS] = (bf16)0.0f;
       }
-      if (nxt.hh >= 0) store_qstage<D>(sm, buf ^ 1, qr, tid);
-      __syncthreads();
+      // the other buffer's Q/dO stage was released by every wave at the previous barrier
+      if (!staged_next && nxt.hh >= 0) store_qstage<D>(sm, buf ^ 1, qr, a.q_len, mask, tid);
+      staged_next = false;
+      lds_barrier();
+      QRef nxt2 = {-1, 0};
+      if (nxt.hh >= 0) nxt2 = next_qtile(sm, a, nxt.hh, nxt.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
+      {
+        const QRef ld = nxt2.hh >= 0 ? nxt2 : cur;  // always issue the loads (see load_qstage)
+        load_qstage<D>(qr, a, stage_base, kvh * a.group + ld.hh, ld.qt * kBQ, tid);
+      }
       // dQ[q][32*wave .. +31] += dS[q][:] K[:][...]  (scale already folded into dS)
-      if (wave * 32 < D) {
+      if (D == 128 || wave * 32 < D) {  // D = 64: two waves cover the dims
         f32x16 acc = {};
         const bf16* dsr = sm.ds[buf] + r * kSS + h * 8;
 #pragma unroll
@@ -347,23 +387,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           const bf16x8 bk = concat(lds_read_tr4(p), lds_read_tr4(p + 4 * kKS));
           acc = mfma32x32x16(ad, bk, acc);
         }
+        // always 16 atomics (rows past the end add 0 to row r0): a fixed count keeps
+        // the staging waits precise (see load_qstage)
         float* dqp = a.dq + ((int64_t)r0 * a.hq + head) * D + wave * 32 + r;
         const int64_t rs = (int64_t)a.hq * D;
-        if (r1 - r0 == kBQ) {
 #pragma unroll
-          for (int aa = 0; aa < 16; ++aa)
-            unsafeAtomicAdd(dqp + (8 * (aa >> 2) + 4 * h + (aa & 3)) * rs, acc[aa]);
-        } else {
-#pragma unroll
-          for (int aa = 0; aa < 16; ++aa) {
-            const int q = 8 * (aa >> 2) + 4 * h + (aa & 3);
-            if (r0 + q < r1) unsafeAtomicAdd(dqp + q * rs, acc[aa]);
-          }
+        for (int aa = 0; aa < 16; ++aa) {
+          const int q = 8 * (aa >> 2) + 4 * h + (aa & 3);
+          const bool ok = r0 + q < r1;
+          unsafeAtomicAdd(dqp + (ok ? q : 0) * rs, ok ? acc[aa] : 0.0f);
         }
       }
       if (nxt.hh < 0) break;
       buf ^= 1;
       cur = nxt;
+      nxt = nxt2;
     }
   }
 
@@ -411,6 +449,8 @@ hipError_t launch_bwd_d(BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int bwd_max_rows() { return kMaxQTiles * kBQ; }
 
 hipError_t launch_bwd(const BwdArgs& args, int d, hipStream_t stream) {
   BwdArgs a = args;

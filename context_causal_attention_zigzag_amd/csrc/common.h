@@ -81,6 +81,29 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Work-group barrier that only orders LDS traffic: waits for this wave's outstanding
+// LDS operations, then s_barrier.  Global stores and atomics stay in flight (a plain
+// __syncthreads() would wait for every outstanding global access of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Barrier after direct global->LDS loads: waits for this wave's outstanding vector
+// memory loads (which include the LDS fills) and LDS operations, then s_barrier.
+__device__ __forceinline__ void fill_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's 16 bytes land at
+// lds_base + 16*l (lds_base wave-uniform), as measured on gfx950.
+__device__ __forceinline__ void global_to_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+// Same with 4 bytes per lane: lane l's dword lands at lds_base + 4*l.
+__device__ __forceinline__ void global_to_lds4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 4, 0, 0);
+}
+
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
 
@@ -116,7 +139,7 @@ __device__ __forceinline__ int xcd_remap(int b, int padded_n) {
 // ---------------------------------------------------------------------------
 // Kernel-argument tables (passed by value).
 constexpr int kMaxSegs = 32;
-constexpr int kMaxJobs = 24;
+constexpr int kMaxJobs = 20;
 
 struct SegDesc {
   const void* k;
@@ -124,19 +147,25 @@ struct SegDesc {
   const int32_t* pos;
   const int32_t* doc;
   int32_t len;
-  int32_t pad_;
+  int32_t tile_off;  // index of this segment's first KV tile in its job's tile sequence
 };
 
 struct JobDesc {
   const void* q;
   const int32_t* pos;
   const int32_t* doc;
-  void* o;        // final output (input dtype) or fp32 partial output
-  float* lse;     // [len, hq]
+  void* o;           // final output (input dtype) or fp32 partial output
+  float* lse;        // [len, hq]
+  float* ws_o;       // split partials [n_split][len][hq][d] (n_split > 1)
+  float* ws_lse;     // split partial LSE [n_split][len][hq]
   int32_t len;
   int32_t seg_begin;
   int32_t seg_end;
   int32_t wg_begin;  // first logical work-group of this job
+  int32_t n_split;   // KV splits per query tile (1: no split)
+  int32_t tiles_per_split;
+  int32_t n_tiles;   // KV tiles over all of the job's segments
+  int32_t pad_;
 };
 
 struct FwdArgs {
@@ -184,9 +213,17 @@ hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int
                             const void* const* src, void* const* dst, const int64_t* row_bytes,
                             hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool partial_out, hipStream_t stream);
+// Split plan for forward jobs: fills n_split / tiles_per_split / n_tiles of each job and
+// the segments' tile offsets; returns the workspace bytes the plan needs.
+size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split);
+// Points the split jobs' partial buffers into a workspace of plan_fwd's size.
+void assign_fwd_workspace(FwdArgs& a, int d, void* ws);
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
                         hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream);
+int bwd_max_rows();  // local query rows the backward kernel supports
+// One launch merging the KV splits of every split job of a forward launch.
+hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream);
 
 }  // namespace cpattn

@@ -25,8 +25,9 @@
 //    is skipped on almost every tile.
 //  - Tiles are classified per work-group (skip empty tiles entirely) and per wave
 //    (fully visible tiles run without mask arithmetic).
-//  - K/V tiles are double-buffered in LDS; the next visible tile's global loads are
-//    in flight while the current tile computes; one barrier per tile.
+//  - K/V tiles are double-buffered in LDS and filled by direct global->LDS loads
+//    (no register staging): the next visible tile streams in while the current one
+//    computes; one barrier per tile.
 //
 // fp32 kernel: a plain VALU kernel, one thread per (query row, head), used for fp32
 // inputs (exact fp32 arithmetic, no bf16 rounding anywhere).
@@ -87,57 +88,154 @@ __device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int 
   return {-1, 0};
 }
 
+// Iterator over the KV tiles one work-group processes.  Scan mode walks the job's
+// segments with next_tile().  Mask mode (KV split across work-groups) first classifies
+// every tile of the job lane-parallel into four 64-bit ballot masks over the job's
+// tile sequence, then yields the visible tiles of rank [first, first + count).
+struct TileIter {
+  bool mask_mode;
+  uint64_t v0, v1, v2, v3;
+  uint64_t m;   // unvisited bits of the current word
+  int w;        // current word
+  int left;     // tiles still to yield
+  int seg;      // segment of the last yielded tile
+  __device__ __forceinline__ uint64_t word(int i) const {
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+  }
+};
+
+__device__ __forceinline__ void iter_init_masks(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
+                                                int qmin, int qmax, int qdmin, int qdmax) {
+  uint64_t v[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    bool vis = false;
+    const int g = 64 * w + lane;
+    if (64 * w < job.n_tiles) {
+      for (int s = job.seg_begin; s < job.seg_end; ++s) {
+        const int len = a.segs[s].len;
+        const int t = g - a.segs[s].tile_off;
+        if (t >= 0 && t * kBK < len) {
+          const int k0 = t * kBK, k1 = min(len, k0 + kBK) - 1;
+          const int32_t* pos = a.segs[s].pos;
+          int kdmin = 0, kdmax = 0;
+          if (a.mask == kMaskCausalDoc) {
+            kdmin = a.segs[s].doc[k0];
+            kdmax = a.segs[s].doc[k1];
+          }
+          vis = classify(a.mask, qmin, qmax, qdmin, qdmax, pos[k0], pos[k1], kdmin, kdmax) != kTileEmpty;
+        }
+      }
+    }
+    v[w] = __ballot(vis);
+  }
+  it.v0 = v[0];
+  it.v1 = v[1];
+  it.v2 = v[2];
+  it.v3 = v[3];
+}
+
+__device__ __forceinline__ int iter_count(const TileIter& it) {
+  return __popcll(it.v0) + __popcll(it.v1) + __popcll(it.v2) + __popcll(it.v3);
+}
+
+// Position the iterator before the visible tile of rank `first`, to yield `count`.
+__device__ __forceinline__ void iter_seek(TileIter& it, int first, int count, int seg_begin) {
+  int w = 0, rank = 0;
+  while (w < 3 && rank + __popcll(it.word(w)) <= first) {
+    rank += __popcll(it.word(w));
+    ++w;
+  }
+  uint64_t m = it.word(w);
+  for (; rank < first; ++rank) m &= m - 1;
+  it.w = w;
+  it.m = m;
+  it.left = count;
+  it.seg = seg_begin;
+}
+
+__device__ __forceinline__ TileRef iter_next(TileIter& it, const FwdArgs& a, const JobDesc& job, TileRef prev,
+                                             int qmin, int qmax, int qdmin, int qdmax) {
+  if (!it.mask_mode) {
+    if (prev.seg < 0) return next_tile(a, job.seg_end, job.seg_begin, 0, qmin, qmax, qdmin, qdmax);
+    return next_tile(a, job.seg_end, prev.seg, prev.tile + 1, qmin, qmax, qdmin, qdmax);
+  }
+  if (it.left == 0) return {-1, 0};
+  while (it.m == 0) {
+    ++it.w;
+    it.m = it.word(it.w);
+  }
+  const int g = 64 * it.w + __builtin_ctzll(it.m);
+  it.m &= it.m - 1;
+  --it.left;
+  while (it.seg + 1 < job.seg_end && a.segs[it.seg + 1].tile_off <= g) ++it.seg;
+  return {it.seg, g - a.segs[it.seg].tile_off};
+}
+
+// Direct global->LDS fill of one KV tile.  The tile's LDS image is a sequence of
+// 16-byte slots (row-major, kKS/8 or kVS/8 slots per key row, the last ones padding);
+// fill instruction jj of the work-group writes slots 64*jj .. 64*jj+63, lane l slot
+// 64*jj + l.  Each lane's (key row, column) per instruction is fixed for the kernel;
+// padding slots load a valid dummy chunk and key rows past a ragged tile's end are
+// clamped to its last key (those keys are masked).
 template <int D>
-struct TileRegs {
-  static constexpr int kChunks = kBK * D / 8 / kThreads;  // 16-byte chunks per thread (K and V)
-  u32x4 k[kChunks];
-  u32x4 v[kChunks];
-  int32_t pos;
-  int32_t doc;
+struct FillPlan {
+  static constexpr int kKSlots = FwdSmem<D>::kKS / 8;
+  static constexpr int kVSlots = FwdSmem<D>::kVS / 8;
+  static constexpr int kKInst = kBK * kKSlots / kWave;
+  static constexpr int kVInst = kBK * kVSlots / kWave;
+  static constexpr int kKPer = (kKInst + 3) / 4;  // per wave (4 waves)
+  static constexpr int kVPer = (kVInst + 3) / 4;
+  static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
+  uint32_t krow[kKPer], kcol[kKPer], vrow[kVPer], vcol[kVPer];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int slot = kWave * (wave + 4 * j) + lane;
+      const int c = slot % kKSlots;
+      krow[j] = slot / kKSlots;
+      kcol[j] = c < D / 8 ? c * 8 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int slot = kWave * (wave + 4 * j) + lane;
+      const int c = slot % kVSlots;
+      vrow[j] = slot / kVSlots;
+      vcol[j] = c < D / 8 ? c * 8 : 0;
+    }
+  }
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const SegDesc& sg, int tile, int kvh,
-                                          int hkv, int mask, int tid) {
+__device__ __forceinline__ void fill_tile(FwdSmem<D>& sm, int buf, const SegDesc& sg, int tile, int kvh,
+                                          int hkv, int mask, int wave, int lane, const FillPlan<D>& fp) {
+  using FP = FillPlan<D>;
   const int k0 = tile * kBK;
-  const int klen = min(kBK, sg.len - k0);
-  const bf16* kb = reinterpret_cast<const bf16*>(sg.k);
-  const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
-  constexpr int kCPK = D / 8;  // chunks per key row
+  const int last = min(kBK, sg.len - k0) - 1;
+  const uint32_t rs = (uint32_t)hkv * D;  // elements between consecutive keys
+  const bf16* kb = reinterpret_cast<const bf16*>(sg.k) + ((int64_t)k0 * hkv + kvh) * D;
+  const bf16* vb = reinterpret_cast<const bf16*>(sg.v) + ((int64_t)k0 * hkv + kvh) * D;
+  char* kl = reinterpret_cast<char*>(sm.k[buf]);
+  char* vl = reinterpret_cast<char*>(sm.v[buf]);
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = c / kCPK, dc = c % kCPK;
-    if (key < klen) {
-      const int64_t off = ((int64_t)(k0 + key) * hkv + kvh) * D + dc * 8;
-      r.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
-    } else {
-      r.k[i] = u32x4{0, 0, 0, 0};
-      r.v[i] = u32x4{0, 0, 0, 0};
+  for (int j = 0; j < FP::kKPer; ++j) {
+    const int jj = wave + 4 * j;
+    if (jj < FP::kKInst) {
+      const uint32_t row = min(fp.krow[j], (uint32_t)last);
+      global_to_lds16(kb + row * rs + fp.kcol[j], kl + jj * kWave * 16);
     }
   }
-  if (tid < kBK) {
-    r.pos = tid < klen ? sg.pos[k0 + tid] : kPosPad;
-    r.doc = (mask == kMaskCausalDoc && tid < klen) ? sg.doc[k0 + tid] : 0;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(FwdSmem<D>& sm, int buf, const TileRegs<D>& r, int tid) {
-  constexpr int kCPK = D / 8;
-  constexpr int kKS = FwdSmem<D>::kKS, kVS = FwdSmem<D>::kVS;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = c / kCPK, dc = c % kCPK;
-    *reinterpret_cast<u32x4*>(&sm.k[buf][key * kKS + dc * 8]) = r.k[i];
-    *reinterpret_cast<u32x4*>(&sm.v[buf][key * kVS + dc * 8]) = r.v[i];
+  for (int j = 0; j < FP::kVPer; ++j) {
+    const int jj = wave + 4 * j;
+    if (jj < FP::kVInst) {
+      const uint32_t row = min(fp.vrow[j], (uint32_t)last);
+      global_to_lds16(vb + row * rs + fp.vcol[j], vl + jj * kWave * 16);
+    }
   }
-  if (tid < kBK) {
-    sm.kpos[buf][tid] = r.pos;
-    sm.kdoc[buf][tid] = r.doc;
-  }
+  if (wave == 0) global_to_lds4(sg.pos + k0 + min(lane, last), sm.kpos[buf]);
+  if (wave == 1 && mask == kMaskCausalDoc) global_to_lds4(sg.doc + k0 + min(lane, last), sm.kdoc[buf]);
 }
 
 // One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
@@ -238,9 +336,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int hpw = a.heads_per_wg;
   const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
   const int n_qt = (job.len + qt_rows - 1) / qt_rows;
+  const int nsplit = job.n_split;
   const int local = logical - job.wg_begin;
-  const int hg = local / n_qt;
-  const int qt = n_qt - 1 - (local - hg * n_qt);  // heaviest (latest) query tiles first
+  const int split = local % nsplit;
+  const int rest = local / nsplit;
+  const int hg = rest / n_qt;
+  const int qt = n_qt - 1 - (rest - hg * n_qt);  // heaviest (latest) query tiles first
   const int r0 = qt * qt_rows, r1 = min(job.len, r0 + qt_rows);
   const int head = hg * hpw + wave % hpw;
   const int kvh = (hg * hpw) / a.group;
@@ -290,16 +391,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m = neg_inf(), l = 0.0f;
 
-  TileRef cur = next_tile(a, job.seg_end, job.seg_begin, 0, qmin, qmax, qdmin, qdmax);
+  // destination: split partial (fp32, workspace), edge partial (fp32) or final output
+  const bool out32 = PARTIAL_OUT || nsplit > 1;
+  float* lse_dst = nsplit > 1 ? job.ws_lse + (int64_t)split * job.len * a.hq : job.lse;
+
+  TileIter it;
+  it.mask_mode = nsplit > 1;
+  if (nsplit > 1) {
+    iter_init_masks(it, a, job, lane, qmin, qmax, qdmin, qdmax);
+    const int total = iter_count(it);
+    const int first = split * job.tiles_per_split;
+    if (first >= total) {  // nothing to do in this split: an empty partial state
+      if (row_ok && (lane >> 5) == 0) lse_dst[(int64_t)myrow * a.hq + head] = neg_inf();
+      return;
+    }
+    iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
+  }
+
+  FillPlan<D> fp;
+  fp.init(wave, lane);
+  TileRef cur = iter_next(it, a, job, TileRef{-1, 0}, qmin, qmax, qdmin, qdmax);
   if (cur.seg >= 0) {
-    TileRegs<D> tr;
-    load_tile<D>(tr, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, tid);
-    store_tile<D>(sm, 0, tr, tid);
-    __syncthreads();
+    fill_tile<D>(sm, 0, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, wave, lane, fp);
+    fill_barrier();
     int buf = 0;
     while (true) {
-      const TileRef nxt = next_tile(a, job.seg_end, cur.seg, cur.tile + 1, qmin, qmax, qdmin, qdmax);
-      if (nxt.seg >= 0) load_tile<D>(tr, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, tid);
+      const TileRef nxt = iter_next(it, a, job, cur, qmin, qmax, qdmin, qdmax);
+      // the other buffer was released by every wave at the previous barrier
+      if (nxt.seg >= 0) fill_tile<D>(sm, buf ^ 1, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, wave, lane, fp);
       if (wave_rows) {
         const int klen = min(kBK, a.segs[cur.seg].len - cur.tile * kBK);
         const int32_t* kp = sm.kpos[buf];
@@ -316,8 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                              a.scale_log2, lane);
       }
       if (nxt.seg < 0) break;
-      store_tile<D>(sm, buf ^ 1, tr, tid);
-      __syncthreads();
+      fill_barrier();
       buf ^= 1;
       cur = nxt;
     }
@@ -331,6 +449,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (row_ok) {
     const int h = lane >> 5;
     const int64_t rowoff = ((int64_t)myrow * a.hq + head) * D;
+    float* o32 = nsplit > 1 ? job.ws_o + (int64_t)split * job.len * a.hq * D : reinterpret_cast<float*>(job.o);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -338,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         const int d0 = db * 32 + g * 8 + h * 4;
         f32x4 v = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
                    o[db][4 * g + 3] * inv};
-        if (PARTIAL_OUT) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(job.o) + rowoff + d0) = v;
+        if (out32) {
+          *reinterpret_cast<f32x4*>(o32 + rowoff + d0) = v;
         } else {
           bf16x4 b;
           b[0] = (bf16)v[0];
@@ -350,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         }
       }
     }
-    if (h == 0) job.lse[(int64_t)myrow * a.hq + head] = lse;
+    if (h == 0) lse_dst[(int64_t)myrow * a.hq + head] = lse;
   }
 }
 
@@ -454,7 +573,7 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
     for (int j = 0; j < a.n_jobs; ++j) {
       a.jobs[j].wg_begin = total;
       const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-      total += n_qt * (a.hq / hpw);
+      total += n_qt * (a.hq / hpw) * a.jobs[j].n_split;
     }
     a.total_wgs = total;
     a.padded_wgs = (total + 7) & ~7;
@@ -463,6 +582,15 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
       hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // log-sum-exp merge of the KV splits of every split job, one launch
+    bool any_split = false;
+    for (int j = 0; j < a.n_jobs; ++j) any_split |= a.jobs[j].n_split > 1;
+    if (any_split) {
+      e = launch_merge_split_jobs(a, D, partial_out ? 1 : dtype, stream);
+      if (e != hipSuccess) return e;
+    }
   } else {
     int total = 0;
     for (int j = 0; j < a.n_jobs; ++j) {
@@ -477,7 +605,75 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
   return hipGetLastError();
 }
 
+constexpr int kMaxSplitTiles = 256;   // tiles a split job may span (four ballot masks)
+// 1024 keys per split at least: each split writes an fp32 partial output of its query
+// tile (4*d bytes per row) for 4*d flops per row and key, so shorter runs would turn
+// the kernel into a writer of partial states
+constexpr int kMinTilesPerSplit = 16;
+constexpr int kMaxSplits = 64;        // parts the merge kernel takes
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
+
+// KV-split plan.  A launch needs on the order of 4 work-groups per compute unit (two
+// resident per CU, two rounds) to fill the chip; when the query tiles alone give fewer,
+// each job's visible KV tiles are cut into splits of tiles_per_split tiles so that
+// the expected number of busy work-groups (causal: about half of a job's tiles are
+// visible to an average query tile) reaches that target.  Jobs spanning more than
+// 256 KV tiles are never split (they already carry enough work per query tile).
+size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split) {
+  for (int j = 0; j < a.n_jobs; ++j) {
+    JobDesc& jb = a.jobs[j];
+    int off = 0;
+    for (int s = jb.seg_begin; s < jb.seg_end; ++s) {
+      a.segs[s].tile_off = off;
+      off += (a.segs[s].len + kBK - 1) / kBK;
+    }
+    jb.n_tiles = off;
+    jb.n_split = 1;
+    jb.tiles_per_split = off;
+    jb.ws_o = nullptr;
+    jb.ws_lse = nullptr;
+  }
+  if (dtype != 0 || !allow_split) return 0;
+  const int hpw = a.heads_per_wg;
+  const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
+  int64_t base = 0;
+  for (int j = 0; j < a.n_jobs; ++j) base += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw);
+  const int64_t target = 4LL * num_cu;
+  if (base == 0 || base >= target) return 0;
+  size_t bytes = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    JobDesc& jb = a.jobs[j];
+    if (jb.n_tiles > kMaxSplitTiles || jb.n_tiles < 2 * kMinTilesPerSplit) continue;
+    int64_t u = (base * jb.n_tiles + 2 * target - 1) / (2 * target);
+    if (u < kMinTilesPerSplit) u = kMinTilesPerSplit;
+    int ns = (int)((jb.n_tiles + u - 1) / u);
+    if (ns > kMaxSplits) {
+      ns = kMaxSplits;
+      u = (jb.n_tiles + ns - 1) / ns;
+    }
+    if (ns <= 1) continue;
+    jb.n_split = ns;
+    jb.tiles_per_split = (int)u;
+    bytes += align256((size_t)ns * jb.len * a.hq * d * sizeof(float));
+    bytes += align256((size_t)ns * jb.len * a.hq * sizeof(float));
+  }
+  return bytes;
+}
+
+void assign_fwd_workspace(FwdArgs& a, int d, void* ws) {
+  char* p = reinterpret_cast<char*>(ws);
+  for (int j = 0; j < a.n_jobs; ++j) {
+    JobDesc& jb = a.jobs[j];
+    if (jb.n_split <= 1) continue;
+    jb.ws_o = reinterpret_cast<float*>(p);
+    p += align256((size_t)jb.n_split * jb.len * a.hq * d * sizeof(float));
+    jb.ws_lse = reinterpret_cast<float*>(p);
+    p += align256((size_t)jb.n_split * jb.len * a.hq * sizeof(float));
+  }
+}
 
 hipError_t launch_fwd(const FwdArgs& args, int d, int dtype, bool partial_out, hipStream_t stream) {
   FwdArgs a = args;

@@ -65,7 +65,88 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (c == 0) a.lse_out[pair] = lse;
 }
 
+// Merge of the KV-split partial states of several forward jobs in one launch: job j
+// has n parts at ws_o + p*len*hq*d / ws_lse + p*len*hq and writes (o, lse).
+struct MergeJobsArgs {
+  const float* ws_o[kMaxJobs];
+  const float* ws_lse[kMaxJobs];
+  void* o[kMaxJobs];
+  float* lse[kMaxJobs];
+  int64_t pair_begin[kMaxJobs + 1];  // prefix of len*hq over the jobs
+  int32_t n[kMaxJobs];
+  int32_t n_jobs;
+  int32_t d;
+};
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
+  const int tpp = a.d >> 2;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t gpair = gid / tpp;
+  const int c = (int)(gid - gpair * tpp);
+  if (gpair >= a.pair_begin[a.n_jobs]) return;
+  int j = 0;
+  while (j + 1 < a.n_jobs && a.pair_begin[j + 1] <= gpair) ++j;
+  const int64_t pair = gpair - a.pair_begin[j];
+  const int64_t stride = a.pair_begin[j + 1] - a.pair_begin[j];  // len * hq
+  const int n = a.n[j];
+  const float* lp = a.ws_lse[j] + pair;
+  float mx = neg_inf();
+  for (int p = 0; p < n; ++p) mx = fmaxf(mx, lp[p * stride]);
+  const int64_t off = pair * a.d + 4 * c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse = neg_inf();
+  if (mx != neg_inf()) {
+    float sum = 0.f;
+    for (int p = 0; p < n; ++p) sum += fast_exp2((lp[p * stride] - mx) * kLog2e);
+    lse = mx + fast_log2(sum) * kLn2;
+    for (int p = 0; p < n; ++p) {
+      const float lj = lp[p * stride];
+      if (lj == neg_inf()) continue;
+      const float w = fast_exp2((lj - lse) * kLog2e);
+      acc += w * *reinterpret_cast<const f32x4*>(a.ws_o[j] + p * stride * a.d + off);
+    }
+  }
+  if (OUT_BF16) {
+    bf16x4 r;
+    r[0] = (bf16)acc[0];
+    r[1] = (bf16)acc[1];
+    r[2] = (bf16)acc[2];
+    r[3] = (bf16)acc[3];
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o[j]) + off) = r;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o[j]) + off) = acc;
+  }
+  if (c == 0) a.lse[j][pair] = lse;
+}
+
 }  // namespace
+
+hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream) {
+  MergeJobsArgs a{};
+  int64_t pairs = 0;
+  for (int j = 0; j < f.n_jobs; ++j) {
+    const JobDesc& jb = f.jobs[j];
+    if (jb.n_split <= 1) continue;
+    const int k = a.n_jobs++;
+    a.ws_o[k] = jb.ws_o;
+    a.ws_lse[k] = jb.ws_lse;
+    a.o[k] = jb.o;
+    a.lse[k] = jb.lse;
+    a.n[k] = jb.n_split;
+    a.pair_begin[k] = pairs;
+    pairs += (int64_t)jb.len * f.hq;
+  }
+  a.pair_begin[a.n_jobs] = pairs;
+  a.d = d;
+  if (pairs == 0) return hipSuccess;
+  const int64_t blocks = (pairs * (d / 4) + kThreads - 1) / kThreads;
+  if (out_dtype == 0)
+    hipLaunchKernelGGL(merge_jobs_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_jobs_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,

@@ -23,7 +23,8 @@ import torch
 
 from . import (PART_THD, PART_ZIGZAG, MASK_CAUSAL, MASK_CAUSAL_DOC, attn_desc, cpattn_bwd,
                cpattn_bwd_workspace_bytes, cpattn_merge, cpattn_partition, cpattn_stream_fwd,
-               cpattn_tile_fwd, kv_seg, q_block)
+               cpattn_stream_fwd_workspace_bytes, cpattn_tile_fwd, cpattn_tile_fwd_workspace_bytes,
+               kv_seg, q_block)
 
 
 def ring_order(cp: int, rank: int):
@@ -108,13 +109,30 @@ class RankShare:
         return out
 
     # ---- the computations ------------------------------------------------------------
-    def stream_fwd(self, granularity="owner", o=None, lse=None, scale=0.0):
+    def stream_fwd(self, granularity="owner", o=None, lse=None, scale=0.0, workspace="auto"):
         n = self.q.shape[0]
         o = torch.empty_like(self.q) if o is None else o
         lse = torch.empty((n, self.hq), dtype=torch.float32, device=self.q.device) if lse is None else lse
         segs = [s for s, _, _ in self.segments(granularity)]
-        cpattn_stream_fwd(self.desc(scale), q_block(self.q, self.q_idx, self.q_doc), segs, o, lse)
+        cpattn_stream_fwd(self.desc(scale), q_block(self.q, self.q_idx, self.q_doc), segs, o, lse,
+                          workspace)
         return o, lse
+
+    def stream_workspace(self, granularity="owner", scale=0.0):
+        segs = [s for s, _, _ in self.segments(granularity)]
+        n = cpattn_stream_fwd_workspace_bytes(self.desc(scale), q_block(self.q, self.q_idx, self.q_doc), segs)
+        return torch.empty(n, dtype=torch.uint8, device=self.q.device) if n else None
+
+    def tile_workspace(self, edges, scale=0.0):
+        qbs, segs = self._edge_args(edges)
+        n = cpattn_tile_fwd_workspace_bytes(self.desc(scale), qbs, segs)
+        return torch.empty(n, dtype=torch.uint8, device=self.q.device) if n else None
+
+    def _edge_args(self, edges):
+        qbs = []
+        for (a, b), _, _ in edges:
+            qbs.append(q_block(self.q[a:b], self.q_idx[a:b], None if self.q_doc is None else self.q_doc[a:b]))
+        return qbs, [s for _, s, _ in edges]
 
     def alloc_tile_buffers(self, granularity="owner"):
         edges = self.edges(granularity)
@@ -124,12 +142,9 @@ class RankShare:
                           torch.empty((b - a, self.hq), dtype=torch.float32, device=self.q.device)))
         return edges, parts
 
-    def tile_fwd(self, edges, parts, scale=0.0):
-        qbs = []
-        for (a, b), _, _ in edges:
-            qbs.append(q_block(self.q[a:b], self.q_idx[a:b], None if self.q_doc is None else self.q_doc[a:b]))
-        cpattn_tile_fwd(self.desc(scale), qbs, [s for _, s, _ in edges], [p[0] for p in parts],
-                        [p[1] for p in parts])
+    def tile_fwd(self, edges, parts, scale=0.0, workspace="auto"):
+        qbs, segs = self._edge_args(edges)
+        cpattn_tile_fwd(self.desc(scale), qbs, segs, [p[0] for p in parts], [p[1] for p in parts], workspace)
 
     def merge(self, edges, parts, o=None, lse=None):
         n = self.q.shape[0]

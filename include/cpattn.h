@@ -139,12 +139,27 @@ int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_ra
  *  q_blocks, segs   host arrays [n_edges]: the edge's queries and its KV segment.
  *  o_parts          host array [n_edges] of device fp32 [q.len, hq, d] outputs O_ij.
  *  lse_parts        host array [n_edges] of device fp32 [q.len, hq] outputs L_ij.
+ *  workspace        device buffer (256-byte aligned) of workspace_bytes, or NULL.
+ *                   With at least cpattn_tile_fwd_workspace_bytes() bytes, an edge
+ *                   whose query tiles alone leave the GPU underfilled has its visible
+ *                   KV tiles split over several work-groups whose partial states are
+ *                   merged into O_ij (the same associative merge as cpattn_merge);
+ *                   with less (or NULL) every query tile runs in one work-group.
+ *                   Contents on entry are ignored; the results do not depend on it
+ *                   beyond floating-point rounding.
  * Rows of a block that see nothing of the segment get (0, -inf).
  * Errors: ARG, UNSUPPORTED (d not 64/128, hq % hkv, dtype, mask), HIP.
  */
 int cpattn_tile_fwd(const cpattn_attn_desc* desc, int32_t n_edges,
                     const cpattn_q_block* q_blocks, const cpattn_kv_seg* segs,
-                    float* const* o_parts, float* const* lse_parts, void* stream);
+                    float* const* o_parts, float* const* lse_parts, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that let cpattn_tile_fwd split the edges' KV ranges over more
+ * work-groups when the edges alone cannot fill the GPU (0: no split planned, or
+ * invalid arguments).  The plan depends on the arguments and the current device. */
+size_t cpattn_tile_fwd_workspace_bytes(const cpattn_attn_desc* desc, int32_t n_edges,
+                                       const cpattn_q_block* q_blocks, const cpattn_kv_seg* segs);
 
 /*
  * cpattn_merge — the associative log-sum-exp merge of partial states.
@@ -180,10 +195,20 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
  *  n_segs, segs     host array of KV segments in arrival order (1..32).
  *  o_out            device [q.len, hq, d] in desc.dtype (final output O).
  *  lse_out          device fp32 [q.len, hq] (lambda, natural log).
- * Errors: ARG, UNSUPPORTED, HIP.
+ *  workspace        as for cpattn_tile_fwd (cpattn_stream_fwd_workspace_bytes()): when
+ *                   the query tiles cannot fill the GPU, each query tile's visible KV
+ *                   tiles (in arrival order) are cut into consecutive runs, each run
+ *                   keeps its own running (m, l, a) state, and the runs' partial states
+ *                   are merged by log-sum-exp — the pool form of the same computation.
+ * Errors: ARG, ALIGN, UNSUPPORTED, HIP.
  */
 int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
-                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* stream);
+                      const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for the KV-split plan of cpattn_stream_fwd (0: no split planned). */
+size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
+                                         int32_t n_segs, const cpattn_kv_seg* segs);
 
 /*
  * cpattn_bwd — LSE-replay backward of one rank's share.
@@ -194,7 +219,8 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
  * dK_j = sum_i dS_ij Q_i / sqrt(d), dV_j = sum_i P_ij G_i, and the K/V gradient
  * contributions of all local queries are summed per owner (per segment here).
  *
- *  q, segs          as for cpattn_stream_fwd (bf16 only in this version).
+ *  q, segs          as for cpattn_stream_fwd (bf16 only in this version; at most
+ *                   65536 local query rows, else CPATTN_ERR_UNSUPPORTED).
  *  o                device [q.len, hq, d] forward output (desc.dtype).
  *  lse              device fp32 [q.len, hq] forward log-sum-exp.
  *  dout             device [q.len, hq, d] upstream gradient G (desc.dtype).

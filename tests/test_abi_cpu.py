@@ -85,7 +85,7 @@ def stream_call(d, q=None, segs=None):
     q = q or qb()
     segs = segs if segs is not None else [sg()]
     arr = (C.cpattn_kv_seg * max(1, len(segs)))(*segs)
-    return C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), len(segs), arr, FAKE, FAKE, None)
+    return C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), len(segs), arr, FAKE, FAKE, None, 0, None)
 
 
 def test_attention_validation():
@@ -108,15 +108,34 @@ def test_tile_and_merge_validation():
     q = (C.cpattn_q_block * 1)(qb())
     s = (C.cpattn_kv_seg * 1)(sg())
     nul = (ctypes.c_void_p * 1)(None)
-    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 1, q, s, nul, nul, None) == C.ERR_ARG
-    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), -1, q, s, nul, nul, None) == C.ERR_ARG
-    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 0, q, s, nul, nul, None) == C.OK   # no-op
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 1, q, s, nul, nul, None, 0, None) == C.ERR_ARG
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), -1, q, s, nul, nul, None, 0, None) == C.ERR_ARG
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 0, q, s, nul, nul, None, 0, None) == C.OK   # no-op
+    p1 = (ctypes.c_void_p * 1)(FAKE)
+    assert C.lib.cpattn_tile_fwd(ctypes.byref(d), 1, q, s, p1, p1, FAKE + 16, 1 << 20, None) == C.ERR_ALIGN
     p = (ctypes.c_void_p * 1)(FAKE)
     assert C.lib.cpattn_merge(0, p, p, 10, 8, 128, C.BF16, FAKE, FAKE, None) == C.ERR_ARG
     assert C.lib.cpattn_merge(65, p, p, 10, 8, 128, C.BF16, FAKE, FAKE, None) == C.ERR_ARG
     assert C.lib.cpattn_merge(1, p, p, 10, 8, 6, C.BF16, FAKE, FAKE, None) == C.ERR_UNSUPPORTED
     assert C.lib.cpattn_merge(1, p, p, 10, 8, 128, 9, FAKE, FAKE, None) == C.ERR_UNSUPPORTED
     assert C.lib.cpattn_merge(1, p, p, 0, 8, 128, C.BF16, FAKE, FAKE, None) == C.OK   # no-op
+
+
+def test_forward_workspace_plan():
+    # a small share (2048 rows x 8 heads, 4 segments of 2048 keys) cannot fill 256 CUs
+    # with query tiles alone: a split is planned; a large one (64 query tiles x 64 heads) not
+    d = desc()
+    q = qb(2048)
+    segs = (C.cpattn_kv_seg * 4)(*[sg(2048)] * 4)
+    small = C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 4, segs)
+    assert small > 0 and small % 256 == 0
+    big = desc(hq=64, hkv=64)
+    qbig = qb(8192)
+    assert C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(big), ctypes.byref(qbig), 4, segs) == 0
+    assert C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(desc(dtype=C.F32)), ctypes.byref(q), 4, segs) == 0
+    qa = (C.cpattn_q_block * 2)(qb(1024), qb(1024))
+    sa = (C.cpattn_kv_seg * 2)(sg(2048), sg(2048))
+    assert C.lib.cpattn_tile_fwd_workspace_bytes(ctypes.byref(d), 2, qa, sa) > 0
 
 
 def test_bwd_validation_and_workspace():

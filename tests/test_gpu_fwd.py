@@ -28,19 +28,22 @@ def check_share(name, q, k, v, cp, rank, cu=None, granularities=("owner", "chunk
     rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), cp, rank, cu)
     assert np.array_equal(rs.q_idx.cpu().numpy(), rows)
     for gran in granularities:
-        say(f"{name} rank={rank} stream gran={gran}")
-        o, lse = rs.stream_fwd(gran)
-        torch.cuda.synchronize()
-        assert_close(o, o_ref, tol_o, f"{name} r{rank} stream/{gran} O")
-        assert_close(lse, l_ref, tol_l, f"{name} r{rank} stream/{gran} LSE")
-        if tile:
-            say(f"{name} rank={rank} tile+merge gran={gran}")
-            edges, parts = rs.alloc_tile_buffers(gran)
-            rs.tile_fwd(edges, parts)
-            o2, l2 = rs.merge(edges, parts)
+        # "auto": KV splits over several work-groups where planned; None: one per query tile
+        for ws in ("auto", None):
+            tag = "split" if ws else "nosplit"
+            say(f"{name} rank={rank} stream gran={gran} {tag}")
+            o, lse = rs.stream_fwd(gran, workspace=ws)
             torch.cuda.synchronize()
-            assert_close(o2, o_ref, tol_o, f"{name} r{rank} tile/{gran} O")
-            assert_close(l2, l_ref, tol_l, f"{name} r{rank} tile/{gran} LSE")
+            assert_close(o, o_ref, tol_o, f"{name} r{rank} stream/{gran}/{tag} O")
+            assert_close(lse, l_ref, tol_l, f"{name} r{rank} stream/{gran}/{tag} LSE")
+            if tile:
+                say(f"{name} rank={rank} tile+merge gran={gran} {tag}")
+                edges, parts = rs.alloc_tile_buffers(gran)
+                rs.tile_fwd(edges, parts, workspace=ws)
+                o2, l2 = rs.merge(edges, parts)
+                torch.cuda.synchronize()
+                assert_close(o2, o_ref, tol_o, f"{name} r{rank} tile/{gran}/{tag} O")
+                assert_close(l2, l_ref, tol_l, f"{name} r{rank} tile/{gran}/{tag} LSE")
     return rs
 
 
