@@ -73,7 +73,8 @@ lib.cpattn_stream_fwd_workspace_bytes.restype = _c_sz
 lib.cpattn_bwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
                            _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
 lib.cpattn_bwd.restype = _c_i32
-lib.cpattn_bwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _c_i64]
+lib.cpattn_bwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
+                                           _P(cpattn_kv_seg)]
 lib.cpattn_bwd_workspace_bytes.restype = _c_sz
 
 EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
@@ -230,8 +231,9 @@ def cpattn_stream_fwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o_out, ls
     _check(st, "cpattn_stream_fwd")
 
 
-def cpattn_bwd_workspace_bytes(desc: cpattn_attn_desc, q_len: int) -> int:
-    return int(lib.cpattn_bwd_workspace_bytes(ctypes.byref(desc), q_len))
+def cpattn_bwd_workspace_bytes(desc: cpattn_attn_desc, q: cpattn_q_block, segs) -> int:
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    return int(lib.cpattn_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(q), len(segs), sa))
 
 
 def cpattn_bwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o, lse, dout, dq, dk, dv,

@@ -74,6 +74,10 @@ SegDesc to_seg(const cpattn_kv_seg& s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_ERR_HIP; }
 
+size_t bwd_delta_bytes(const cpattn_attn_desc* desc, int64_t q_len) {
+  return ((size_t)q_len * (size_t)desc->hq * sizeof(float) + 255) & ~(size_t)255;
+}
+
 // Compute units of the current device (256 when no device is visible, for planning).
 int device_cus() {
   int dev = 0, n = 0;
@@ -278,10 +282,18 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, int64_t q_len) {
-  if (desc == nullptr || q_len < 0 || desc->hq < 1) return 0;
-  const size_t bytes = (size_t)q_len * (size_t)desc->hq * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                  const cpattn_kv_seg* segs) {
+  if (check_desc(desc) != CPATTN_OK || check_qblock(desc, q) != CPATTN_OK) return 0;
+  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return 0;
+  for (int s = 0; s < n_segs; ++s)
+    if (check_seg(desc, &segs[s]) != CPATTN_OK) return 0;
+  const size_t delta = bwd_delta_bytes(desc, q->len);
+  if (q->len == 0) return delta;
+  FwdArgs f{};
+  fill_common(f, desc);
+  fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);
+  return delta + plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true);
 }
 
 int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -302,12 +314,12 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
       if (!aligned16(dk[s]) || !aligned16(dv[s])) return CPATTN_ERR_ALIGN;
     }
   }
+  const size_t delta_bytes = bwd_delta_bytes(desc, q->len);
   if (q->len > 0) {
     if (o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr) return CPATTN_ERR_ARG;
     if (!aligned16(o) || !aligned16(dout) || !aligned16(dq)) return CPATTN_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < cpattn_bwd_workspace_bytes(desc, q->len))
-      return CPATTN_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return CPATTN_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < delta_bytes) return CPATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
   }
   BwdArgs a{};
   for (int s = 0; s < n_segs; ++s) {
@@ -317,11 +329,10 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   }
   a.q = q->q;
   a.qpos = q->pos;
-  a.qdoc = q->doc != nullptr ? q->doc : q->pos;  // always a readable array (read, unused)
+  a.qdoc = q->doc;
   a.o = o;
   a.lse = lse;
   a.dout = dout;
-  a.dq = dq;
   a.delta = reinterpret_cast<float*>(workspace);
   a.q_len = (int32_t)q->len;
   a.n_segs = n_segs;
@@ -331,7 +342,19 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   a.mask = desc->mask;
   a.scale = eff_scale(desc);
   a.scale_log2 = a.scale * kLog2e;
-  return hip_status(launch_bwd(a, desc->d, reinterpret_cast<hipStream_t>(stream)));
+  // dQ pass: one query-major job over the same segments, split like a forward job
+  FwdArgs f{};
+  fill_common(f, desc);
+  fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
+  if (q->len > 0) {
+    const int cus = device_cus();
+    char* rest = reinterpret_cast<char*>(workspace) + delta_bytes;
+    const size_t avail = workspace_bytes - delta_bytes;
+    size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true);
+    if (need > avail) need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false);  // too small: no split
+    if (need > 0) assign_fwd_workspace(f, desc->d, rest);
+  }
+  return hip_status(launch_bwd(a, f, a.scale, desc->d, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -190,7 +190,6 @@ struct BwdArgs {
   const void* o;
   const float* lse;
   const void* dout;
-  float* dq;
   float* dk[kMaxSegs];
   float* dv[kMaxSegs];
   float* delta;          // workspace [q_len, hq]: rowsum(dO * O)
@@ -221,9 +220,11 @@ void assign_fwd_workspace(FwdArgs& a, int d, void* ws);
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
                         hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream);
+// Backward: delta, dQ (query-major, `dq` holds its jobs / split plan / workspace), dK/dV.
+hipError_t launch_bwd(const BwdArgs& a, const FwdArgs& dq, float scale, int d, hipStream_t stream);
 int bwd_max_rows();  // local query rows the backward kernel supports
 // One launch merging the KV splits of every split job of a forward launch.
-hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream);
+hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream,
+                                   bool sum = false);
 
 }  // namespace cpattn

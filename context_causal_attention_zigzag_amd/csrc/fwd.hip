@@ -32,211 +32,17 @@
 // fp32 kernel: a plain VALU kernel, one thread per (query row, head), used for fp32
 // inputs (exact fp32 arithmetic, no bf16 rounding anywhere).
 #include "common.h"
+#include "kv_stream.h"
 
 namespace cpattn {
 
 namespace {
 
-constexpr int kBK = 64;         // keys per KV tile
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kRowsPerWave = 32;
-constexpr float kTau = 8.0f;    // lazy-rescale threshold (log2 units)
-constexpr int kPosPad = 0x7fffffff;
+using namespace kv;
 
 template <int D>
-struct FwdSmem {
-  // Row strides measured conflict-free on gfx950's 64-bank LDS: 16-byte row reads
-  // need a stride of 4 (mod 16) dwords, transposing reads 16 (mod 64) dwords.
-  static constexpr int kKS = D + 8;    // K: row reads
-  static constexpr int kVS = D + 32;   // V: transposing reads
-  bf16 k[2][kBK * kKS];
-  bf16 v[2][kBK * kVS];
-  int32_t kpos[2][kBK];
-  int32_t kdoc[2][kBK];
-};
+using FwdSmem = KvSmem<D, D + 8, D + 32>;  // K: row reads; V: transposing reads
 
-struct TileRef {
-  int seg;
-  int tile;
-};
-
-// Next KV tile at or after (s, t) that the query range can see; seg = -1 if none.
-__device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int s, int t, int qmin,
-                                             int qmax, int qdmin, int qdmax) {
-  const int mask = a.mask;
-  for (; s < seg_end; ++s, t = 0) {
-    const int len = a.segs[s].len;
-    const int32_t* pos = a.segs[s].pos;
-    const int32_t* doc = a.segs[s].doc;
-    const int nt = (len + kBK - 1) / kBK;
-    for (; t < nt; ++t) {
-      const int k0 = t * kBK;
-      const int k1 = min(len, k0 + kBK) - 1;
-      if (mask == kMaskNone) return {s, t};
-      const int kmin = pos[k0];
-      // positions ascend inside a segment: once a tile starts after the last query,
-      // no later tile of that segment is visible either
-      if (kmin > qmax) break;
-      int kdmin = 0, kdmax = 0;
-      if (mask == kMaskCausalDoc) {
-        kdmin = doc[k0];
-        kdmax = doc[k1];
-      }
-      if (classify(mask, qmin, qmax, qdmin, qdmax, kmin, pos[k1], kdmin, kdmax) != kTileEmpty) return {s, t};
-    }
-  }
-  return {-1, 0};
-}
-
-// Iterator over the KV tiles one work-group processes.  Scan mode walks the job's
-// segments with next_tile().  Mask mode (KV split across work-groups) first classifies
-// every tile of the job lane-parallel into four 64-bit ballot masks over the job's
-// tile sequence, then yields the visible tiles of rank [first, first + count).
-struct TileIter {
-  bool mask_mode;
-  uint64_t v0, v1, v2, v3;
-  uint64_t m;   // unvisited bits of the current word
-  int w;        // current word
-  int left;     // tiles still to yield
-  int seg;      // segment of the last yielded tile
-  __device__ __forceinline__ uint64_t word(int i) const {
-    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
-  }
-};
-
-__device__ __forceinline__ void iter_init_masks(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
-                                                int qmin, int qmax, int qdmin, int qdmax) {
-  uint64_t v[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    bool vis = false;
-    const int g = 64 * w + lane;
-    if (64 * w < job.n_tiles) {
-      for (int s = job.seg_begin; s < job.seg_end; ++s) {
-        const int len = a.segs[s].len;
-        const int t = g - a.segs[s].tile_off;
-        if (t >= 0 && t * kBK < len) {
-          const int k0 = t * kBK, k1 = min(len, k0 + kBK) - 1;
-          const int32_t* pos = a.segs[s].pos;
-          int kdmin = 0, kdmax = 0;
-          if (a.mask == kMaskCausalDoc) {
-            kdmin = a.segs[s].doc[k0];
-            kdmax = a.segs[s].doc[k1];
-          }
-          vis = classify(a.mask, qmin, qmax, qdmin, qdmax, pos[k0], pos[k1], kdmin, kdmax) != kTileEmpty;
-        }
-      }
-    }
-    v[w] = __ballot(vis);
-  }
-  it.v0 = v[0];
-  it.v1 = v[1];
-  it.v2 = v[2];
-  it.v3 = v[3];
-}
-
-__device__ __forceinline__ int iter_count(const TileIter& it) {
-  return __popcll(it.v0) + __popcll(it.v1) + __popcll(it.v2) + __popcll(it.v3);
-}
-
-// Position the iterator before the visible tile of rank `first`, to yield `count`.
-__device__ __forceinline__ void iter_seek(TileIter& it, int first, int count, int seg_begin) {
-  int w = 0, rank = 0;
-  while (w < 3 && rank + __popcll(it.word(w)) <= first) {
-    rank += __popcll(it.word(w));
-    ++w;
-  }
-  uint64_t m = it.word(w);
-  for (; rank < first; ++rank) m &= m - 1;
-  it.w = w;
-  it.m = m;
-  it.left = count;
-  it.seg = seg_begin;
-}
-
-__device__ __forceinline__ TileRef iter_next(TileIter& it, const FwdArgs& a, const JobDesc& job, TileRef prev,
-                                             int qmin, int qmax, int qdmin, int qdmax) {
-  if (!it.mask_mode) {
-    if (prev.seg < 0) return next_tile(a, job.seg_end, job.seg_begin, 0, qmin, qmax, qdmin, qdmax);
-    return next_tile(a, job.seg_end, prev.seg, prev.tile + 1, qmin, qmax, qdmin, qdmax);
-  }
-  if (it.left == 0) return {-1, 0};
-  while (it.m == 0) {
-    ++it.w;
-    it.m = it.word(it.w);
-  }
-  const int g = 64 * it.w + __builtin_ctzll(it.m);
-  it.m &= it.m - 1;
-  --it.left;
-  while (it.seg + 1 < job.seg_end && a.segs[it.seg + 1].tile_off <= g) ++it.seg;
-  return {it.seg, g - a.segs[it.seg].tile_off};
-}
-
-// Direct global->LDS fill of one KV tile.  The tile's LDS image is a sequence of
-// 16-byte slots (row-major, kKS/8 or kVS/8 slots per key row, the last ones padding);
-// fill instruction jj of the work-group writes slots 64*jj .. 64*jj+63, lane l slot
-// 64*jj + l.  Each lane's (key row, column) per instruction is fixed for the kernel;
-// padding slots load a valid dummy chunk and key rows past a ragged tile's end are
-// clamped to its last key (those keys are masked).
-template <int D>
-struct FillPlan {
-  static constexpr int kKSlots = FwdSmem<D>::kKS / 8;
-  static constexpr int kVSlots = FwdSmem<D>::kVS / 8;
-  static constexpr int kKInst = kBK * kKSlots / kWave;
-  static constexpr int kVInst = kBK * kVSlots / kWave;
-  static constexpr int kKPer = (kKInst + 3) / 4;  // per wave (4 waves)
-  static constexpr int kVPer = (kVInst + 3) / 4;
-  static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
-  uint32_t krow[kKPer], kcol[kKPer], vrow[kVPer], vcol[kVPer];
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
-      const int c = slot % kKSlots;
-      krow[j] = slot / kKSlots;
-      kcol[j] = c < D / 8 ? c * 8 : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
-      const int c = slot % kVSlots;
-      vrow[j] = slot / kVSlots;
-      vcol[j] = c < D / 8 ? c * 8 : 0;
-    }
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void fill_tile(FwdSmem<D>& sm, int buf, const SegDesc& sg, int tile, int kvh,
-                                          int hkv, int mask, int wave, int lane, const FillPlan<D>& fp) {
-  using FP = FillPlan<D>;
-  const int k0 = tile * kBK;
-  const int last = min(kBK, sg.len - k0) - 1;
-  const uint32_t rs = (uint32_t)hkv * D;  // elements between consecutive keys
-  const bf16* kb = reinterpret_cast<const bf16*>(sg.k) + ((int64_t)k0 * hkv + kvh) * D;
-  const bf16* vb = reinterpret_cast<const bf16*>(sg.v) + ((int64_t)k0 * hkv + kvh) * D;
-  char* kl = reinterpret_cast<char*>(sm.k[buf]);
-  char* vl = reinterpret_cast<char*>(sm.v[buf]);
-#pragma unroll
-  for (int j = 0; j < FP::kKPer; ++j) {
-    const int jj = wave + 4 * j;
-    if (jj < FP::kKInst) {
-      const uint32_t row = min(fp.krow[j], (uint32_t)last);
-      global_to_lds16(kb + row * rs + fp.kcol[j], kl + jj * kWave * 16);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < FP::kVPer; ++j) {
-    const int jj = wave + 4 * j;
-    if (jj < FP::kVInst) {
-      const uint32_t row = min(fp.vrow[j], (uint32_t)last);
-      global_to_lds16(vb + row * rs + fp.vcol[j], vl + jj * kWave * 16);
-    }
-  }
-  if (wave == 0) global_to_lds4(sg.pos + k0 + min(lane, last), sm.kpos[buf]);
-  if (wave == 1 && mask == kMaskCausalDoc) global_to_lds4(sg.doc + k0 + min(lane, last), sm.kdoc[buf]);
-}
 
 // One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
 template <int D, bool MASKED>
@@ -408,17 +214,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
   }
 
-  FillPlan<D> fp;
+  FillPlan<D, FwdSmem<D>> fp;
   fp.init(wave, lane);
   TileRef cur = iter_next(it, a, job, TileRef{-1, 0}, qmin, qmax, qdmin, qdmax);
   if (cur.seg >= 0) {
-    fill_tile<D>(sm, 0, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, wave, lane, fp);
+    fill_tile<D, FwdSmem<D>>(sm, 0, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, wave, lane, fp);
     fill_barrier();
     int buf = 0;
     while (true) {
       const TileRef nxt = iter_next(it, a, job, cur, qmin, qmax, qdmin, qdmax);
       // the other buffer was released by every wave at the previous barrier
-      if (nxt.seg >= 0) fill_tile<D>(sm, buf ^ 1, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, wave, lane, fp);
+      if (nxt.seg >= 0) fill_tile<D, FwdSmem<D>>(sm, buf ^ 1, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, wave, lane, fp);
       if (wave_rows) {
         const int klen = min(kBK, a.segs[cur.seg].len - cur.tile * kBK);
         const int32_t* kp = sm.kpos[buf];

@@ -78,7 +78,9 @@ struct MergeJobsArgs {
   int32_t d;
 };
 
-template <bool OUT_BF16>
+// SUM: plain sum of the parts whose flag (the LSE slot) is not -inf, for split
+// gradient partials; otherwise the log-sum-exp merge.
+template <bool OUT_BF16, bool SUM>
 __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
   const int tpp = a.d >> 2;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -91,10 +93,16 @@ __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
   const int64_t stride = a.pair_begin[j + 1] - a.pair_begin[j];  // len * hq
   const int n = a.n[j];
   const float* lp = a.ws_lse[j] + pair;
-  float mx = neg_inf();
-  for (int p = 0; p < n; ++p) mx = fmaxf(mx, lp[p * stride]);
   const int64_t off = pair * a.d + 4 * c;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (SUM) {
+    for (int p = 0; p < n; ++p)
+      if (lp[p * stride] != neg_inf()) acc += *reinterpret_cast<const f32x4*>(a.ws_o[j] + p * stride * a.d + off);
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o[j]) + off) = acc;
+    return;
+  }
+  float mx = neg_inf();
+  for (int p = 0; p < n; ++p) mx = fmaxf(mx, lp[p * stride]);
   float lse = neg_inf();
   if (mx != neg_inf()) {
     float sum = 0.f;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
 
 }  // namespace
 
-hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream) {
+hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream, bool sum) {
   MergeJobsArgs a{};
   int64_t pairs = 0;
   for (int j = 0; j < f.n_jobs; ++j) {
@@ -141,10 +149,12 @@ hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipSt
   a.d = d;
   if (pairs == 0) return hipSuccess;
   const int64_t blocks = (pairs * (d / 4) + kThreads - 1) / kThreads;
-  if (out_dtype == 0)
-    hipLaunchKernelGGL(merge_jobs_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (sum)
+    hipLaunchKernelGGL((merge_jobs_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else if (out_dtype == 0)
+    hipLaunchKernelGGL((merge_jobs_kernel<true, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_jobs_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((merge_jobs_kernel<false, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -163,8 +163,9 @@ class RankShare:
         dq = torch.empty((self.q.shape[0], self.hq, self.d), dtype=torch.float32, device=dev)
         dk = [torch.empty((b - a, self.hkv, self.d), dtype=torch.float32, device=dev) for _, _, (a, b) in segs]
         dv = [torch.empty_like(x) for x in dk]
-        ws = torch.empty(max(1, cpattn_bwd_workspace_bytes(self.desc(), self.q.shape[0])),
-                         dtype=torch.uint8, device=dev)
+        segs_ = [s_ for s_, _, _ in segs]
+        ws = torch.empty(max(1, cpattn_bwd_workspace_bytes(self.desc(), q_block(self.q, self.q_idx, self.q_doc),
+                                                            segs_)), dtype=torch.uint8, device=dev)
         return dq, dk, dv, ws
 
     def bwd(self, o, lse, g, bufs=None, granularity="owner", scale=0.0):

@@ -228,8 +228,12 @@ size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpa
  *  dk, dv           host arrays [n_segs] of device fp32 [segs[s].len, hkv, d] outputs:
  *                   the summed contribution of all local queries (and all query
  *                   heads of a group) to segment s's keys and values.
- *  workspace        device buffer of at least cpattn_bwd_workspace_bytes() bytes,
- *                   256-byte aligned; contents on entry are ignored.
+ *  workspace        256-byte aligned device buffer, at least q.len * hq * 4 bytes
+ *                   (rounded up to 256); cpattn_bwd_workspace_bytes() bytes enable the
+ *                   split dQ pass.  Contents on entry are ignored.
+ * Computed as three passes without atomics: D = rowsum(dO * O); dQ query-major
+ * (S and dP recomputed per key tile); dK/dV key-major with the per-owner sums in
+ * registers.
  * Errors: ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -237,8 +241,13 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
                float* dq, float* const* dk, float* const* dv, void* workspace,
                size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace cpattn_bwd needs for `q_len` local rows (0 on bad args). */
-size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, int64_t q_len);
+/* Bytes of device workspace for cpattn_bwd (0 on invalid arguments): the per-row
+ * rowsum(dO * O) values, plus room for the dQ pass to split its KV tiles over more
+ * work-groups when the local queries alone cannot fill the GPU.  A workspace that
+ * only holds the first part (q.len * hq * 4 bytes, rounded up to 256) is accepted
+ * and runs the dQ pass unsplit. */
+size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                  const cpattn_kv_seg* segs);
 
 #ifdef __cplusplus
 }

@@ -140,10 +140,16 @@ def test_forward_workspace_plan():
 
 def test_bwd_validation_and_workspace():
     d = desc()
-    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), 2048) == 2048 * 8 * 4
-    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), 3) == 256
-    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), -1) == 0
+    s1 = (C.cpattn_kv_seg * 1)(sg(64))
+    q3 = qb(3)
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q3), 1, s1) == 256
+    big = desc(hq=64, hkv=64)
+    q8k = qb(8192)
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(big), ctypes.byref(q8k), 1, s1) == 8192 * 64 * 4
+    segs4 = (C.cpattn_kv_seg * 4)(*[sg(2048)] * 4)
     q = qb(2048)
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 4, segs4) > 2048 * 8 * 4
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(qb(-1)), 4, segs4) == 0
     s = (C.cpattn_kv_seg * 1)(sg())
     p = (ctypes.c_void_p * 1)(FAKE)
     f32 = desc(dtype=C.F32)
@@ -151,6 +157,8 @@ def test_bwd_validation_and_workspace():
                             FAKE, 1 << 20, None) == C.ERR_UNSUPPORTED
     assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
                             FAKE, 100, None) == C.ERR_WORKSPACE
+    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(qb(65537)), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
+                            FAKE, 1 << 30, None) == C.ERR_UNSUPPORTED
     assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
                             None, 1 << 20, None) == C.ERR_WORKSPACE
     nul = (ctypes.c_void_p * 1)(None)

@@ -53,6 +53,23 @@ def test_bwd8k_rank(bwd8k, rank):
     check_bwd("bwd8k", q, k, v, g, w.cp, rank)
 
 
+def test_bwd8k_unsplit_dq_pass(bwd8k):
+    # a workspace holding only rowsum(dO*O) runs the dQ pass without KV splits
+    w, q, k, v, g = bwd8k
+    import context_causal_attention_zigzag_amd as C
+    rs, rows, gr, dq_split, dk_s, dv_s = run_bwd(q, k, v, g, w.cp, 1)
+    o, lse = rs.stream_fwd("owner")
+    dq, dk, dv, _ = rs.alloc_bwd_buffers()
+    small = torch.empty(rs.q.shape[0] * w.hq * 4, dtype=torch.uint8, device=DEV)
+    say("bwd8k unsplit dQ pass")
+    segs = [s_ for s_, _, _ in rs.segments("owner")]
+    C.cpattn_bwd(rs.desc(), C.q_block(rs.q, rs.q_idx), segs, o, lse, gr.to(DEV), dq, dk, dv, small)
+    torch.cuda.synchronize()
+    dq_r, _, _ = OA.attention_bwd(q[torch.as_tensor(rows)], k, v, gr, rows, np.arange(w.seq))
+    assert_close(dq, dq_r, TOL_BF16, "bwd8k r1 dQ unsplit")
+    assert_close(dq, dq_split, TOL_BF16, "bwd8k r1 dQ unsplit vs split")
+
+
 @pytest.mark.parametrize("seq,cp,hq,hkv,d", [(800, 4, 4, 2, 128), (512, 2, 8, 1, 64), (384, 2, 12, 4, 128)])
 def test_bwd_small_shapes_and_owner_sums(seq, cp, hq, hkv, d):
     q = workloads.randn((seq, hq, d), 21, "bf16", 0)
@@ -102,7 +119,8 @@ def test_bwd_fully_masked_rows_give_zero_gradients():
     dq = torch.full((tq, h, d), 7.0, device=DEV)
     dk = torch.full((tk, h, d), 7.0, device=DEV)
     dv = torch.full((tk, h, d), 7.0, device=DEV)
-    ws = torch.empty(C.cpattn_bwd_workspace_bytes(desc, tq), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(C.cpattn_bwd_workspace_bytes(desc, C.q_block(q, qpos), [C.kv_seg(k, v, kpos)]),
+                     dtype=torch.uint8, device=DEV)
     C.cpattn_bwd(desc, C.q_block(q, qpos), [C.kv_seg(k, v, kpos)], o, lse, g, dq, [dk], [dv], ws)
     torch.cuda.synchronize()
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
