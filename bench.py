@@ -11,12 +11,16 @@ One step = the whole hot path for that share:
 Useful FLOPs count visible (query, key) pairs only: S(S+1)/(2cp) per head for every
 zigzag rank; forward 4*d per pair per head (QK^T and PV), backward 10*d (five
 contractions).  value = useful FLOPs of the step (two forwards + one backward) / time.
+The backward runs as its three calls (delta, dQ, dK/dV) so each is timed on its own.
 
 Prints one JSON line (rank 0).  ``--workload s128k`` runs the 128K share instead.
+``--copy-mib N`` only runs a plain device copy of N MiB (``--steps`` times): the
+known-size reference that calibrates the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +31,51 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+CSRC = os.path.join(ROOT, "context_causal_attention_zigzag_amd", "csrc")
+# kernel -> (source files it is built from, counter summary under profiles/)
+# timed call -> the kernel it launches (rocprofv3 names it with its template arguments)
+KERNEL_OF = {"partition": "partition_kernel", "merge": "merge_kernel<true>", "bwd_delta": "bwd_delta_kernel<{d}>",
+             "bwd_dkdv": "bwd_dkdv_kernel<{d}>", "tile_fwd": "fwd_bf16_kernel<{d}, ...>",
+             "stream_fwd": "fwd_bf16_kernel<{d}, ...>", "bwd_dq": "bwd_dq_kernel<{d}>"}
+TRAFFIC = {"bwd_dkdv": (("bwd.hip", "kv_stream.h", "common.h"), "bwd_dkdv_kernel_{w}_traffic.txt")}
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    if kernel not in TRAFFIC:
+        return None
+    files, name = TRAFFIC[kernel]
+    path = os.path.join(ROOT, "profiles", name.format(w=workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_sha256") != source_hash(files):
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(mib, reps):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": reps}), flush=True)
 
 
 def main():
@@ -37,11 +86,15 @@ def main():
     ap.add_argument("--workload", default="s8k", choices=["s8k", "s128k"])
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the other ranks' KV segments are "
                                    "emulated as local buffers; --gpus above 1 is not supported"}))
         sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps)
+        return
 
     import numpy as np
     import torch
@@ -65,14 +118,19 @@ def main():
     l_t = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
     o_s = torch.empty_like(rs.q)
     l_s = torch.empty_like(l_t)
-    bwd_bufs = rs.alloc_bwd_buffers(gran)
+    dq, dk, dv, _ = rs.alloc_bwd_buffers(gran)
+    desc = rs.desc()
+    qblk = C.q_block(rs.q, rs.q_idx, rs.q_doc)
+    bsegs = [s_ for s_, _, _ in rs.segments(gran)]
+    delta = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
+    ws_dq = torch.empty(max(1, C.cpattn_bwd_dq_workspace_bytes(desc, qblk, bsegs)), dtype=torch.uint8, device=dev)
     ws_tile = rs.tile_workspace(edges)
     ws_stream = rs.stream_workspace(gran)
     # partition outputs of this rank (Q and its own K/V shard), rewritten every step
     p_idx = torch.empty(n_local, dtype=torch.int32, device=dev)
     p_out = [torch.empty((n_local,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in (gq, gk, gv)]
 
-    names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd"]
+    names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
     ev = {n: [] for n in names}
 
     def step(timed):
@@ -93,7 +151,11 @@ def main():
         mark()
         rs.stream_fwd(gran, o_s, l_s, workspace=ws_stream)
         mark()
-        rs.bwd(o_s, l_s, g, bwd_bufs, gran)
+        C.cpattn_bwd_delta(desc, o_s, g, delta)
+        mark()
+        C.cpattn_bwd_dq(desc, qblk, bsegs, l_s, delta, g, dq, ws_dq)
+        mark()
+        C.cpattn_bwd_dkdv(desc, qblk, bsegs, l_s, delta, g, dk, dv)
         mark()
         if timed:
             for i, n in enumerate(names):
@@ -110,26 +172,45 @@ def main():
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
     step_ms = sum(ms.values())
+    bwd_ms = ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"]
     pairs = w.seq * (w.seq + 1) // (2 * w.cp)
-    f_fwd = 4.0 * w.d * w.hq * pairs
-    f_bwd = 10.0 * w.d * w.hq * pairs
+    unit = w.d * w.hq * pairs            # (visible pair, head, head-dim element) units
+    f_fwd = 4.0 * unit
+    f_bwd = 10.0 * unit
     step_flops = 2 * f_fwd + f_bwd
     tflops = lambda f, t_ms: f / (t_ms * 1e-3) / 1e12  # noqa: E731
+    gbs = lambda b, t_ms: b / (t_ms * 1e-3) / 1e9  # noqa: E731
     # algorithmic bytes of the bandwidth-bound steps
     elt = 2
     part_bytes = 2 * n_local * (w.hq + 2 * w.hkv) * w.d * elt + 4 * n_local
     n_parts = [sum(1 for e in edges if e[0] == ch) for ch in rs.q_chunks()]
     merge_bytes = sum(n * (n_local // 2) * w.hq * (w.d * 4 + 4) for n in n_parts) + n_local * w.hq * (w.d * elt + 4)
-    per_kernel = {
-        "partition": {"us": ms["partition"] * 1e3, "GB/s": part_bytes / (ms["partition"] * 1e-3) / 1e9},
-        "tile_fwd": {"us": ms["tile_fwd"] * 1e3, "TFLOP/s": tflops(f_fwd, ms["tile_fwd"])},
-        "merge": {"us": ms["merge"] * 1e3, "GB/s": merge_bytes / (ms["merge"] * 1e-3) / 1e9},
-        "stream_fwd": {"us": ms["stream_fwd"] * 1e3, "TFLOP/s": tflops(f_fwd, ms["stream_fwd"])},
-        "bwd": {"us": ms["bwd"] * 1e3, "TFLOP/s": tflops(f_bwd, ms["bwd"])},
+    delta_bytes = n_local * w.hq * (2 * w.d * elt + 4)
+    # call -> (kernel launches, bound, algorithmic work, unit); the forward calls add a
+    # merge launch when their plan splits the KV tiles, the dQ call a sum launch
+    split_t = ws_tile is not None
+    split_s = ws_stream is not None
+    split_q = ws_dq.numel() > 1
+    calls = {
+        "partition": (1, "hbm", part_bytes),
+        "tile_fwd": (1 + split_t, "mfma", f_fwd),
+        "merge": (1, "hbm", merge_bytes),
+        "stream_fwd": (1 + split_s, "mfma", f_fwd),
+        "bwd_delta": (1, "hbm", delta_bytes),
+        "bwd_dq": (1 + split_q, "mfma", 2.0 * unit),   # dQ = dS K; S and dP recomputed, not counted
+        "bwd_dkdv": (1, "mfma", 8.0 * unit),            # S, dP, dV = P^T dO, dK = dS^T Q
     }
-    dom = max(["tile_fwd", "stream_fwd", "bwd"], key=lambda n: ms[n])
-    dom_flops = f_bwd if dom == "bwd" else f_fwd
-    achieved = tflops(dom_flops, ms[dom])
+    per_kernel = {}
+    for n, (launches, bound, work) in calls.items():
+        rate = gbs(work, ms[n]) if bound == "hbm" else tflops(work, ms[n])
+        per_kernel[n] = {"us": ms[n] * 1e3, ("GB/s" if bound == "hbm" else "TFLOP/s"): rate,
+                         "launches": launches}
+    per_kernel["bwd"] = {"us": bwd_ms * 1e3, "TFLOP/s": tflops(f_bwd, bwd_ms)}
+    # roofline of the dominant kernel: the longest call that is one launch
+    dom = max((n for n in calls if calls[n][0] == 1), key=lambda n: ms[n])
+    _, bound, work = calls[dom]
+    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    achieved = tflops(work, ms[dom]) if bound == "mfma" else gbs(work, ms[dom])
     out = {
         "metric": "causal attn TFLOP/s per rank-share (fwd, bwd) at 1 MI355X; % bf16 MFMA peak",
         "value": round(tflops(step_flops, step_ms), 3),
@@ -150,18 +231,24 @@ def main():
                    "visible_pairs_per_head": pairs},
         "pct_bf16_peak": round(100 * tflops(step_flops, step_ms) / PEAK_BF16_TFLOPS, 2),
         "per_kernel": {n: {kk: round(vv, 2) for kk, vv in d_.items()} for n, d_ in per_kernel.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "bwd_tflops": round(tflops(f_bwd, bwd_ms), 2),
+        "fwd_tflops": {"tile+merge": round(tflops(f_fwd, ms["tile_fwd"] + ms["merge"]), 2),
+                       "stream": round(tflops(f_fwd, ms["stream_fwd"]), 2)},
+        "roofline": {"kernel": KERNEL_OF[dom].format(d=w.d), "call": dom, "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, args.workload),
+                     "algorithmic": work},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, w, r)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(q, k, v, w, r):
+def cpu_baseline(q, k, v, w, r, min_seconds=12.0, max_reps=8):
     """The float64 oracle, as it stands, on a bounded sample of the same share: forward and
-    backward of every 2nd local query row against all keys."""
+    backward of the rank's query rows against all keys, repeated until about
+    ``min_seconds`` of CPU work (the 8K share is small); for larger shares an evenly
+    spaced subset of the rows, sized for one repetition of about that length."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -169,19 +256,27 @@ def cpu_baseline(q, k, v, w, r):
     import oracle
     from oracle import attention as OA
 
-    rows = oracle.zigzag_indices(w.seq, w.cp, r)[::2]
+    rows = oracle.zigzag_indices(w.seq, w.cp, r)
+    if w.seq > 8192:
+        rows = rows[:: max(1, len(rows) // 64)]
     g = torch.randn((len(rows), w.hq, w.d), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
-    t0 = time.perf_counter()
-    OA.attention_fwd(q[torch.as_tensor(rows)], k, v, rows, np.arange(w.seq))
-    OA.attention_bwd(q[torch.as_tensor(rows)], k, v, g, rows, np.arange(w.seq))
-    dt = time.perf_counter() - t0
+    qr = q[torch.as_tensor(rows)]
+    keys = np.arange(w.seq)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OA.attention_fwd(qr, k, v, rows, keys)
+        OA.attention_bwd(qr, k, v, g, rows, keys)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps or w.seq > 8192:
+            break
     pairs = int(np.sum(rows + 1))
-    flops = (4.0 + 10.0) * w.d * w.hq * pairs
+    flops = reps * (4.0 + 10.0) * w.d * w.hq * pairs
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 numpy oracle, forward + backward of {len(rows)} of the rank's "
-                      f"{w.seq // w.cp} query rows (every 2nd) against all {w.seq} keys, all {w.hq} heads; "
-                      f"useful FLOPs counted on visible pairs; {dt:.1f} s"}
+                      f"{w.seq // w.cp} query rows against all {w.seq} keys, all {w.hq} heads, "
+                      f"{reps} repetition(s); useful FLOPs counted on visible pairs; {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -76,10 +76,22 @@ lib.cpattn_bwd.restype = _c_i32
 lib.cpattn_bwd_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
                                            _P(cpattn_kv_seg)]
 lib.cpattn_bwd_workspace_bytes.restype = _c_sz
+lib.cpattn_bwd_delta.argtypes = [_P(cpattn_attn_desc), _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]
+lib.cpattn_bwd_delta.restype = _c_i32
+lib.cpattn_bwd_dq.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
+                              _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
+lib.cpattn_bwd_dq.restype = _c_i32
+lib.cpattn_bwd_dq_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
+                                              _P(cpattn_kv_seg)]
+lib.cpattn_bwd_dq_workspace_bytes.restype = _c_sz
+lib.cpattn_bwd_dkdv.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
+                                _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp]
+lib.cpattn_bwd_dkdv.restype = _c_i32
 
 EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
             "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
-            "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes")
+            "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
+            "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv")
 
 
 class CpattnError(RuntimeError):
@@ -246,3 +258,36 @@ def cpattn_bwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o, lse, dout, dq
                         0 if workspace is None else workspace.numel() * workspace.element_size(),
                         _stream(stream))
     _check(st, "cpattn_bwd")
+
+
+def cpattn_bwd_delta(desc: cpattn_attn_desc, o, dout, delta, stream=None):
+    """D = rowsum(dout * o) per (row, head) into fp32 ``delta`` [rows, hq]."""
+    rows = 0 if o is None else o.shape[0]
+    st = lib.cpattn_bwd_delta(ctypes.byref(desc), rows, _ptr(o) if rows else None,
+                              _ptr(dout) if rows else None, _ptr(delta) if rows else None, _stream(stream))
+    _check(st, "cpattn_bwd_delta")
+
+
+def cpattn_bwd_dq_workspace_bytes(desc: cpattn_attn_desc, q: cpattn_q_block, segs) -> int:
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    return int(lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(desc), ctypes.byref(q), len(segs), sa))
+
+
+def cpattn_bwd_dq(desc: cpattn_attn_desc, q: cpattn_q_block, segs, lse, delta, dout, dq, workspace=None,
+                  stream=None):
+    """dQ pass of the backward (``workspace``: uint8 device tensor or None = unsplit)."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    wp, wb = _ws_args(workspace)
+    st = lib.cpattn_bwd_dq(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(lse), _ptr(delta),
+                           _ptr(dout), _ptr(dq), wp, wb, _stream(stream))
+    _check(st, "cpattn_bwd_dq")
+
+
+def cpattn_bwd_dkdv(desc: cpattn_attn_desc, q: cpattn_q_block, segs, lse, delta, dout, dk, dv,
+                    stream=None):
+    """dK/dV pass of the backward: per-segment sums over all local rows."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    st = lib.cpattn_bwd_dkdv(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(lse), _ptr(delta),
+                             _ptr(dout), _vp_array([_ptr(x) for x in dk]), _vp_array([_ptr(x) for x in dv]),
+                             _stream(stream))
+    _check(st, "cpattn_bwd_dkdv")

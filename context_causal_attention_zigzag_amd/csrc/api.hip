@@ -282,45 +282,77 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
-                                  const cpattn_kv_seg* segs) {
-  if (check_desc(desc) != CPATTN_OK || check_qblock(desc, q) != CPATTN_OK) return 0;
-  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return 0;
-  for (int s = 0; s < n_segs; ++s)
-    if (check_seg(desc, &segs[s]) != CPATTN_OK) return 0;
-  const size_t delta = bwd_delta_bytes(desc, q->len);
-  if (q->len == 0) return delta;
-  FwdArgs f{};
-  fill_common(f, desc);
-  fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);
-  return delta + plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true);
-}
+}  // extern "C"
 
-int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
-               const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout, float* dq,
-               float* const* dk, float* const* dv, void* workspace, size_t workspace_bytes,
-               void* stream) {
+namespace {
+
+// Checks shared by the backward calls (bf16 only): description, query block, segments.
+int check_bwd_problem(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                      const cpattn_kv_seg* segs) {
   int st = check_desc(desc);
   if (st != CPATTN_OK) return st;
   if (desc->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
   if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
-  if (q->len > bwd_max_rows()) return CPATTN_ERR_UNSUPPORTED;
-  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr || dk == nullptr || dv == nullptr)
-    return CPATTN_ERR_ARG;
-  for (int s = 0; s < n_segs; ++s) {
+  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return CPATTN_ERR_ARG;
+  for (int s = 0; s < n_segs; ++s)
     if ((st = check_seg(desc, &segs[s])) != CPATTN_OK) return st;
-    if (segs[s].len > 0) {
-      if (dk[s] == nullptr || dv[s] == nullptr) return CPATTN_ERR_ARG;
-      if (!aligned16(dk[s]) || !aligned16(dv[s])) return CPATTN_ERR_ALIGN;
-    }
+  return CPATTN_OK;
+}
+
+// Per-row inputs of the dQ and dK/dV passes (only read when there are local rows).
+int check_bwd_rows(const cpattn_q_block* q, const float* lse, const float* delta, const void* dout) {
+  if (q->len == 0) return CPATTN_OK;
+  if (lse == nullptr || delta == nullptr || dout == nullptr) return CPATTN_ERR_ARG;
+  return aligned16(dout) ? CPATTN_OK : CPATTN_ERR_ALIGN;
+}
+
+int check_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                 const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                 const float* dq) {
+  int st = check_bwd_problem(desc, q, n_segs, segs);
+  if (st != CPATTN_OK) return st;
+  if ((st = check_bwd_rows(q, lse, delta, dout)) != CPATTN_OK) return st;
+  if (q->len > 0 && dq == nullptr) return CPATTN_ERR_ARG;
+  if (q->len > 0 && !aligned16(dq)) return CPATTN_ERR_ALIGN;
+  return CPATTN_OK;
+}
+
+int check_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                   const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                   float* const* dk, float* const* dv) {
+  int st = check_bwd_problem(desc, q, n_segs, segs);
+  if (st != CPATTN_OK) return st;
+  if (q->len > bwd_max_rows()) return CPATTN_ERR_UNSUPPORTED;
+  if ((st = check_bwd_rows(q, lse, delta, dout)) != CPATTN_OK) return st;
+  if (dk == nullptr || dv == nullptr) return CPATTN_ERR_ARG;
+  for (int s = 0; s < n_segs; ++s) {
+    if (segs[s].len == 0) continue;
+    if (dk[s] == nullptr || dv[s] == nullptr) return CPATTN_ERR_ARG;
+    if (!aligned16(dk[s]) || !aligned16(dv[s])) return CPATTN_ERR_ALIGN;
   }
-  const size_t delta_bytes = bwd_delta_bytes(desc, q->len);
-  if (q->len > 0) {
-    if (o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr) return CPATTN_ERR_ARG;
-    if (!aligned16(o) || !aligned16(dout) || !aligned16(dq)) return CPATTN_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < delta_bytes) return CPATTN_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
-  }
+  return CPATTN_OK;
+}
+
+// The dQ pass as one query-major job over the segments; split over KV tiles into the
+// workspace when it holds the plan's partial buffers.
+hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                      const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                      float* dq, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (q->len == 0) return hipSuccess;
+  FwdArgs f{};
+  fill_common(f, desc);
+  fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
+  const int cus = device_cus();
+  size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true);
+  if (need > 0 && (workspace == nullptr || need > workspace_bytes))
+    need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false);  // too small: no split
+  if (need > 0) assign_fwd_workspace(f, desc->d, workspace);
+  return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, stream);
+}
+
+hipError_t run_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                        const cpattn_kv_seg* segs, const float* lse, const float* delta,
+                        const void* dout, float* const* dk, float* const* dv, hipStream_t stream) {
   BwdArgs a{};
   for (int s = 0; s < n_segs; ++s) {
     a.segs[s] = to_seg(segs[s]);
@@ -330,10 +362,9 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   a.q = q->q;
   a.qpos = q->pos;
   a.qdoc = q->doc;
-  a.o = o;
   a.lse = lse;
   a.dout = dout;
-  a.delta = reinterpret_cast<float*>(workspace);
+  a.delta = delta;
   a.q_len = (int32_t)q->len;
   a.n_segs = n_segs;
   a.hq = desc->hq;
@@ -342,19 +373,91 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   a.mask = desc->mask;
   a.scale = eff_scale(desc);
   a.scale_log2 = a.scale * kLog2e;
-  // dQ pass: one query-major job over the same segments, split like a forward job
+  return launch_bwd_dkdv(a, desc->d, stream);
+}
+
+size_t bwd_dq_split_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                          const cpattn_kv_seg* segs) {
+  if (q->len == 0) return 0;
   FwdArgs f{};
   fill_common(f, desc);
-  fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
+  fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);
+  return plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpattn_bwd_delta(const cpattn_attn_desc* desc, int64_t rows, const void* o, const void* dout,
+                     float* delta, void* stream) {
+  int st = check_desc(desc);
+  if (st != CPATTN_OK) return st;
+  if (desc->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
+  if (rows < 0 || rows > INT32_MAX) return CPATTN_ERR_ARG;
+  if (rows == 0) return CPATTN_OK;
+  if (o == nullptr || dout == nullptr || delta == nullptr) return CPATTN_ERR_ARG;
+  if (!aligned16(o) || !aligned16(dout)) return CPATTN_ERR_ALIGN;
+  return hip_status(launch_bwd_delta(o, dout, delta, rows * desc->hq, desc->d,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t cpattn_bwd_dq_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                     const cpattn_kv_seg* segs) {
+  if (check_bwd_problem(desc, q, n_segs, segs) != CPATTN_OK) return 0;
+  return bwd_dq_split_bytes(desc, q, n_segs, segs);
+}
+
+int cpattn_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                  const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                  float* dq, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq);
+  if (st != CPATTN_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
+  return hip_status(run_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq, workspace, workspace_bytes,
+                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cpattn_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                    const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                    float* const* dk, float* const* dv, void* stream) {
+  const int st = check_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv);
+  if (st != CPATTN_OK) return st;
+  return hip_status(run_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv,
+                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                  const cpattn_kv_seg* segs) {
+  if (check_bwd_problem(desc, q, n_segs, segs) != CPATTN_OK) return 0;
+  return bwd_delta_bytes(desc, q->len) + bwd_dq_split_bytes(desc, q, n_segs, segs);
+}
+
+int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+               const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout, float* dq,
+               float* const* dk, float* const* dv, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_bwd_problem(desc, q, n_segs, segs);
+  if (st != CPATTN_OK) return st;
+  const size_t delta_bytes = bwd_delta_bytes(desc, q->len);
+  float* delta = reinterpret_cast<float*>(workspace);
   if (q->len > 0) {
-    const int cus = device_cus();
-    char* rest = reinterpret_cast<char*>(workspace) + delta_bytes;
-    const size_t avail = workspace_bytes - delta_bytes;
-    size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true);
-    if (need > avail) need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false);  // too small: no split
-    if (need > 0) assign_fwd_workspace(f, desc->d, rest);
+    if (o == nullptr) return CPATTN_ERR_ARG;
+    if (!aligned16(o)) return CPATTN_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < delta_bytes) return CPATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
   }
-  return hip_status(launch_bwd(a, f, a.scale, desc->d, reinterpret_cast<hipStream_t>(stream)));
+  if ((st = check_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq)) != CPATTN_OK) return st;
+  if ((st = check_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv)) != CPATTN_OK) return st;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_bwd_delta(o, dout, delta, q->len * desc->hq, desc->d, hs);
+  if (e == hipSuccess) {
+    char* rest = q->len > 0 ? reinterpret_cast<char*>(workspace) + delta_bytes : nullptr;
+    e = run_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq, rest,
+                   q->len > 0 ? workspace_bytes - delta_bytes : 0, hs);
+  }
+  if (e == hipSuccess) e = run_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv, hs);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -550,34 +550,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
-hipError_t launch_bwd_d(BwdArgs& a, FwdArgs& f, const DqExtra& x, hipStream_t stream) {
-  const int64_t pairs = (int64_t)a.q_len * a.hq;
-  if (pairs > 0) {
-    const int64_t threads = pairs * (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(a.o),
-                       reinterpret_cast<const bf16*>(a.dout), a.delta, pairs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // dQ, query-major (work-groups as in the forward kernel)
-    const int qt_rows = (kv::kThreads / kWave) * kv::kRowsPerWave / f.heads_per_wg;
-    int total = 0;
-    for (int j = 0; j < f.n_jobs; ++j) {
-      f.jobs[j].wg_begin = total;
-      total += ((f.jobs[j].len + qt_rows - 1) / qt_rows) * (f.hq / f.heads_per_wg) * f.jobs[j].n_split;
-    }
-    f.total_wgs = total;
-    f.padded_wgs = (total + 7) & ~7;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(f.padded_wgs), dim3(kThreads), 0, stream, f, x);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (f.jobs[0].n_split > 1) {
-      e = launch_merge_split_jobs(f, D, 1, stream, true);
-      if (e != hipSuccess) return e;
-    }
+}  // namespace
+
+hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t pairs, int d,
+                            hipStream_t stream) {
+  if (pairs == 0) return hipSuccess;
+  const int64_t threads = pairs * (d / 8);
+  const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+  if (d == 64)
+    hipLaunchKernelGGL((bwd_delta_kernel<64>), grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const bf16*>(o), reinterpret_cast<const bf16*>(dout), delta, pairs);
+  else
+    hipLaunchKernelGGL((bwd_delta_kernel<128>), grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const bf16*>(o), reinterpret_cast<const bf16*>(dout), delta, pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* delta, float scale, int d,
+                         hipStream_t stream) {
+  FwdArgs f = args;
+  // work-groups as in the forward kernel
+  const int qt_rows = (kv::kThreads / kWave) * kv::kRowsPerWave / f.heads_per_wg;
+  int total = 0;
+  for (int j = 0; j < f.n_jobs; ++j) {
+    f.jobs[j].wg_begin = total;
+    total += ((f.jobs[j].len + qt_rows - 1) / qt_rows) * (f.hq / f.heads_per_wg) * f.jobs[j].n_split;
   }
-  // dK/dV, key-major
+  if (total == 0) return hipSuccess;
+  f.total_wgs = total;
+  f.padded_wgs = (total + 7) & ~7;
+  const DqExtra x{dout, delta, scale};
+  if (d == 64)
+    hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(f.padded_wgs), dim3(kThreads), 0, stream, f, x);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(f.padded_wgs), dim3(kThreads), 0, stream, f, x);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int j = 0; j < f.n_jobs; ++j)
+    if (f.jobs[j].n_split > 1) return launch_merge_split_jobs(f, d, 1, stream, true);
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& args, int d, hipStream_t stream) {
+  BwdArgs a = args;
   int total = 0;
   for (int s = 0; s < a.n_segs; ++s) {
     a.seg_wg_begin[s] = total;
@@ -587,20 +602,13 @@ hipError_t launch_bwd_d(BwdArgs& a, FwdArgs& f, const DqExtra& x, hipStream_t st
   a.total_wgs = total;
   a.padded_wgs = (total + 7) & ~7;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+  if (d == 64)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-}  // namespace
-
 int bwd_max_rows() { return kMaxQTiles * kBQ; }
-
-hipError_t launch_bwd(const BwdArgs& args, const FwdArgs& dq_args, float scale, int d, hipStream_t stream) {
-  BwdArgs a = args;
-  FwdArgs f = dq_args;
-  DqExtra x{args.dout, args.delta, scale};
-  if (d == 64) return launch_bwd_d<64>(a, f, x, stream);
-  return launch_bwd_d<128>(a, f, x, stream);
-}
 
 }  // namespace cpattn

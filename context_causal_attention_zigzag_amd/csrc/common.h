@@ -187,12 +187,11 @@ struct BwdArgs {
   const void* q;
   const int32_t* qpos;
   const int32_t* qdoc;
-  const void* o;
   const float* lse;
   const void* dout;
   float* dk[kMaxSegs];
   float* dv[kMaxSegs];
-  float* delta;          // workspace [q_len, hq]: rowsum(dO * O)
+  const float* delta;    // [q_len, hq]: rowsum(dO * O)
   int32_t q_len;
   int32_t n_segs;
   int32_t seg_wg_begin[kMaxSegs + 1];
@@ -220,8 +219,13 @@ void assign_fwd_workspace(FwdArgs& a, int d, void* ws);
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
                         hipStream_t stream);
-// Backward: delta, dQ (query-major, `dq` holds its jobs / split plan / workspace), dK/dV.
-hipError_t launch_bwd(const BwdArgs& a, const FwdArgs& dq, float scale, int d, hipStream_t stream);
+// Backward passes: delta = rowsum(dO * O) over `pairs` (row, head) pairs; dQ
+// (query-major, `dq` holds its job, split plan and partial buffers); dK/dV (key-major).
+hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t pairs, int d,
+                            hipStream_t stream);
+hipError_t launch_bwd_dq(const FwdArgs& dq, const void* dout, const float* delta, float scale, int d,
+                         hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t stream);
 int bwd_max_rows();  // local query rows the backward kernel supports
 // One launch merging the KV splits of every split job of a forward launch.
 hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream,

@@ -231,9 +231,9 @@ size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpa
  *  workspace        256-byte aligned device buffer, at least q.len * hq * 4 bytes
  *                   (rounded up to 256); cpattn_bwd_workspace_bytes() bytes enable the
  *                   split dQ pass.  Contents on entry are ignored.
- * Computed as three passes without atomics: D = rowsum(dO * O); dQ query-major
- * (S and dP recomputed per key tile); dK/dV key-major with the per-owner sums in
- * registers.
+ * Computed as three passes without atomics — the calls below, in this order:
+ * cpattn_bwd_delta into the start of the workspace, cpattn_bwd_dq with the rest of
+ * the workspace, cpattn_bwd_dkdv.
  * Errors: ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -248,6 +248,56 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
  * and runs the dQ pass unsplit. */
 size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                                   const cpattn_kv_seg* segs);
+
+/*
+ * The three passes of cpattn_bwd as separate calls, for callers that schedule them
+ * around communication: D once per backward, then per arriving KV segment the
+ * dK/dV pass (whose result can go back to the segment's owner at once) and the dQ
+ * pass.  Running cpattn_bwd_delta, cpattn_bwd_dq and cpattn_bwd_dkdv over the same
+ * arguments gives exactly the outputs of cpattn_bwd.  Same source as cpattn_bwd.
+ */
+
+/* cpattn_bwd_delta — D_i = sum_d G_i * O_i per (row, head), the term the softmax
+ * derivative subtracts from dP (dS = P (dP - D)).
+ *  rows             local query rows (>= 0); 0 is a no-op.
+ *  o, dout          device [rows, hq, d] bf16 forward output and upstream gradient
+ *                   (16-byte aligned).
+ *  delta            device fp32 [rows, hq] output.
+ * Errors: ARG, ALIGN, UNSUPPORTED (fp32 inputs), HIP. */
+int cpattn_bwd_delta(const cpattn_attn_desc* desc, int64_t rows, const void* o, const void* dout,
+                     float* delta, void* stream);
+
+/* cpattn_bwd_dq — dQ_i = scale * sum_j dS_ij K_j over every visible key of the
+ * segments, with P and dP rebuilt per key tile (query-major pass).
+ *  q, n_segs, segs  as for cpattn_bwd.
+ *  lse, delta       device fp32 [q.len, hq]: forward log-sum-exp and cpattn_bwd_delta.
+ *  dout             device [q.len, hq, d] bf16 upstream gradient.
+ *  dq               device fp32 [q.len, hq, d] output.
+ *  workspace        NULL, or a 256-byte aligned device buffer; with
+ *                   cpattn_bwd_dq_workspace_bytes() bytes the KV tiles of each query
+ *                   tile are split over more work-groups when the queries alone cannot
+ *                   fill the GPU (fp32 partial sums, added in a second launch);
+ *                   a smaller buffer runs unsplit.  Contents on entry are ignored.
+ * Errors: ARG, ALIGN, UNSUPPORTED, HIP. */
+int cpattn_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                  const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                  float* dq, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that let cpattn_bwd_dq split (0: no split planned or invalid arguments). */
+size_t cpattn_bwd_dq_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                     const cpattn_kv_seg* segs);
+
+/* cpattn_bwd_dkdv — per segment s: dV_s = sum_i P_is^T G_i and dK_s = scale *
+ * sum_i dS_is^T Q_i over all local query rows i (and all query heads of each kv
+ * head's group): the contribution this rank returns to the owner of segment s.
+ * One launch, key-major.
+ *  q, n_segs, segs  as for cpattn_bwd (at most 65536 local rows).
+ *  lse, delta, dout as for cpattn_bwd_dq.
+ *  dk, dv           as for cpattn_bwd.
+ * Errors: ARG, ALIGN, UNSUPPORTED, HIP. */
+int cpattn_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                    const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
+                    float* const* dk, float* const* dv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -164,3 +164,47 @@ def test_bwd_validation_and_workspace():
     nul = (ctypes.c_void_p * 1)(None)
     assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, nul, p,
                             FAKE, 1 << 20, None) == C.ERR_ARG
+
+
+def test_bwd_pass_calls_validation():
+    d = desc()
+    f32 = desc(dtype=C.F32)
+    lib = C.lib
+    # delta: dtype, size, pointers, alignment; zero rows is a no-op that touches nothing
+    assert lib.cpattn_bwd_delta(ctypes.byref(f32), 64, FAKE, FAKE, FAKE, None) == C.ERR_UNSUPPORTED
+    assert lib.cpattn_bwd_delta(ctypes.byref(d), -1, FAKE, FAKE, FAKE, None) == C.ERR_ARG
+    assert lib.cpattn_bwd_delta(ctypes.byref(d), 0, None, None, None, None) == C.OK
+    assert lib.cpattn_bwd_delta(ctypes.byref(d), 64, FAKE, None, FAKE, None) == C.ERR_ARG
+    assert lib.cpattn_bwd_delta(ctypes.byref(d), 64, FAKE + 8, FAKE, FAKE, None) == C.ERR_ALIGN
+    s4 = (C.cpattn_kv_seg * 4)(*[sg(2048)] * 4)
+    q = qb(2048)
+    # dQ workspace = the combined call's workspace minus the delta rows
+    full = lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 4, s4)
+    assert lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 4, s4) == full - 2048 * 8 * 4
+    assert lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(f32), ctypes.byref(q), 4, s4) == 0
+    assert lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 0, s4) == 0
+    # dQ: missing per-row inputs, output, alignment
+    assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, None, FAKE, FAKE, None, 0,
+                             None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, None, None, 0,
+                             None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE + 4, FAKE, None, 0,
+                             None) == C.ERR_ALIGN
+    assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
+                             1 << 20, None) == C.ERR_ALIGN
+    assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(qb(0)), 4, s4, None, None, None, None, None, 0,
+                             None) == C.OK
+    # dK/dV: row limit, output tables, alignment
+    p = (ctypes.c_void_p * 4)(*[FAKE] * 4)
+    nul = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    odd = (ctypes.c_void_p * 4)(FAKE, FAKE + 4, FAKE, FAKE)
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(qb(65537)), 4, s4, FAKE, FAKE, FAKE, p, p,
+                               None) == C.ERR_UNSUPPORTED
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, None, p,
+                               None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, p, nul,
+                               None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, odd, p,
+                               None) == C.ERR_ALIGN
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(f32), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, p, p,
+                               None) == C.ERR_UNSUPPORTED

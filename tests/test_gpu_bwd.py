@@ -70,6 +70,31 @@ def test_bwd8k_unsplit_dq_pass(bwd8k):
     assert_close(dq, dq_split, TOL_BF16, "bwd8k r1 dQ unsplit vs split")
 
 
+def test_bwd8k_pass_calls_match_combined_call(bwd8k):
+    # delta, dQ and dK/dV as separate calls give exactly what cpattn_bwd gives
+    w, q, k, v, g = bwd8k
+    import context_causal_attention_zigzag_amd as C
+    rs, rows, gr, dq_c, dk_c, dv_c = run_bwd(q, k, v, g, w.cp, 2)
+    o, lse = rs.stream_fwd("owner")
+    gd = gr.to(DEV)
+    dq, dk, dv, _ = rs.alloc_bwd_buffers()
+    desc = rs.desc()
+    qb = C.q_block(rs.q, rs.q_idx)
+    segs = [s_ for s_, _, _ in rs.segments("owner")]
+    delta = torch.empty((rs.q.shape[0], w.hq), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(1, C.cpattn_bwd_dq_workspace_bytes(desc, qb, segs)), dtype=torch.uint8, device=DEV)
+    say("bwd8k pass calls")
+    C.cpattn_bwd_delta(desc, o, gd, delta)
+    C.cpattn_bwd_dq(desc, qb, segs, lse, delta, gd, dq, ws)
+    C.cpattn_bwd_dkdv(desc, qb, segs, lse, delta, gd, dk, dv)
+    torch.cuda.synchronize()
+    d_ref = (o.double() * gd.double()).sum(-1).float()
+    assert_close(delta, d_ref, 1e-3, "bwd8k r2 delta")
+    assert torch.equal(dq, dq_c)
+    for a, b in zip(dk + dv, dk_c + dv_c):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("seq,cp,hq,hkv,d", [(800, 4, 4, 2, 128), (512, 2, 8, 1, 64), (384, 2, 12, 4, 128)])
 def test_bwd_small_shapes_and_owner_sums(seq, cp, hq, hkv, d):
     q = workloads.randn((seq, hq, d), 21, "bf16", 0)
