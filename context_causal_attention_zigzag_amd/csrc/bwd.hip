@@ -63,7 +63,9 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
 // ---------------------------------------------------------------------------
 // dQ pass
 template <int D>
-using DqSmem = kv::KvSmem<D, D + 32, D + 8>;  // K: row reads and transposing reads; V: row reads
+// K is read both as rows and transposed (row stride D + 24: conflict-free for both on
+// gfx950), V only as rows (D + 8).
+using DqSmem = kv::KvSmem<D, D + 24, D + 8>;
 
 struct DqExtra {
   const void* dout;
@@ -263,79 +265,72 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
 
 // ---------------------------------------------------------------------------
 // dK/dV pass
+//
+// Software pipeline over the query tiles a work-group visits (per wave, tile i):
+//   S_i, dP_i contractions  ->  dV/dK contractions of tile i-1, interleaved with the
+//   P_i / dS_i arithmetic (independent of them)  ->  next iteration.
+// Tiles i-1 and i are read while tiles i+1 and i+2 land in LDS (direct global->LDS
+// fills issued two iterations ahead), so four tile buffers rotate.
+constexpr int kQBufs = 4;
+
 template <int D>
-struct BwdSmem {
-  // Row stride for gfx950's 64-bank LDS: transposing reads are conflict-free at 16
-  // (mod 64) dwords, 16-byte row reads at 4 (mod 16) dwords; Q and dO serve both,
-  // with twice as many transposing reads.
-  static constexpr int kRS = D + 32;
-  bf16 qs[2][kBQ * kRS];
-  bf16 dos[2][kBQ * kRS];
-  float lse2[2][kBQ];
-  float delta[2][kBQ];
-  int32_t qpos[2][kBQ];
-  int32_t qdoc[2][kBQ];
+struct DkdvSmem {
+  // Row stride (elements) measured on gfx950 to serve both access patterns of these
+  // tiles without bank conflicts: 16-byte row reads and transposing reads (D + 24:
+  // 304 bytes for D = 128; D + 32 conflicts on row reads, D + 8 on transposing reads).
+  static constexpr int kRS = D + 24;
+  static constexpr int kSlots = kRS / 8;                                // 16-byte slots per row
+  static constexpr int kTileInst = (kBQ * kSlots + kWave - 1) / kWave;  // fill instructions per tile
+  // image of one tile: the rows, then slack that the last fill instruction's slots
+  // past the last row write into
+  static constexpr int kImage = kTileInst * kWave * 8;  // elements
+  static constexpr int kBigPer = 2 * kTileInst / 4;      // Q and dO fill instructions per wave
+  static constexpr int kFillPer = kBigPer + 1;            // + one 4-byte-per-lane fill
+  static_assert(2 * kTileInst % 4 == 0, "whole fill instructions per wave");
+  alignas(16) bf16 qs[kQBufs][kImage];
+  alignas(16) bf16 dos[kQBufs][kImage];
+};
+
+// Per-row values of the query tiles and the tile range table: a separate LDS object
+// from the tile images, so that reading them never waits on outstanding image fills.
+struct RowSmem {
+  alignas(16) float ld[kQBufs][2][kBQ];    // log-sum-exp, then delta, of the tile's rows
+  alignas(16) int32_t pd[kQBufs][2][kBQ];  // positions, then document ids
   // first/last position and document of every query tile
   int32_t qtab[4][kMaxQTiles];
 };
 
-template <int D>
-struct QStageRegs {
-  static constexpr int kChunks = kBQ * D / 8 / 128;  // 16-byte chunks per thread
-  u32x4 x[kChunks];  // rows of Q (threads 0..127) or of dO (threads 128..255)
-  float lse2, delta;
-  int32_t pos, doc;
-};
+// A kernel-argument pointer held in scalar registers.
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>((uint64_t)hi << 32 | lo);
+}
 
+// Per-lane source slots of the Q / dO fill instructions: fill instruction jj of a tile
+// writes the 64 16-byte slots 64*jj .. 64*jj+63 of the tile image, lane l slot
+// 64*jj + l (row-major, kSlots per row, the last ones padding).
 template <int D>
-__device__ __forceinline__ void load_qstage(QStageRegs<D>& r, const BwdArgs& a, const bf16* base, int head,
-                                            int r0, int tid) {
-  constexpr int kCPR = D / 8;
-  const int u = tid & 127;
+struct QFillPlan {
+  using Sm = DkdvSmem<D>;
+  uint32_t slot[Sm::kBigPer];  // row << 16 | element column
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
-    const int c = u + 128 * i;
-    const int row = r0 + c / kCPR, dc = c % kCPR;
-    r.x[i] = row < a.q_len ? *reinterpret_cast<const u32x4*>(base + ((int64_t)row * a.hq + head) * D + dc * 8)
-                           : u32x4{0, 0, 0, 0};
-  }
-  if (tid < kBQ) {
-    const int row = r0 + tid;
-    if (row < a.q_len) {
-      const float l = a.lse[(int64_t)row * a.hq + head];
-      r.lse2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // a row with no key adds nothing
-      r.delta = a.delta[(int64_t)row * a.hq + head];
-      r.pos = a.qpos[row];
-      r.doc = a.mask == kMaskCausalDoc ? a.qdoc[row] : 0;
-    } else {
-      r.lse2 = __builtin_inff();
-      r.delta = 0.0f;
-      r.pos = -kPosPad - 1;  // sees nothing
-      r.doc = 0;
+    for (int j = 0; j < Sm::kBigPer; ++j) {
+      const int jj = (wave + 4 * j) % Sm::kTileInst;
+      const int s = kWave * jj + lane;
+      const int c = s % Sm::kSlots;
+      // slots past the last row (slack) and padding slots load a valid dummy chunk
+      slot[j] = (uint32_t)min(s / Sm::kSlots, kBQ - 1) << 16 | (uint32_t)(c < D / 8 ? c * 8 : 0);
     }
   }
-}
+};
 
-template <int D>
-__device__ __forceinline__ void store_qstage(BwdSmem<D>& sm, int buf, const QStageRegs<D>& r, int tid) {
-  constexpr int kCPR = D / 8, kRS = BwdSmem<D>::kRS;
-  bf16* dst = (tid >> 7) ? sm.dos[buf] : sm.qs[buf];
-  const int u = tid & 127;
-#pragma unroll
-  for (int i = 0; i < QStageRegs<D>::kChunks; ++i) {
-    const int c = u + 128 * i;
-    *reinterpret_cast<u32x4*>(&dst[(c / kCPR) * kRS + (c % kCPR) * 8]) = r.x[i];
-  }
-  if (tid < kBQ) {
-    sm.lse2[buf][tid] = r.lse2;
-    sm.delta[buf][tid] = r.delta;
-    sm.qpos[buf][tid] = r.pos;
-    sm.qdoc[buf][tid] = r.doc;
-  }
-}
-
-struct QRef {
-  int hh;  // head within the kv group
+struct QItem {
+  int hh;  // head within the kv group (-1: none)
   int qt;  // query tile
 };
 
@@ -343,15 +338,14 @@ struct QRange {
   int pmin, pmax, dmin, dmax;
 };
 
-template <int D>
-__device__ __forceinline__ QRange qrange(const BwdSmem<D>& sm, int t) {
+__device__ __forceinline__ QRange qrange(const RowSmem& sm, int t) {
   return {sm.qtab[0][t], sm.qtab[1][t], sm.qtab[2][t], sm.qtab[3][t]};
 }
 
-// Next visible (head, query tile) at or after (hh, qt) for the key range [kmin, kmax].
-template <int D>
-__device__ __forceinline__ QRef next_qtile(const BwdSmem<D>& sm, const BwdArgs& a, int hh, int qt, int n_qt,
-                                           int kmin, int kmax, int kdmin, int kdmax) {
+// Next visible (head, query tile) after `it` for the key range [kmin, kmax].
+__device__ __forceinline__ QItem next_qitem(const RowSmem& sm, const BwdArgs& a, QItem it, int n_qt, int kmin,
+                                            int kmax, int kdmin, int kdmax) {
+  int hh = it.hh, qt = it.qt + 1;
   for (; hh < a.group; ++hh, qt = 0) {
     for (; qt < n_qt; ++qt) {
       const QRange q = qrange(sm, qt);
@@ -362,76 +356,235 @@ __device__ __forceinline__ QRef next_qtile(const BwdSmem<D>& sm, const BwdArgs& 
   return {-1, 0};
 }
 
-// One (32-row query tile, this wave's 32 keys) block: S = Q K^T and dP = dO V^T from
-// row-major LDS rows and register-resident K/V; P and dS in the accumulator layout;
-// dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by transposing
-// LDS reads in the accumulators' contraction order.
-// `masked` (wave-uniform) selects the per-element mask; one inlined copy of the step
-// keeps the register allocation of the kernel tractable.
+// Direct global->LDS load of 16 bytes per lane (lane l's bytes land at LDS byte offset
+// lds_off + 16 l), issued as inline assembly: the compiler does not track it, so LDS
+// reads of other buffers never wait for it; the kernel waits for its fills itself
+// (s_waitcnt vmcnt before the barrier that publishes a tile).
+// (m0 is reserved for the compiler, which warns about the clobber; no code of this
+// kernel keeps a value in m0 across these statements.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void fill16_untracked(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+
+// Same with 4 bytes per lane (lane l's dword lands at lds_off + 4 l).
+__device__ __forceinline__ void fill4_untracked(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// Issues this wave's kBigPer direct global->LDS fill instructions of the Q / dO
+// images of query tile `it` into buffer `buf`.  Rows past the end are clamped to the
+// last row (their positions mark them invisible, see row_value).
+template <int D, bool DOC>
+__device__ __forceinline__ void fill_qtile(DkdvSmem<D>& sm, RowSmem& rsm, int buf, const BwdArgs& a,
+                                           const QFillPlan<D>& fp, QItem it, int kvh, int wave, int lane) {
+  using Sm = DkdvSmem<D>;
+  const int head = kvh * a.group + it.hh;
+  const int r0 = it.qt * kBQ;
+  const uint32_t last = (uint32_t)(min(kBQ, a.q_len - r0) - 1);
+  const uint32_t rs = (uint32_t)a.hq * D;
+  const int64_t base = ((int64_t)r0 * a.hq + head) * D;
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + base;
+  const bf16* ob = reinterpret_cast<const bf16*>(a.dout) + base;
+#pragma unroll
+  for (int j = 0; j < Sm::kBigPer; ++j) {
+    const int jj = wave + 4 * j;
+    const bool isq = jj < Sm::kTileInst;
+    const uint32_t row = min(fp.slot[j] >> 16, last);
+    const bf16* src = (isq ? qb : ob) + (row * rs + (fp.slot[j] & 0xffffu));
+    const uint32_t dst = lds_offset(isq ? sm.qs[buf] : sm.dos[buf]) + (isq ? jj : jj - Sm::kTileInst) * kWave * 16;
+    fill16_untracked(src, dst);
+  }
+  // per-row values: wave 1 positions (lanes 0..31) and document ids (32..63), the
+  // others log-sum-exp (0..31) and delta (32..63) (identical data)
+  const int q = r0 + (int)min((uint32_t)(lane & 31), last);
+  const auto* qpos = uniform_ptr(a.qpos);
+  const auto* qdoc = DOC ? uniform_ptr(a.qdoc) : qpos;
+  const auto* lse = uniform_ptr(a.lse);
+  const auto* del = uniform_ptr(a.delta);
+  const void* src = wave == 1 ? static_cast<const void*>((lane < 32 ? qpos : qdoc) + q)
+                              : static_cast<const void*>((lane < 32 ? lse : del) + (int64_t)q * a.hq + head);
+  fill4_untracked(src, wave == 1 ? lds_offset(rsm.pd[buf]) : lds_offset(rsm.ld[buf]));
+}
+
+// Wave 1 marks the rows of tile `it` past the end invisible (position INT_MIN) once
+// its position fill has landed.
+__device__ __forceinline__ void seal_qtile(RowSmem& rsm, int buf, const BwdArgs& a, QItem it, int wave, int lane) {
+  if (wave != 1) return;
+  const int nvalid = a.q_len - it.qt * kBQ;
+  if (nvalid < kBQ && lane < kBQ && lane >= nvalid) rsm.pd[buf][0][lane] = INT32_MIN;
+}
+
+// Waits for this wave's outstanding fills except the last `keep` tile's (every tile
+// fill is kFillPer instructions per wave).
 template <int D>
-__device__ __forceinline__ void dkdv_step(BwdSmem<D>& sm, int buf, const bf16x8 (&kf)[D / 16],
-                                          const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
-                                          f32x16 (&dv)[D / 32], int kpos, int kdoc, bool key_ok,
-                                          bool masked, int mask, float scale, float scale_log2, int lane) {
-  constexpr int kRS = BwdSmem<D>::kRS;
-  const int r = lane & 31, h = lane >> 5;
-  f32x16 s = {}, dp = {};
-  const bf16* qrow = sm.qs[buf] + r * kRS + h * 8;
-  const bf16* orow = sm.dos[buf] + r * kRS + h * 8;
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
-    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(orow + ds * 16);
-    s = mfma32x32x16(aq, kf[ds], s);
-    dp = mfma32x32x16(ao, vf[ds], dp);
-  }
-  bf16x8 pf[2], dsf[2];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int q0 = 8 * g + 4 * h;
-    const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][q0]);
-    const f32x4 dl = *reinterpret_cast<const f32x4*>(&sm.delta[buf][q0]);
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[4 * g + e], scale_log2, -l2[e]));
-    if (masked) {
-      const int4 qp = *reinterpret_cast<const int4*>(&sm.qpos[buf][q0]);
-      const int4 qd = *reinterpret_cast<const int4*>(&sm.qdoc[buf][q0]);
-      const int qpa[4] = {qp.x, qp.y, qp.z, qp.w};
-      const int qda[4] = {qd.x, qd.y, qd.z, qd.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bool vis = key_ok;
-        if (mask != kMaskNone) vis = vis && kpos <= qpa[e];
-        if (mask == kMaskCausalDoc) vis = vis && kdoc == qda[e];
-        p[e] = vis ? p[e] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int a = 4 * g + e;
-      pf[a >> 3][a & 7] = (bf16)p[e];
-      dsf[a >> 3][a & 7] = (bf16)(p[e] * (dp[a] - dl[e]) * scale);
-    }
-  }
-  const bf16* qtr = sm.qs[buf] + tr_lane_offset<4>(lane, kRS);
-  const bf16* otr = sm.dos[buf] + tr_lane_offset<4>(lane, kRS);
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int off = sl * 16 * kRS + db * 32;
-      const bf16x8 ao = concat(lds_read_tr4(otr + off), lds_read_tr4(otr + off + 8 * kRS));
-      const bf16x8 aq = concat(lds_read_tr4(qtr + off), lds_read_tr4(qtr + off + 8 * kRS));
-      dv[db] = mfma32x32x16(ao, pf[sl], dv[db]);
-      dk[db] = mfma32x32x16(aq, dsf[sl], dk[db]);
-    }
+__device__ __forceinline__ void wait_fills(bool keep_one_tile) {
+  static_assert(DkdvSmem<D>::kFillPer == 6 || DkdvSmem<D>::kFillPer == 4, "immediates below");
+  if (keep_one_tile) {
+    if (DkdvSmem<D>::kFillPer == 6)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
+// S = Q K^T and dP = dO V^T for this wave's 32 keys: Q / dO rows from LDS as A
+// operands, K / V in registers as B operands.  Accumulator layout: lane l holds key
+// (l % 32) and queries 8(a/4) + 4(l/32) + a%4.
 template <int D>
+__device__ __forceinline__ void dkdv_sdp(const DkdvSmem<D>& sm, int buf, const bf16x8 (&kf)[D / 16],
+                                         const bf16x8 (&vf)[D / 16], f32x16& s, f32x16& dp, int lane) {
+  constexpr int kRS = DkdvSmem<D>::kRS;
+  const int r = lane & 31, h = lane >> 5;
+  const bf16* qrow = sm.qs[buf] + r * kRS + h * 8;
+  const bf16* orow = sm.dos[buf] + r * kRS + h * 8;
+  // all operands first: the reads overlap each other and the first contractions
+  bf16x8 aq[D / 16], ao[D / 16];
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    aq[ds] = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
+    ao[ds] = *reinterpret_cast<const bf16x8*>(orow + ds * 16);
+  }
+  s = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+    s = mfma32x32x16(aq[ds], kf[ds], s);
+    dp = mfma32x32x16(ao[ds], vf[ds], dp);
+  }
+}
+
+// P and dS/scale for accumulator group g (queries 8g + 4h .. +3): P rebuilt from the
+// row's log-sum-exp, then the visibility test (key position <= query position, same
+// document); kpos_eff is the key's position for masked tiles and INT_MIN + 1 for
+// fully visible ones, INT_MAX for keys past the segment's end.
+// Per-row values of the tile for this lane's 16 queries (4 groups of 4).
+template <bool DOC>
+struct RowVals {
+  f32x4 l[4], dl[4];
+  int4 qp[4], qd[DOC ? 4 : 1];
+};
+
+template <bool DOC>
+__device__ __forceinline__ void load_rows(const RowSmem& sm, int buf, int h, RowVals<DOC>& rv) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int q0 = 8 * g + 4 * h;
+    rv.l[g] = *reinterpret_cast<const f32x4*>(&sm.ld[buf][0][q0]);
+    rv.dl[g] = *reinterpret_cast<const f32x4*>(&sm.ld[buf][1][q0]);
+    rv.qp[g] = *reinterpret_cast<const int4*>(&sm.pd[buf][0][q0]);
+    if (DOC) rv.qd[DOC ? g : 0] = *reinterpret_cast<const int4*>(&sm.pd[buf][1][q0]);
+  }
+}
+
+template <int D, bool DOC>
+__device__ __forceinline__ void dkdv_pds(const RowVals<DOC>& rv, const f32x16& s, const f32x16& dp, int g,
+                                         int kpos_eff, int kdoc, float scale_log2, bf16x8 (&pf)[2],
+                                         bf16x8 (&dsf)[2]) {
+  const f32x4 l = rv.l[g];
+  const f32x4 dl = rv.dl[g];
+  const int4 qp = rv.qp[g];
+  int4 qd = {0, 0, 0, 0};
+  if (DOC) qd = rv.qd[DOC ? g : 0];
+  const int qpa[4] = {qp.x, qp.y, qp.z, qp.w};
+  const int qda[4] = {qd.x, qd.y, qd.z, qd.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * g + e;
+    float p = fast_exp2(fmaf(s[i], scale_log2, -l[e] * kLog2e));
+    bool vis = kpos_eff <= qpa[e];
+    if (DOC) vis = vis && kdoc == qda[e];
+    p = vis ? p : 0.0f;
+    pf[i >> 3][i & 7] = (bf16)p;
+    dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - dl[e]));
+  }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS for the 32-dim block db and 16-query slice sl
+// (pair j = 2 db + sl); the transposed operands come from transposing LDS reads in
+// the accumulators' contraction order.
+struct TrOps {
+  bf16x8 ao, aq;
+};
+
+template <int D>
+__device__ __forceinline__ TrOps dkdv_ops(const DkdvSmem<D>& sm, int buf, int j, int lane) {
+  constexpr int kRS = DkdvSmem<D>::kRS;
+  const int db = j >> 1, sl = j & 1;
+  const int off = tr_lane_offset<4>(lane, kRS) + sl * 16 * kRS + db * 32;
+  const bf16* qtr = sm.qs[buf] + off;
+  const bf16* otr = sm.dos[buf] + off;
+  return {concat(lds_read_tr4(otr), lds_read_tr4(otr + 8 * kRS)), concat(lds_read_tr4(qtr), lds_read_tr4(qtr + 8 * kRS))};
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_mma(const TrOps& op, int j, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2],
+                                         f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+  const int db = j >> 1, sl = j & 1;
+  dv[db] = mfma32x32x16(op.ao, pf[sl], dv[db]);
+  dk[db] = mfma32x32x16(op.aq, dsf[sl], dk[db]);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_acc_all(const DkdvSmem<D>& sm, int buf, const bf16x8 (&pf)[2],
+                                             const bf16x8 (&dsf)[2], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                             int lane) {
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) dkdv_mma<D>(dkdv_ops<D>(sm, buf, j, lane), j, pf, dsf, dk, dv);
+}
+
+// Instruction order of one step, in two scheduling phases (group masks: 0x008
+// matrix, 0x100 LDS read, 0x002 vector ALU, 0x400 transcendental).
+// Phase 1: the tile's per-row values and the S / dP operands are read six ahead of
+// the S / dP contractions.  Phase 2: each dV/dK contraction of the previous tile
+// carries two transposing reads (operands two pairs ahead) and, from the third on, a
+// share of the P / dS arithmetic (whose inputs are the last S / dP results).
+template <int D, bool DOC>
+__device__ __forceinline__ void dkdv_schedule_sdp() {
+  constexpr int kSdp = D / 8;            // S and dP contractions (= their row reads)
+  constexpr int kSmall = DOC ? 16 : 12;  // per-row value reads
+  constexpr int kLead = 6;
+  __builtin_amdgcn_sched_group_barrier(0x100, kSmall + kLead, 0);
+#pragma unroll
+  for (int k = 0; k < kSdp - kLead; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_schedule_acc() {
+  constexpr int kAcc = D / 8;  // dV/dK contractions
+#pragma unroll
+  for (int k = 0; k < kAcc; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (k >= 2) __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+  }
+}
+
+template <int D, bool DOC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ BwdSmem<D> sm;
+  using Sm = DkdvSmem<D>;
+  constexpr int kJ = D / 16;  // (dim block, query slice) pairs of the dV/dK contractions
+  __shared__ Sm sm;
+  __shared__ RowSmem rs;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
   if (logical >= a.total_wgs) return;
   int s = 0;
@@ -446,9 +599,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
   const int mask = a.mask;
+  const bool docmask = DOC;
   const bf16* kb = reinterpret_cast<const bf16*>(sg.k);
   const bf16* vb = reinterpret_cast<const bf16*>(sg.v);
-  const bf16* stage_base = wave >= 2 ? reinterpret_cast<const bf16*>(a.dout) : reinterpret_cast<const bf16*>(a.q);
 
   // this wave's keys as B operands (lane: key 32*wave + r, dims 16*ds + 8*h .. +7)
   const int mykey = k0 + wave * 32 + r;
@@ -463,13 +616,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       vf[ds] = *reinterpret_cast<const bf16x8*>(vb + base + ds * 16);
     }
   }
-  const int kpos = key_ok ? sg.pos[mykey] : kPosPad;
-  const int kdoc = (key_ok && mask == kMaskCausalDoc) ? sg.doc[mykey] : 0;
+  // effective key position of masked tiles (keys past the end are never visible)
+  const int kpos_mask = key_ok ? (mask == kMaskNone ? INT32_MIN + 1 : sg.pos[mykey]) : INT32_MAX;
+  const int kdoc = (key_ok && docmask) ? sg.doc[mykey] : 0;
 
   // key ranges of the work-group and of this wave (non-decreasing positions)
   const int kmin = sg.pos[k0], kmax = sg.pos[k1 - 1];
   int kdmin = 0, kdmax = 0;
-  if (mask == kMaskCausalDoc) {
+  if (docmask) {
     kdmin = sg.doc[k0];
     kdmax = sg.doc[k1 - 1];
   }
@@ -479,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   if (wave_keys) {
     wkmin = sg.pos[wk0];
     wkmax = sg.pos[wk1 - 1];
-    if (mask == kMaskCausalDoc) {
+    if (docmask) {
       wkdmin = sg.doc[wk0];
       wkdmax = sg.doc[wk1 - 1];
     }
@@ -489,11 +643,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_qt = (a.q_len + kBQ - 1) / kBQ;
   for (int t = tid; t < n_qt; t += kThreads) {
     const int q0 = t * kBQ, q1 = min(a.q_len, q0 + kBQ) - 1;
-    sm.qtab[0][t] = a.qpos[q0];
-    sm.qtab[1][t] = a.qpos[q1];
-    sm.qtab[2][t] = mask == kMaskCausalDoc ? a.qdoc[q0] : 0;
-    sm.qtab[3][t] = mask == kMaskCausalDoc ? a.qdoc[q1] : 0;
+    rs.qtab[0][t] = a.qpos[q0];
+    rs.qtab[1][t] = a.qpos[q1];
+    rs.qtab[2][t] = docmask ? a.qdoc[q0] : 0;
+    rs.qtab[3][t] = docmask ? a.qdoc[q1] : 0;
   }
+  QFillPlan<D> fp;
+  fp.init(wave, lane);
   lds_barrier();
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -503,38 +659,84 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  QRef cur = next_qtile(sm, a, 0, 0, n_qt, kmin, kmax, kdmin, kdmax);
+  QItem cur = next_qitem(rs, a, QItem{0, -1}, n_qt, kmin, kmax, kdmin, kdmax);
   if (cur.hh >= 0) {
-    QStageRegs<D> qr;
-    load_qstage<D>(qr, a, stage_base, kvh * a.group + cur.hh, cur.qt * kBQ, tid);
-    store_qstage<D>(sm, 0, qr, tid);
+    // prologue: tiles 0 and 1 in flight, then landed
+    QItem n1 = next_qitem(rs, a, cur, n_qt, kmin, kmax, kdmin, kdmax);
+    fill_qtile<D, DOC>(sm, rs, 0, a, fp, cur, kvh, wave, lane);
+    if (n1.hh >= 0) fill_qtile<D, DOC>(sm, rs, 1, a, fp, n1, kvh, wave, lane);
+    QItem nf = n1.hh >= 0 ? next_qitem(rs, a, n1, n_qt, kmin, kmax, kdmin, kdmax) : QItem{-1, 0};
+    // every load so far (fills and this wave's key values) has landed: the builtin
+    // form lets the compiler know, so it adds no waits of its own inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    seal_qtile(rs, 0, a, cur, wave, lane);
+    if (n1.hh >= 0) seal_qtile(rs, 1, a, n1, wave, lane);
     lds_barrier();
-    int buf = 0;
+
+    // One straight-line step per tile for every wave: a wave whose keys see nothing of
+    // the tile runs it masked (P = 0), and the first step's "previous tile" dV/dK
+    // contractions run on zeros.
+    int buf = 0, pbuf = 0;
+    bf16x8 ppf[2] = {}, pdsf[2] = {};
     while (true) {
-      const QRef nxt = next_qtile(sm, a, cur.hh, cur.qt + 1, n_qt, kmin, kmax, kdmin, kdmax);
-      if (nxt.hh >= 0) load_qstage<D>(qr, a, stage_base, kvh * a.group + nxt.hh, nxt.qt * kBQ, tid);
-      const int r0 = cur.qt * kBQ, r1 = min(a.q_len, r0 + kBQ);
-      if (wave_keys) {
-        const QRange q = qrange(sm, cur.qt);
-        int wcls = classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, wkmin, wkmax, wkdmin, wkdmax);
-        if (wcls == kTileFull && (wk1 - wk0 < 32 || r1 - r0 < kBQ)) wcls = kTilePartial;
-        if (wcls != kTileEmpty)
-          dkdv_step<D>(sm, buf, kf, vf, dk, dv, kpos, kdoc, key_ok, wcls == kTilePartial, mask, a.scale,
-                       a.scale_log2, lane);
+      // fill of tile i+2 (its buffers held tile i-2, released at the last barrier)
+      const bool issued = nf.hh >= 0;
+      if (issued) fill_qtile<D, DOC>(sm, rs, (buf + 2) & 3, a, fp, nf, kvh, wave, lane);
+      int kpos_eff = kpos_mask;
+      {
+        const QRange q = qrange(rs, cur.qt);
+        const int cls = classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, wkmin, wkmax, wkdmin, wkdmax);
+        // fully visible tiles skip the position test (ragged tiles never count as full)
+        if (wave_keys && cls == kTileFull && wk1 - wk0 == 32 && a.q_len - cur.qt * kBQ >= kBQ)
+          kpos_eff = INT32_MIN + 1;
       }
-      if (nxt.hh < 0) break;
-      // the other buffer was released by every wave at the previous barrier
-      store_qstage<D>(sm, buf ^ 1, qr, tid);
+      f32x16 sv, dpv;
+      __builtin_amdgcn_sched_barrier(0);
+      RowVals<DOC> rv;
+      load_rows<DOC>(rs, buf, h, rv);
+      dkdv_sdp<D>(sm, buf, kf, vf, sv, dpv, lane);
+      dkdv_schedule_sdp<D, DOC>();
+      // first operands of the previous tile's dV/dK contractions
+      TrOps ops[2] = {dkdv_ops<D>(sm, pbuf, 0, lane), dkdv_ops<D>(sm, pbuf, 1, lane)};
+      __builtin_amdgcn_sched_barrier(0);
+      // the P / dS arithmetic belongs to the second phase: tie its inputs to this point
+      asm volatile("" : "+v"(sv), "+v"(dpv));
+      bf16x8 pf[2], dsf[2];
+      // dV/dK of the previous tile, with this tile's P / dS arithmetic in between
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        dkdv_mma<D>(ops[j & 1], j, ppf, pdsf, dk, dv);
+        if (j + 2 < kJ) ops[j & 1] = dkdv_ops<D>(sm, pbuf, j + 2, lane);
+        if ((j + 1) * 4 % kJ == 0)
+          dkdv_pds<D, DOC>(rv, sv, dpv, (j + 1) * 4 / kJ - 1, kpos_eff, kdoc, a.scale_log2, pf, dsf);
+      }
+      dkdv_schedule_acc<D>();
+      __builtin_amdgcn_sched_barrier(0);
+      // keep the P / dS arithmetic in this step (it is consumed by the next one)
+      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
+      pbuf = buf;
+      ppf[0] = pf[0];
+      ppf[1] = pf[1];
+      pdsf[0] = dsf[0];
+      pdsf[1] = dsf[1];
+      if (n1.hh < 0) break;
+      // tile i+1 landed (tile i+2's fill may still be in flight)
+      wait_fills<D>(issued);
+      seal_qtile(rs, (buf + 1) & 3, a, n1, wave, lane);
       lds_barrier();
-      buf ^= 1;
-      cur = nxt;
+      cur = n1;
+      n1 = nf;
+      if (nf.hh >= 0) nf = next_qitem(rs, a, nf, n_qt, kmin, kmax, kdmin, kdmax);
+      buf = (buf + 1) & 3;
     }
+    dkdv_acc_all<D>(sm, pbuf, ppf, pdsf, dk, dv, lane);
   }
 
   // per-owner sums: this wave's 32 keys, all local queries and all heads of the group
   if (key_ok) {
     float* dkp = a.dk[s];
     float* dvp = a.dv[s];
+    const float sc = a.scale;
     const int64_t rowoff = ((int64_t)mykey * a.hkv + kvh) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -542,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = db * 32 + 8 * g + 4 * h;
         *reinterpret_cast<f32x4*>(dkp + rowoff + d0) =
-            f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+            f32x4{dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc};
         *reinterpret_cast<f32x4*>(dvp + rowoff + d0) =
             f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
       }
@@ -602,10 +804,16 @@ hipError_t launch_bwd_dkdv(const BwdArgs& args, int d, hipStream_t stream) {
   a.total_wgs = total;
   a.padded_wgs = (total + 7) & ~7;
   if (total == 0) return hipSuccess;
-  if (d == 64)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+  const bool doc = a.mask == kMaskCausalDoc;
+  const dim3 grid(a.padded_wgs), block(kThreads);
+  if (d == 64 && doc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), grid, block, 0, stream, a);
+  else if (d == 64)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), grid, block, 0, stream, a);
+  else if (doc)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
