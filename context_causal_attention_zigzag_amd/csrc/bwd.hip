@@ -266,12 +266,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
 // ---------------------------------------------------------------------------
 // dK/dV pass
 //
-// Software pipeline over the query tiles a work-group visits (per wave, tile i):
-//   S_i, dP_i contractions  ->  dV/dK contractions of tile i-1, interleaved with the
-//   P_i / dS_i arithmetic (independent of them)  ->  next iteration.
-// Tiles i-1 and i are read while tiles i+1 and i+2 land in LDS (direct global->LDS
-// fills issued two iterations ahead), so four tile buffers rotate.
-constexpr int kQBufs = 4;
+// Software pipeline over the query tiles a work-group visits; iteration i of a wave
+// runs three independent pieces of work side by side:
+//   the S / dP contractions of tile i+1,
+//   the dV / dK contractions of tile i-1 (with its P / dS from iteration i-1),
+//   the P / dS arithmetic of tile i (from its S / dP of iteration i-1),
+// so the matrix cores and the vector ALU never wait on each other inside an iteration.
+// Tiles i-1 .. i+1 are read while tiles i+2 (landed) and i+3 (filling, two iterations
+// ahead) occupy the other LDS buffers: five tile buffers rotate.
+constexpr int kQBufs = 5;
 
 template <int D>
 struct DkdvSmem {
@@ -342,17 +345,13 @@ __device__ __forceinline__ QRange qrange(const RowSmem& sm, int t) {
   return {sm.qtab[0][t], sm.qtab[1][t], sm.qtab[2][t], sm.qtab[3][t]};
 }
 
-// Next visible (head, query tile) after `it` for the key range [kmin, kmax].
-__device__ __forceinline__ QItem next_qitem(const RowSmem& sm, const BwdArgs& a, QItem it, int n_qt, int kmin,
-                                            int kmax, int kdmin, int kdmax) {
-  int hh = it.hh, qt = it.qt + 1;
-  for (; hh < a.group; ++hh, qt = 0) {
-    for (; qt < n_qt; ++qt) {
-      const QRange q = qrange(sm, qt);
-      if (classify(a.mask, q.pmin, q.pmax, q.dmin, q.dmax, kmin, kmax, kdmin, kdmax) != kTileEmpty)
-        return {hh, qt};
-    }
-  }
+// The work-group's items are (head within the group, query tile) for every head and
+// the query tiles [lo, hi) that the key range can see: positions (and documents) are
+// non-decreasing along the query block, so those tiles are contiguous (a tile inside
+// the range that nonetheless sees nothing is processed masked, with the same result).
+__device__ __forceinline__ QItem next_qitem(QItem it, int group, int lo, int hi) {
+  if (it.qt + 1 < hi) return {it.hh, it.qt + 1};
+  if (it.hh + 1 < group) return {it.hh + 1, lo};
   return {-1, 0};
 }
 
@@ -360,6 +359,10 @@ __device__ __forceinline__ QItem next_qitem(const RowSmem& sm, const BwdArgs& a,
 // lds_off + 16 l), issued as inline assembly: the compiler does not track it, so LDS
 // reads of other buffers never wait for it; the kernel waits for its fills itself
 // (s_waitcnt vmcnt before the barrier that publishes a tile).
+// (m0 is reserved for the compiler, which warns about the clobber; no code of this
+// kernel keeps a value in m0 across these statements.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 // (m0 is reserved for the compiler, which warns about the clobber; no code of this
 // kernel keeps a value in m0 across these statements.)
 #pragma clang diagnostic push
@@ -469,6 +472,19 @@ __device__ __forceinline__ void dkdv_sdp(const DkdvSmem<D>& sm, int buf, const b
   }
 }
 
+// Row operands of the S / dP contraction step ds: the A operands (Q and dO rows of this
+// lane's row r = lane % 32, dims 16 ds + 8 h .. +7).
+struct RowOps {
+  bf16x8 aq, ao;
+};
+
+template <int D>
+__device__ __forceinline__ RowOps dkdv_rowops(const DkdvSmem<D>& sm, int buf, int ds, int lane) {
+  constexpr int kRS = DkdvSmem<D>::kRS;
+  const int off = (lane & 31) * kRS + (lane >> 5) * 8 + ds * 16;
+  return {*reinterpret_cast<const bf16x8*>(sm.qs[buf] + off), *reinterpret_cast<const bf16x8*>(sm.dos[buf] + off)};
+}
+
 // P and dS/scale for accumulator group g (queries 8g + 4h .. +3): P rebuilt from the
 // row's log-sum-exp, then the visibility test (key position <= query position, same
 // document); kpos_eff is the key's position for masked tiles and INT_MIN + 1 for
@@ -548,34 +564,24 @@ __device__ __forceinline__ void dkdv_acc_all(const DkdvSmem<D>& sm, int buf, con
   for (int j = 0; j < D / 16; ++j) dkdv_mma<D>(dkdv_ops<D>(sm, buf, j, lane), j, pf, dsf, dk, dv);
 }
 
-// Instruction order of one step, in two scheduling phases (group masks: 0x008
-// matrix, 0x100 LDS read, 0x002 vector ALU, 0x400 transcendental).
-// Phase 1: the tile's per-row values and the S / dP operands are read six ahead of
-// the S / dP contractions.  Phase 2: each dV/dK contraction of the previous tile
-// carries two transposing reads (operands two pairs ahead) and, from the third on, a
-// share of the P / dS arithmetic (whose inputs are the last S / dP results).
+// Instruction order of one iteration (scheduling-group masks: 0x008 matrix, 0x100 LDS
+// read, 0x002 vector ALU, 0x400 transcendental): the per-row values and the first
+// operands are read up front; then every contraction carries one or two operand reads
+// (two pairs ahead) and a share of the P / dS arithmetic, which none of them depends
+// on.
 template <int D, bool DOC>
-__device__ __forceinline__ void dkdv_schedule_sdp() {
-  constexpr int kSdp = D / 8;            // S and dP contractions (= their row reads)
-  constexpr int kSmall = DOC ? 16 : 12;  // per-row value reads
+__device__ __forceinline__ void dkdv_schedule() {
+  constexpr int kMfma = D / 4;                // S, dP, dV, dK contractions
+  constexpr int kReads = D / 8 + 4 * (D / 16);  // row and transposing operand reads
+  constexpr int kSmall = DOC ? 16 : 12;       // per-row value reads
   constexpr int kLead = 6;
+  constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
   __builtin_amdgcn_sched_group_barrier(0x100, kSmall + kLead, 0);
 #pragma unroll
-  for (int k = 0; k < kSdp - kLead; ++k) {
+  for (int k = 0; k < kMfma; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_schedule_acc() {
-  constexpr int kAcc = D / 8;  // dV/dK contractions
-#pragma unroll
-  for (int k = 0; k < kAcc; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    if (k >= 2) __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
   }
 }
 
@@ -648,9 +654,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     rs.qtab[2][t] = docmask ? a.qdoc[q0] : 0;
     rs.qtab[3][t] = docmask ? a.qdoc[q1] : 0;
   }
+  __shared__ int vis_lo, vis_hi;
+  if (tid == 0) {
+    vis_lo = INT32_MAX;
+    vis_hi = -1;
+  }
   QFillPlan<D> fp;
   fp.init(wave, lane);
   lds_barrier();
+  // range of query tiles the work-group's keys can see
+  {
+    int lo = INT32_MAX, hi = -1;
+    for (int t = tid; t < n_qt; t += kThreads) {
+      const QRange q = qrange(rs, t);
+      if (classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, kmin, kmax, kdmin, kdmax) != kTileEmpty) {
+        lo = min(lo, t);
+        hi = max(hi, t);
+      }
+    }
+    if (hi >= 0) {
+      atomicMin(&vis_lo, lo);
+      atomicMax(&vis_hi, hi);
+    }
+  }
+  lds_barrier();
+  const int qlo = vis_lo, qhi = vis_hi + 1;
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -659,29 +687,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  QItem cur = next_qitem(rs, a, QItem{0, -1}, n_qt, kmin, kmax, kdmin, kdmax);
+  QItem cur = qhi > qlo ? QItem{0, qlo} : QItem{-1, 0};
   if (cur.hh >= 0) {
-    // prologue: tiles 0 and 1 in flight, then landed
-    QItem n1 = next_qitem(rs, a, cur, n_qt, kmin, kmax, kdmin, kdmax);
+    // prologue: tiles 0, 1, 2 filled and landed, S / dP of tile 0
+    QItem n1 = next_qitem(cur, a.group, qlo, qhi);
+    QItem n2 = n1.hh >= 0 ? next_qitem(n1, a.group, qlo, qhi) : QItem{-1, 0};
     fill_qtile<D, DOC>(sm, rs, 0, a, fp, cur, kvh, wave, lane);
     if (n1.hh >= 0) fill_qtile<D, DOC>(sm, rs, 1, a, fp, n1, kvh, wave, lane);
-    QItem nf = n1.hh >= 0 ? next_qitem(rs, a, n1, n_qt, kmin, kmax, kdmin, kdmax) : QItem{-1, 0};
+    if (n2.hh >= 0) fill_qtile<D, DOC>(sm, rs, 2, a, fp, n2, kvh, wave, lane);
+    QItem nf = n2.hh >= 0 ? next_qitem(n2, a.group, qlo, qhi) : QItem{-1, 0};
     // every load so far (fills and this wave's key values) has landed: the builtin
     // form lets the compiler know, so it adds no waits of its own inside the loop
     __builtin_amdgcn_s_waitcnt(0x0F70);
     seal_qtile(rs, 0, a, cur, wave, lane);
     if (n1.hh >= 0) seal_qtile(rs, 1, a, n1, wave, lane);
+    if (n2.hh >= 0) seal_qtile(rs, 2, a, n2, wave, lane);
     lds_barrier();
+    f32x16 sv, dpv;
+    dkdv_sdp<D>(sm, 0, kf, vf, sv, dpv, lane);
 
-    // One straight-line step per tile for every wave: a wave whose keys see nothing of
-    // the tile runs it masked (P = 0), and the first step's "previous tile" dV/dK
-    // contractions run on zeros.
-    int buf = 0, pbuf = 0;
+    // Iteration i (tile i in buffer b0, i-1 in bp, i+1 in b1, i+2 in b2): one
+    // straight-line body for every wave.  A wave whose keys see nothing of a tile runs
+    // it masked (P = 0); the first iteration's "previous tile" dV/dK contractions run
+    // on zeros over tile 0's (valid) image, and the last one's "next tile" S / dP on a
+    // buffer whose results are not used.
+    int b0 = 0, bp = 0;
     bf16x8 ppf[2] = {}, pdsf[2] = {};
     while (true) {
-      // fill of tile i+2 (its buffers held tile i-2, released at the last barrier)
+      const int b1 = b0 == kQBufs - 1 ? 0 : b0 + 1;
+      const int b2 = b1 == kQBufs - 1 ? 0 : b1 + 1;
+      const int b3 = b2 == kQBufs - 1 ? 0 : b2 + 1;
+      // fill of tile i+3 (its buffers held tile i-2, released at the last barrier)
       const bool issued = nf.hh >= 0;
-      if (issued) fill_qtile<D, DOC>(sm, rs, (buf + 2) & 3, a, fp, nf, kvh, wave, lane);
+      if (issued) fill_qtile<D, DOC>(sm, rs, b3, a, fp, nf, kvh, wave, lane);
       int kpos_eff = kpos_mask;
       {
         const QRange q = qrange(rs, cur.qt);
@@ -690,46 +728,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if (wave_keys && cls == kTileFull && wk1 - wk0 == 32 && a.q_len - cur.qt * kBQ >= kBQ)
           kpos_eff = INT32_MIN + 1;
       }
-      f32x16 sv, dpv;
       __builtin_amdgcn_sched_barrier(0);
       RowVals<DOC> rv;
-      load_rows<DOC>(rs, buf, h, rv);
-      dkdv_sdp<D>(sm, buf, kf, vf, sv, dpv, lane);
-      dkdv_schedule_sdp<D, DOC>();
-      // first operands of the previous tile's dV/dK contractions
-      TrOps ops[2] = {dkdv_ops<D>(sm, pbuf, 0, lane), dkdv_ops<D>(sm, pbuf, 1, lane)};
-      __builtin_amdgcn_sched_barrier(0);
-      // the P / dS arithmetic belongs to the second phase: tie its inputs to this point
-      asm volatile("" : "+v"(sv), "+v"(dpv));
+      load_rows<DOC>(rs, b0, h, rv);
+      // S / dP of tile i, computed last iteration
+      f32x16 scur = sv, dpcur = dpv;
+      asm volatile("" : "+v"(scur), "+v"(dpcur));
       bf16x8 pf[2], dsf[2];
-      // dV/dK of the previous tile, with this tile's P / dS arithmetic in between
+      RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
+      TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
+      sv = f32x16{};
+      dpv = f32x16{};
+      // stage k: the contractions of pair k and the operand reads of pair k + 2 (stage
+      // boundaries keep each read two stages ahead of its use)
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        dkdv_mma<D>(ops[j & 1], j, ppf, pdsf, dk, dv);
-        if (j + 2 < kJ) ops[j & 1] = dkdv_ops<D>(sm, pbuf, j + 2, lane);
-        if ((j + 1) * 4 % kJ == 0)
-          dkdv_pds<D, DOC>(rv, sv, dpv, (j + 1) * 4 / kJ - 1, kpos_eff, kdoc, a.scale_log2, pf, dsf);
+      for (int k = 0; k < D / 16; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        // S / dP of tile i+1, contraction step k
+        sv = mfma32x32x16(ro[k & 1].aq, kf[k], sv);
+        dpv = mfma32x32x16(ro[k & 1].ao, vf[k], dpv);
+        // dV / dK of tile i-1, pair k
+        dkdv_mma<D>(to[k & 1], k, ppf, pdsf, dk, dv);
+        if (k + 2 < D / 16) {
+          ro[k & 1] = dkdv_rowops<D>(sm, b1, k + 2, lane);
+          to[k & 1] = dkdv_ops<D>(sm, bp, k + 2, lane);
+        }
+        // P / dS of tile i, a quarter per (D / 64) stages
+        if ((k + 1) * 4 % (D / 16) == 0)
+          dkdv_pds<D, DOC>(rv, scur, dpcur, (k + 1) * 4 / (D / 16) - 1, kpos_eff, kdoc, a.scale_log2, pf, dsf);
       }
-      dkdv_schedule_acc<D>();
       __builtin_amdgcn_sched_barrier(0);
-      // keep the P / dS arithmetic in this step (it is consumed by the next one)
+      // keep the P / dS arithmetic in this iteration (it is consumed by the next one)
       asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
-      pbuf = buf;
+      bp = b0;
       ppf[0] = pf[0];
       ppf[1] = pf[1];
       pdsf[0] = dsf[0];
       pdsf[1] = dsf[1];
       if (n1.hh < 0) break;
-      // tile i+1 landed (tile i+2's fill may still be in flight)
+      // tile i+2 landed (tile i+3's fill may still be in flight)
       wait_fills<D>(issued);
-      seal_qtile(rs, (buf + 1) & 3, a, n1, wave, lane);
+      if (n2.hh >= 0) seal_qtile(rs, b2, a, n2, wave, lane);
       lds_barrier();
       cur = n1;
-      n1 = nf;
-      if (nf.hh >= 0) nf = next_qitem(rs, a, nf, n_qt, kmin, kmax, kdmin, kdmax);
-      buf = (buf + 1) & 3;
+      n1 = n2;
+      n2 = nf;
+      if (nf.hh >= 0) nf = next_qitem(nf, a.group, qlo, qhi);
+      b0 = b1;
     }
-    dkdv_acc_all<D>(sm, pbuf, ppf, pdsf, dk, dv, lane);
+    dkdv_acc_all<D>(sm, bp, ppf, pdsf, dk, dv, lane);
   }
 
   // per-owner sums: this wave's 32 keys, all local queries and all heads of the group
