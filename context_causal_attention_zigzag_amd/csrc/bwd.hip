@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
   float* flag_dst = nsplit > 1 ? job.ws_lse + (int64_t)split * job.len * a.hq : nullptr;
   TileIter it;
   it.mask_mode = nsplit > 1;
+  if (nsplit == 1) iter_init_ranges(it, a, job, lane, qmin, qmax, qdmin, qdmax);
   if (nsplit > 1) {
     iter_init_masks(it, a, job, lane, qmin, qmax, qdmin, qdmax);
     const int total = iter_count(it);
@@ -303,15 +304,6 @@ struct RowSmem {
   int32_t qtab[4][kMaxQTiles];
 };
 
-// A kernel-argument pointer held in scalar registers.
-template <class T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const T*>((uint64_t)hi << 32 | lo);
-}
-
 // Per-lane source slots of the Q / dO fill instructions: fill instruction jj of a tile
 // writes the 64 16-byte slots 64*jj .. 64*jj+63 of the tile image, lane l slot
 // 64*jj + l (row-major, kSlots per row, the last ones padding).
@@ -353,39 +345,6 @@ __device__ __forceinline__ QItem next_qitem(QItem it, int group, int lo, int hi)
   if (it.qt + 1 < hi) return {it.hh, it.qt + 1};
   if (it.hh + 1 < group) return {it.hh + 1, lo};
   return {-1, 0};
-}
-
-// Direct global->LDS load of 16 bytes per lane (lane l's bytes land at LDS byte offset
-// lds_off + 16 l), issued as inline assembly: the compiler does not track it, so LDS
-// reads of other buffers never wait for it; the kernel waits for its fills itself
-// (s_waitcnt vmcnt before the barrier that publishes a tile).
-// (m0 is reserved for the compiler, which warns about the clobber; no code of this
-// kernel keeps a value in m0 across these statements.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// (m0 is reserved for the compiler, which warns about the clobber; no code of this
-// kernel keeps a value in m0 across these statements.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void fill16_untracked(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_off), "v"(g)
-               : "memory", "m0");
-}
-
-// Same with 4 bytes per lane (lane l's dword lands at lds_off + 4 l).
-__device__ __forceinline__ void fill4_untracked(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(lds_off), "v"(g)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 }
 
 // Issues this wave's kBigPer direct global->LDS fill instructions of the Q / dO
@@ -588,7 +547,6 @@ __device__ __forceinline__ void dkdv_schedule() {
 template <int D, bool DOC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using Sm = DkdvSmem<D>;
-  constexpr int kJ = D / 16;  // (dim block, query slice) pairs of the dV/dK contractions
   __shared__ Sm sm;
   __shared__ RowSmem rs;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);

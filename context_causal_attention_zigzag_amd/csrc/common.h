@@ -104,8 +104,71 @@ __device__ __forceinline__ void global_to_lds4(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 4, 0, 0);
 }
 
+// Direct global->LDS loads issued as inline assembly (lane l's 16 bytes land at LDS
+// byte offset lds_off + 16 l; the 4-byte form at lds_off + 4 l).  The compiler does
+// not track them, so its wait insertion never makes an LDS read of another buffer
+// wait for them; a kernel using them waits for its own fills (s_waitcnt vmcnt) before
+// the barrier that publishes the data.  m0 is reserved for the compiler, which warns
+// about the clobber; kernels using these keep no value of their own in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void fill16_untracked(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void fill4_untracked(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte offset of a __shared__ address (wave-uniform).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// A kernel-argument pointer held in scalar registers (a per-lane choice between two
+// arguments is then made on their values, not on their addresses, which would fetch
+// them with a vector load).
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>((uint64_t)hi << 32 | lo);
+}
+
+// Exchange between the two lane halves (v_permlane32_swap, a VALU instruction on
+// gfx950).  lo_hi(x) yields, in every lane l, the values of lane l % 32 (first) and of
+// lane l % 32 + 32 (second): combining the two gives the same result, in the same
+// operation order, in both halves.
+struct LoHi {
+  float lo, hi;
+};
+__device__ __forceinline__ LoHi lo_hi(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0]: lanes 0..31 keep x, lanes 32..63 receive lanes 0..31; r[1]: lanes 0..31
+  // receive lanes 32..63, lanes 32..63 keep x
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float half_max(float x) {
+  const LoHi p = lo_hi(x);
+  return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const LoHi p = lo_hi(x);
+  return p.lo + p.hi;
+}
 // Value held by lane (l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
+__device__ __forceinline__ float swap_halves(float x) {
+  const LoHi p = lo_hi(x);
+  return (threadIdx.x & 32) ? p.lo : p.hi;
+}
 
 // Swap of bits 2 and 3 inside each group of 16 (the contraction order of a C-layout
 // B operand, see the header comment).

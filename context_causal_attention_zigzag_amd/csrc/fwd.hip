@@ -10,7 +10,9 @@
 // fp32 O_ij and L_ij for a later merge) or one query block with its list of segments
 // in ring arrival order (ring-attention page, section 2: final O in the input dtype).
 //
-// bf16 kernel (gfx950 matrix cores), per work-group of 4 waves, 32 query rows per wave:
+// bf16 kernel (gfx950 matrix cores), per work-group of 4 waves, 32 query rows per wave,
+// two work-groups per CU (two waves per SIMD: while one runs its softmax arithmetic
+// or waits on LDS, the other keeps the matrix core busy):
 //  - S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A operand and the
 //    wave's queries, held in registers for the whole loop, the B operand.  Each lane
 //    then owns one query row (column of S^T), so row max / row sum are in-lane plus
@@ -23,8 +25,10 @@
 //  - The running maximum is only moved when a new score exceeds it by more than
 //    2^8 (probabilities stay <= 256, exact in fp32 and bf16 range), so the O rescale
 //    is skipped on almost every tile.
-//  - Tiles are classified per work-group (skip empty tiles entirely) and per wave
-//    (fully visible tiles run without mask arithmetic).
+//  - The tiles a work-group visits, and per wave the tiles it skips and those it sees
+//    whole (no mask arithmetic), are found once per work-group by binary search over
+//    each segment's key positions (kv_stream.h); the loop itself reads no segment
+//    table and no key positions except for partially visible tiles.
 //  - K/V tiles are double-buffered in LDS and filled by direct global->LDS loads
 //    (no register staging): the next visible tile streams in while the current one
 //    computes; one barrier per tile.
@@ -40,9 +44,37 @@ namespace {
 
 using namespace kv;
 
+// K rows at stride D + 8 (row reads), V rows at D + 24 (transposing reads; also
+// conflict-free for row reads): 73 KiB with both double-buffered, two work-groups
+// per CU.
 template <int D>
-using FwdSmem = KvSmem<D, D + 8, D + 32>;  // K: row reads; V: transposing reads
+using FwdSmem = KvSmem<D, D + 8, D + 24>;
 
+// Visibility of this lane's 32 raw scores of a partially visible tile (positions kp /
+// documents kd in LDS, klen keys) for query position qpos / document qdoc: invisible
+// scores become -inf.  Branch-free (the document image is read even when documents
+// are off; its value is then ignored).
+__device__ __forceinline__ void mask_scores(float (&x)[32], const int32_t* kp, const int32_t* kd, int klen,
+                                            int qpos, int qdoc, int mask, int h) {
+  const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
+  const bool docm = mask == kMaskCausalDoc;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int base = kb * 32 + 8 * g + 4 * h;
+      const int4 kpv = *reinterpret_cast<const int4*>(kp + base);
+      const int4 kdv = *reinterpret_cast<const int4*>(kd + base);
+      const int kpa[4] = {kpv.x, kpv.y, kpv.z, kpv.w};
+      const int kda[4] = {kdv.x, kdv.y, kdv.z, kdv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
+        x[kb * 16 + g * 4 + e] = vis ? x[kb * 16 + g * 4 + e] : neg_inf();
+      }
+    }
+  }
+}
 
 // One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
 template <int D, bool MASKED>
@@ -68,31 +100,11 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
     x[i] = s0[i];
     x[16 + i] = s1[i];
   }
-  if (MASKED) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int base = kb * 32 + 8 * g + 4 * h;
-        const int4 kp = *reinterpret_cast<const int4*>(kpos + base);
-        int4 kd = {0, 0, 0, 0};
-        if (mask == kMaskCausalDoc) kd = *reinterpret_cast<const int4*>(kdoc + base);
-        const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
-        const int kda[4] = {kd.x, kd.y, kd.z, kd.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bool vis = base + e < klen;
-          if (mask != kMaskNone) vis = vis && kpa[e] <= qpos;
-          if (mask == kMaskCausalDoc) vis = vis && kda[e] == qdoc;
-          x[kb * 16 + g * 4 + e] = vis ? x[kb * 16 + g * 4 + e] : neg_inf();
-        }
-      }
-    }
-  }
+  if (MASKED) mask_scores(x, kpos, kdoc, klen, qpos, qdoc, mask, h);
   float mt = x[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-  mt = fmaxf(mt, swap_halves(mt)) * scale_log2;  // -inf stays -inf (scale > 0)
+  mt = half_max(mt) * scale_log2;  // -inf stays -inf (scale > 0)
   const float m_new = fmaxf(m, mt);
   const bool need = m_new > m + kTau;
   if (__any(need)) {
@@ -131,14 +143,17 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
 
 template <int D, bool PARTIAL_OUT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
-  __shared__ FwdSmem<D> sm;
+  using Sm = FwdSmem<D>;
+  __shared__ Sm sm;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
   if (logical >= a.total_wgs) return;
   int j = 0;
   while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
   const JobDesc& job = a.jobs[j];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
   const int hpw = a.heads_per_wg;
   const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
   const int n_qt = (job.len + qt_rows - 1) / qt_rows;
@@ -157,11 +172,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int myrow = wr0 + (lane & 31);
   const bool row_ok = myrow < wr1;
   const int mask = a.mask;
+  const bool doc = mask == kMaskCausalDoc;
 
   // work-group and wave query ranges (positions / documents are non-decreasing)
-  const int qmin = job.pos[r0], qmax = job.pos[r1 - 1];
+  const int qmax = job.pos[r1 - 1];
   int qdmin = 0, qdmax = 0, wqdmin = 0, wqdmax = 0;
-  if (mask == kMaskCausalDoc) {
+  if (doc) {
     qdmin = job.doc[r0];
     qdmax = job.doc[r1 - 1];
   }
@@ -169,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (wave_rows) {
     wqmin = job.pos[wr0];
     wqmax = job.pos[wr1 - 1];
-    if (mask == kMaskCausalDoc) {
+    if (doc) {
       wqdmin = job.doc[wr0];
       wqdmax = job.doc[wr1 - 1];
     }
@@ -178,17 +194,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   bf16x8 qf[D / 16];
   int qpos = kPosPad, qdoc = 0;
   {
-    const bf16* qb = reinterpret_cast<const bf16*>(job.q) + ((int64_t)myrow * a.hq + head) * D + (lane >> 5) * 8;
+    const bf16* qb = reinterpret_cast<const bf16*>(job.q) + ((int64_t)myrow * a.hq + head) * D + h * 8;
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      if (row_ok)
-        qf[ds] = *reinterpret_cast<const bf16x8*>(qb + ds * 16);
-      else
-        qf[ds] = bf16x8{};
-    }
+    for (int ds = 0; ds < D / 16; ++ds) qf[ds] = row_ok ? *reinterpret_cast<const bf16x8*>(qb + ds * 16) : bf16x8{};
     if (row_ok) {
       qpos = job.pos[myrow];
-      if (mask == kMaskCausalDoc) qdoc = job.doc[myrow];
+      if (doc) qdoc = job.doc[myrow];
     }
   }
 
@@ -203,57 +214,57 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   TileIter it;
   it.mask_mode = nsplit > 1;
+  iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax);
   if (nsplit > 1) {
-    iter_init_masks(it, a, job, lane, qmin, qmax, qdmin, qdmax);
+    iter_init_masks(it, a, job, lane, job.pos[r0], qmax, qdmin, qdmax);
     const int total = iter_count(it);
     const int first = split * job.tiles_per_split;
     if (first >= total) {  // nothing to do in this split: an empty partial state
-      if (row_ok && (lane >> 5) == 0) lse_dst[(int64_t)myrow * a.hq + head] = neg_inf();
+      if (row_ok && h == 0) lse_dst[(int64_t)myrow * a.hq + head] = neg_inf();
       return;
     }
     iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
   }
 
-  FillPlan<D, FwdSmem<D>> fp;
-  fp.init(wave, lane);
-  TileRef cur = iter_next(it, a, job, TileRef{-1, 0}, qmin, qmax, qdmin, qdmax);
+  const uint32_t rs = (uint32_t)a.hkv * D;  // elements between consecutive keys
+  FillOffs<D, Sm> fo;
+  fo.init(wave, lane, rs);
+  TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
   if (cur.seg >= 0) {
-    fill_tile<D, FwdSmem<D>>(sm, 0, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, wave, lane, fp);
+    KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);
+    fill_tile<D, Sm>(sm, 0, tc, rs, doc, wave, lane, fo);
     fill_barrier();
     int buf = 0;
     while (true) {
-      const TileRef nxt = iter_next(it, a, job, cur, qmin, qmax, qdmin, qdmax);
+      const TileRef nxt = iter_next<true>(it, a, job, cur, 0, 0, 0, 0);
+      KvTile tn = tc;
       // the other buffer was released by every wave at the previous barrier
-      if (nxt.seg >= 0) fill_tile<D, FwdSmem<D>>(sm, buf ^ 1, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, wave, lane, fp);
-      if (wave_rows) {
-        const int klen = min(kBK, a.segs[cur.seg].len - cur.tile * kBK);
-        const int32_t* kp = sm.kpos[buf];
-        const int32_t* kd = sm.kdoc[buf];
-        int wcls = classify(mask, wqmin, wqmax, wqdmin, wqdmax, kp[0], kp[klen - 1],
-                            mask == kMaskCausalDoc ? kd[0] : 0,
-                            mask == kMaskCausalDoc ? kd[klen - 1] : 0);
-        if (wcls == kTileFull && klen < kBK) wcls = kTilePartial;
-        if (wcls == kTileFull)
-          tile_step<D, false>(sm.k[buf], sm.v[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
-                              a.scale_log2, lane);
-        else if (wcls == kTilePartial)
-          tile_step<D, true>(sm.k[buf], sm.v[buf], kp, kd, klen, qf, o, m, l, qpos, qdoc, mask,
-                             a.scale_log2, lane);
+      if (nxt.seg >= 0) {
+        tn = iter_tile(it, nxt, job.seg_begin, kvh, a.hkv, D);
+        fill_tile<D, Sm>(sm, buf ^ 1, tn, rs, doc, wave, lane, fo);
+      }
+      if (!tc.empty) {
+        if (tc.full)
+          tile_step<D, false>(sm.k[buf], sm.v[buf], sm.kpos[buf], sm.kdoc[buf], kBK, qf, o, m, l, qpos, qdoc,
+                              mask, a.scale_log2, lane);
+        else
+          tile_step<D, true>(sm.k[buf], sm.v[buf], sm.kpos[buf], sm.kdoc[buf], tc.last + 1, qf, o, m, l, qpos,
+                             qdoc, mask, a.scale_log2, lane);
       }
       if (nxt.seg < 0) break;
       fill_barrier();
       buf ^= 1;
       cur = nxt;
+      tc = tn;
     }
   }
 
   // finalize: combine the two lane halves' partial sums, normalise, store
-  const float lt = l + swap_halves(l);
+  const float lt = half_sum(l);
   const bool live = lt > 0.0f;
   const float inv = live ? 1.0f / lt : 0.0f;
   const float lse = live ? (m + fast_log2(lt)) * kLn2 : neg_inf();
   if (row_ok) {
-    const int h = lane >> 5;
     const int64_t rowoff = ((int64_t)myrow * a.hq + head) * D;
     float* o32 = nsplit > 1 ? job.ws_o + (int64_t)split * job.len * a.hq * D : reinterpret_cast<float*>(job.o);
 #pragma unroll

@@ -34,40 +34,21 @@ struct KvSmem {
 };
 
 
-// Next KV tile at or after (s, t) that the query range can see; seg = -1 if none.
-__device__ __forceinline__ TileRef next_tile(const FwdArgs& a, int seg_end, int s, int t, int qmin,
-                                             int qmax, int qdmin, int qdmax) {
-  const int mask = a.mask;
-  for (; s < seg_end; ++s, t = 0) {
-    const int len = a.segs[s].len;
-    const int32_t* pos = a.segs[s].pos;
-    const int32_t* doc = a.segs[s].doc;
-    const int nt = (len + kBK - 1) / kBK;
-    for (; t < nt; ++t) {
-      const int k0 = t * kBK;
-      const int k1 = min(len, k0 + kBK) - 1;
-      if (mask == kMaskNone) return {s, t};
-      const int kmin = pos[k0];
-      // positions ascend inside a segment: once a tile starts after the last query,
-      // no later tile of that segment is visible either
-      if (kmin > qmax) break;
-      int kdmin = 0, kdmax = 0;
-      if (mask == kMaskCausalDoc) {
-        kdmin = doc[k0];
-        kdmax = doc[k1];
-      }
-      if (classify(mask, qmin, qmax, qdmin, qdmax, kmin, pos[k1], kdmin, kdmax) != kTileEmpty) return {s, t};
-    }
-  }
-  return {-1, 0};
-}
-
-// Iterator over the KV tiles one work-group processes.  Scan mode walks the job's
-// segments with next_tile().  Mask mode (KV split across work-groups) first classifies
-// every tile of the job lane-parallel into four 64-bit ballot masks over the job's
-// tile sequence, then yields the visible tiles of rank [first, first + count).
+// Iterator over the KV tiles one work-group processes.  Scan mode: positions (and
+// documents) are non-decreasing inside a segment, so the tiles a query range can see
+// are one contiguous range per segment; lane s finds segment s's range once by binary
+// search (iter_init_ranges) and the walk itself touches no memory.  Mask mode (KV
+// split across work-groups) first classifies every tile of the job lane-parallel into
+// four 64-bit ballot masks over the job's tile sequence, then yields the visible tiles
+// of rank [first, first + count).
 struct TileIter {
   bool mask_mode;
+  int rlo, rhi;  // scan mode, lane s: visible tiles [rlo, rhi) of segment seg_begin + s
+  // optional per-lane copy of the job's segment table (lane s: segment seg_begin + s),
+  // read back with readlane so that a tile loop issues no scalar memory loads, and
+  // that segment's visibility ranges for one wave's rows (iter_init_lanes)
+  uint32_t k_lo, k_hi, v_lo, v_hi, p_lo, p_hi, d_lo, d_hi;
+  int len, toff, wlo, whi, flo, fhi;
   uint64_t v0, v1, v2, v3;
   uint64_t m;   // unvisited bits of the current word
   int w;        // current word
@@ -109,6 +90,201 @@ __device__ __forceinline__ void iter_init_masks(TileIter& it, const FwdArgs& a, 
   it.v3 = v[3];
 }
 
+__device__ __forceinline__ void iter_init_ranges(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
+                                                 int qmin, int qmax, int qdmin, int qdmax) {
+  int lo = 0, hi = 0;
+  if (lane < job.seg_end - job.seg_begin) {
+    const SegDesc& sg = a.segs[job.seg_begin + lane];
+    const int nt = (sg.len + kBK - 1) / kBK;
+    hi = nt;
+    if (a.mask != kMaskNone && nt > 0) {
+      const bool docm = a.mask == kMaskCausalDoc;
+      // hi: first tile whose first key lies after the last query (or in a later document)
+      int l0 = 0, h0 = nt;
+      while (l0 < h0) {
+        const int t = (l0 + h0) >> 1;
+        const bool after = sg.pos[t * kBK] > qmax || (docm && sg.doc[t * kBK] > qdmax);
+        if (after) h0 = t; else l0 = t + 1;
+      }
+      hi = l0;
+      // lo: first tile whose last key is in the first query document or later
+      if (docm) {
+        int l1 = 0, h1 = hi;
+        while (l1 < h1) {
+          const int t = (l1 + h1) >> 1;
+          if (sg.doc[min(sg.len, t * kBK + kBK) - 1] >= qdmin) h1 = t; else l1 = t + 1;
+        }
+        lo = l1;
+      }
+    }
+  }
+  it.rlo = lo;
+  it.rhi = hi;
+}
+
+// Scan ranges, per-lane segment table and per-wave visibility ranges in one pass.
+// Lane s binary-searches segment seg_begin + s for six boundaries at once, each a
+// monotone predicate over the tiles (positions and documents are non-decreasing):
+//   hi / whi  first tile whose first key lies after the last query of the work-group /
+//             of the wave (or in a later document): tiles from there on are invisible;
+//   lo / wlo  first tile whose last key is in the first query document of the
+//             work-group / of the wave or later (documents only): tiles before it are
+//             invisible;
+//   fhi       first whole tile whose last key lies after the wave's first query (or in
+//             a later document than the wave's first) ...
+//   flo       ... and the first tile whose first key is in the wave's query document:
+//             tiles in [flo, fhi) are fully visible to every row of the wave (a wave
+//             that spans several documents has none).
+// [lo, hi) is the work-group's walk; [wlo, whi) the tiles the wave computes at all.
+struct VisRanges {
+  int lo, hi, wlo, whi, flo, fhi;
+};
+__device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
+                                                int qmax, int qdmin, int qdmax, bool wave_rows, int wqmin,
+                                                int wqmax, int wqdmin, int wqdmax) {
+  int len = 0, toff = 0;
+  uint64_t kp = 0, vp = 0, pp = 0, dp = 0;
+  VisRanges r = {0, 0, 0, 0, 0, 0};
+  if (lane < job.seg_end - job.seg_begin) {
+    const SegDesc& sg = a.segs[job.seg_begin + lane];
+    len = sg.len;
+    toff = sg.tile_off;
+    kp = reinterpret_cast<uint64_t>(sg.k);
+    vp = reinterpret_cast<uint64_t>(sg.v);
+    pp = reinterpret_cast<uint64_t>(sg.pos);
+    dp = reinterpret_cast<uint64_t>(sg.doc);
+    const int nt = (len + kBK - 1) / kBK, nf = len / kBK;
+    const bool docm = a.mask == kMaskCausalDoc;
+    const int32_t* pos = sg.pos;
+    const int32_t* dc = sg.doc;
+    const int wnt = wave_rows ? nt : 0;
+    const int wnf = wave_rows && (!docm || wqdmin == wqdmax) ? nf : 0;
+    r = {0, nt, 0, wnt, 0, wnf};
+    if (a.mask != kMaskNone) {
+      // [l, h) search intervals; the document-only searches start empty without documents
+      int l0 = 0, h0 = nt, l1 = 0, h1 = docm ? nt : 0, l2 = 0, h2 = wnt, l3 = 0, h3 = docm ? wnt : 0;
+      int l4 = 0, h4 = wnf, l5 = 0, h5 = docm ? wnf : 0;
+      while (l0 < h0 || l1 < h1 || l2 < h2 || l3 < h3 || l4 < h4 || l5 < h5) {
+        const int m0 = (l0 + h0) >> 1, m1 = (l1 + h1) >> 1, m2 = (l2 + h2) >> 1;
+        const int m3 = (l3 + h3) >> 1, m4 = (l4 + h4) >> 1, m5 = (l5 + h5) >> 1;
+        bool p0 = false, p1 = false, p2 = false, p3 = false, p4 = false, p5 = false;
+        if (l0 < h0) p0 = pos[m0 * kBK] > qmax || (docm && dc[m0 * kBK] > qdmax);
+        if (l1 < h1) p1 = dc[min(len, m1 * kBK + kBK) - 1] >= qdmin;
+        if (l2 < h2) p2 = pos[m2 * kBK] > wqmax || (docm && dc[m2 * kBK] > wqdmax);
+        if (l3 < h3) p3 = dc[min(len, m3 * kBK + kBK) - 1] >= wqdmin;
+        if (l4 < h4) p4 = pos[m4 * kBK + kBK - 1] > wqmin || (docm && dc[m4 * kBK + kBK - 1] > wqdmin);
+        if (l5 < h5) p5 = dc[m5 * kBK] >= wqdmin;
+        if (l0 < h0) { if (p0) h0 = m0; else l0 = m0 + 1; }
+        if (l1 < h1) { if (p1) h1 = m1; else l1 = m1 + 1; }
+        if (l2 < h2) { if (p2) h2 = m2; else l2 = m2 + 1; }
+        if (l3 < h3) { if (p3) h3 = m3; else l3 = m3 + 1; }
+        if (l4 < h4) { if (p4) h4 = m4; else l4 = m4 + 1; }
+        if (l5 < h5) { if (p5) h5 = m5; else l5 = m5 + 1; }
+      }
+      r = {l1, l0, l3, l2, l5, l4};
+    }
+  }
+  it.rlo = r.lo;
+  it.rhi = r.hi;
+  it.wlo = r.wlo;
+  it.whi = r.whi;
+  it.flo = r.flo;
+  it.fhi = r.fhi;
+  it.len = len;
+  it.toff = toff;
+  it.k_lo = (uint32_t)kp;
+  it.k_hi = (uint32_t)(kp >> 32);
+  it.v_lo = (uint32_t)vp;
+  it.v_hi = (uint32_t)(vp >> 32);
+  it.p_lo = (uint32_t)pp;
+  it.p_hi = (uint32_t)(pp >> 32);
+  it.d_lo = (uint32_t)dp;
+  it.d_hi = (uint32_t)(dp >> 32);
+}
+
+// One visible tile with its segment's data resolved from the per-lane table
+// (wave-uniform values; the pointers address the tile's first key).
+struct KvTile {
+  const bf16* k;
+  const bf16* v;
+  const int32_t* pos;
+  const int32_t* doc;
+  int last;    // index of the tile's last key (tile length - 1)
+  bool full;   // every key visible to every row of the wave (and a whole tile)
+  bool empty;  // no key visible to any row of the wave
+};
+
+__device__ __forceinline__ uint64_t lane_u64(uint32_t lo, uint32_t hi, int s) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, s) << 32 | (uint32_t)__builtin_amdgcn_readlane(lo, s);
+}
+
+__device__ __forceinline__ KvTile iter_tile(const TileIter& it, TileRef r, int seg_begin, int kvh, int hkv, int D) {
+  const int s = r.seg - seg_begin;
+  const int k0 = r.tile * kBK;
+  const int64_t eoff = ((int64_t)k0 * hkv + kvh) * D;
+  KvTile t;
+  t.k = reinterpret_cast<const bf16*>(lane_u64(it.k_lo, it.k_hi, s)) + eoff;
+  t.v = reinterpret_cast<const bf16*>(lane_u64(it.v_lo, it.v_hi, s)) + eoff;
+  t.pos = reinterpret_cast<const int32_t*>(lane_u64(it.p_lo, it.p_hi, s)) + k0;
+  t.doc = reinterpret_cast<const int32_t*>(lane_u64(it.d_lo, it.d_hi, s)) + k0;
+  t.last = min(kBK, __builtin_amdgcn_readlane(it.len, s) - k0) - 1;
+  t.full = r.tile >= __builtin_amdgcn_readlane(it.flo, s) && r.tile < __builtin_amdgcn_readlane(it.fhi, s);
+  t.empty = r.tile < __builtin_amdgcn_readlane(it.wlo, s) || r.tile >= __builtin_amdgcn_readlane(it.whi, s);
+  return t;
+}
+
+// Direct global->LDS fill of one KV tile into a KvSmem image (see FillPlan for the
+// slot layout), from a resolved tile.  Per fill instruction each lane's source is a
+// fixed element offset (key row * row stride + column) clamped to
+// last * stride + D - 8: rows up to the tile's last key stay exact, rows after it
+// (ragged tile) read the last chunk of key `last` (finite data; those keys are masked).
+template <int D, class Smem>
+struct FillOffs {
+  static constexpr int kKSlots = Smem::kKS / 8;
+  static constexpr int kVSlots = Smem::kVS / 8;
+  static constexpr int kKInst = kBK * kKSlots / kWave;
+  static constexpr int kVInst = kBK * kVSlots / kWave;
+  static constexpr int kKPer = (kKInst + 3) / 4;  // per wave (4 waves)
+  static constexpr int kVPer = (kVInst + 3) / 4;
+  static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
+  uint32_t ko[kKPer], vo[kVPer];
+
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t rs) {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int slot = kWave * (wave + 4 * j) + lane;
+      const int c = slot % kKSlots;
+      ko[j] = (uint32_t)(slot / kKSlots) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int slot = kWave * (wave + 4 * j) + lane;
+      const int c = slot % kVSlots;
+      vo[j] = (uint32_t)(slot / kVSlots) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
+    }
+  }
+};
+
+template <int D, class Smem>
+__device__ __forceinline__ void fill_tile(Smem& sm, int buf, const KvTile& t, uint32_t rs, bool doc, int wave,
+                                          int lane, const FillOffs<D, Smem>& fo) {
+  using FO = FillOffs<D, Smem>;
+  const uint32_t cap = (uint32_t)t.last * rs + D - 8;
+  const uint32_t kl = lds_offset(sm.k[buf]), vl = lds_offset(sm.v[buf]);
+#pragma unroll
+  for (int j = 0; j < FO::kKPer; ++j) {
+    const int jj = wave + 4 * j;
+    if (jj < FO::kKInst) fill16_untracked(t.k + min(fo.ko[j], cap), kl + jj * kWave * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < FO::kVPer; ++j) {
+    const int jj = wave + 4 * j;
+    if (jj < FO::kVInst) fill16_untracked(t.v + min(fo.vo[j], cap), vl + jj * kWave * 16);
+  }
+  if (wave == 0) fill4_untracked(t.pos + min(lane, t.last), lds_offset(sm.kpos[buf]));
+  if (wave == 1 && doc) fill4_untracked(t.doc + min(lane, t.last), lds_offset(sm.kdoc[buf]));
+}
+
 __device__ __forceinline__ int iter_count(const TileIter& it) {
   return __popcll(it.v0) + __popcll(it.v1) + __popcll(it.v2) + __popcll(it.v3);
 }
@@ -128,11 +304,20 @@ __device__ __forceinline__ void iter_seek(TileIter& it, int first, int count, in
   it.seg = seg_begin;
 }
 
+// kLanes: the per-lane segment table is loaded (iter_init_lanes); the walk then
+// reads no kernel arguments either.
+template <bool kLanes = false>
 __device__ __forceinline__ TileRef iter_next(TileIter& it, const FwdArgs& a, const JobDesc& job, TileRef prev,
                                              int qmin, int qmax, int qdmin, int qdmax) {
   if (!it.mask_mode) {
-    if (prev.seg < 0) return next_tile(a, job.seg_end, job.seg_begin, 0, qmin, qmax, qdmin, qdmax);
-    return next_tile(a, job.seg_end, prev.seg, prev.tile + 1, qmin, qmax, qdmin, qdmax);
+    int s = prev.seg < 0 ? job.seg_begin : prev.seg;
+    int t = prev.seg < 0 ? __builtin_amdgcn_readlane(it.rlo, 0) : prev.tile + 1;
+    while (s < job.seg_end) {
+      if (t < __builtin_amdgcn_readlane(it.rhi, s - job.seg_begin)) return {s, t};
+      ++s;
+      if (s < job.seg_end) t = __builtin_amdgcn_readlane(it.rlo, s - job.seg_begin);
+    }
+    return {-1, 0};
   }
   if (it.left == 0) return {-1, 0};
   while (it.m == 0) {
@@ -142,6 +327,10 @@ __device__ __forceinline__ TileRef iter_next(TileIter& it, const FwdArgs& a, con
   const int g = 64 * it.w + __builtin_ctzll(it.m);
   it.m &= it.m - 1;
   --it.left;
+  if (kLanes) {
+    while (it.seg + 1 < job.seg_end && __builtin_amdgcn_readlane(it.toff, it.seg + 1 - job.seg_begin) <= g) ++it.seg;
+    return {it.seg, g - __builtin_amdgcn_readlane(it.toff, it.seg - job.seg_begin)};
+  }
   while (it.seg + 1 < job.seg_end && a.segs[it.seg + 1].tile_off <= g) ++it.seg;
   return {it.seg, g - a.segs[it.seg].tile_off};
 }
