@@ -76,10 +76,12 @@ __device__ __forceinline__ void mask_scores(float (&x)[32], const int32_t* kp, c
   }
 }
 
-// One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.
-template <int D, bool MASKED>
+// One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.  One
+// code path for both kinds of tile (only the mask is conditional), so that the
+// accumulators keep one register home across the loop.
+template <int D>
 __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf16* __restrict__ vs,
-                                          const int32_t* kpos, const int32_t* kdoc, int klen,
+                                          bool masked, const int32_t* kpos, const int32_t* kdoc, int klen,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           float& m, float& l, int qpos, int qdoc, int mask,
                                           float scale_log2, int lane) {
@@ -100,7 +102,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
     x[i] = s0[i];
     x[16 + i] = s1[i];
   }
-  if (MASKED) mask_scores(x, kpos, kdoc, klen, qpos, qdoc, mask, h);
+  if (masked) mask_scores(x, kpos, kdoc, klen, qpos, qdoc, mask, h);
   float mt = x[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
@@ -243,14 +245,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         tn = iter_tile(it, nxt, job.seg_begin, kvh, a.hkv, D);
         fill_tile<D, Sm>(sm, buf ^ 1, tn, rs, doc, wave, lane, fo);
       }
-      if (!tc.empty) {
-        if (tc.full)
-          tile_step<D, false>(sm.k[buf], sm.v[buf], sm.kpos[buf], sm.kdoc[buf], kBK, qf, o, m, l, qpos, qdoc,
-                              mask, a.scale_log2, lane);
-        else
-          tile_step<D, true>(sm.k[buf], sm.v[buf], sm.kpos[buf], sm.kdoc[buf], tc.last + 1, qf, o, m, l, qpos,
-                             qdoc, mask, a.scale_log2, lane);
-      }
+      if (!tc.empty)
+        tile_step<D>(sm.k[buf], sm.v[buf], !tc.full, sm.kpos[buf], sm.kdoc[buf], tc.last + 1, qf, o, m, l, qpos,
+                     qdoc, mask, a.scale_log2, lane);
       if (nxt.seg < 0) break;
       fill_barrier();
       buf ^= 1;
