@@ -99,16 +99,16 @@ __device__ __forceinline__ void dq_step(const bf16* __restrict__ ks, const bf16*
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[4 * g + e], scale_log2, -lse2));
-      if (masked) {
+      if (masked) {  // branch-free; the document image is ignored without documents
+        const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
+        const bool docm = mask == kMaskCausalDoc;
         const int4 kp = *reinterpret_cast<const int4*>(kpos + base);
         const int4 kd = *reinterpret_cast<const int4*>(kdoc + base);
         const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
         const int kda[4] = {kd.x, kd.y, kd.z, kd.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bool vis = base + e < klen;
-          if (mask != kMaskNone) vis = vis && kpa[e] <= qpos;
-          if (mask == kMaskCausalDoc) vis = vis && kda[e] == qdoc;
+          const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
           p[e] = vis ? p[e] : 0.0f;
         }
       }
@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
   while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
   const JobDesc& job = a.jobs[j];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hpw = a.heads_per_wg;
   const int qt_rows = (kv::kThreads / kWave) * kRowsPerWave / hpw;
   const int n_qt = (job.len + qt_rows - 1) / qt_rows;
@@ -205,9 +206,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
   for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
   float* flag_dst = nsplit > 1 ? job.ws_lse + (int64_t)split * job.len * a.hq : nullptr;
+  // tiles of the walk, and per wave the skipped and the fully visible ones, from one
+  // binary search per segment (kv_stream.h); the loop reads no segment table
   TileIter it;
   it.mask_mode = nsplit > 1;
-  if (nsplit == 1) iter_init_ranges(it, a, job, lane, qmin, qmax, qdmin, qdmax);
+  iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax);
   if (nsplit > 1) {
     iter_init_masks(it, a, job, lane, qmin, qmax, qdmin, qdmax);
     const int total = iter_count(it);
@@ -219,31 +222,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
     iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
   }
 
-  FillPlan<D, DqSmem<D>> fp;
-  fp.init(wave, lane);
-  TileRef cur = iter_next(it, a, job, TileRef{-1, 0}, qmin, qmax, qdmin, qdmax);
+  using Sm = DqSmem<D>;
+  const uint32_t rstride = (uint32_t)a.hkv * D;  // elements between consecutive keys
+  FillOffs<D, Sm> fo;
+  fo.init(wave, lane, rstride);
+  const bool doc = mask == kMaskCausalDoc;
+  TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
   if (cur.seg >= 0) {
-    fill_tile<D, DqSmem<D>>(sm, 0, a.segs[cur.seg], cur.tile, kvh, a.hkv, mask, wave, lane, fp);
+    KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);
+    fill_tile<D, Sm>(sm, 0, tc, rstride, doc, wave, lane, fo);
     fill_barrier();
     int buf = 0;
     while (true) {
-      const TileRef nxt = iter_next(it, a, job, cur, qmin, qmax, qdmin, qdmax);
-      if (nxt.seg >= 0) fill_tile<D, DqSmem<D>>(sm, buf ^ 1, a.segs[nxt.seg], nxt.tile, kvh, a.hkv, mask, wave, lane, fp);
-      if (wave_rows) {
-        const int klen = min(kBK, a.segs[cur.seg].len - cur.tile * kBK);
-        const int32_t* kp = sm.kpos[buf];
-        const int32_t* kd = sm.kdoc[buf];
-        int wcls = classify(mask, wqmin, wqmax, wqdmin, wqdmax, kp[0], kp[klen - 1],
-                            mask == kMaskCausalDoc ? kd[0] : 0, mask == kMaskCausalDoc ? kd[klen - 1] : 0);
-        if (wcls == kTileFull && klen < kBK) wcls = kTilePartial;
-        if (wcls != kTileEmpty)
-          dq_step<D>(sm.k[buf], sm.v[buf], kp, kd, klen, qf, of, dq, lse2, dl, qpos, qdoc, wcls == kTilePartial,
-                     mask, x.scale, a.scale_log2, lane);
+      const TileRef nxt = iter_next<true>(it, a, job, cur, 0, 0, 0, 0);
+      KvTile tn = tc;
+      if (nxt.seg >= 0) {
+        tn = iter_tile(it, nxt, job.seg_begin, kvh, a.hkv, D);
+        fill_tile<D, Sm>(sm, buf ^ 1, tn, rstride, doc, wave, lane, fo);
       }
+      if (!tc.empty)
+        dq_step<D>(sm.k[buf], sm.v[buf], sm.kpos[buf], sm.kdoc[buf], tc.last + 1, qf, of, dq, lse2, dl, qpos,
+                   qdoc, !tc.full, mask, x.scale, a.scale_log2, lane);
       if (nxt.seg < 0) break;
       fill_barrier();
       buf ^= 1;
       cur = nxt;
+      tc = tn;
     }
   }
 
