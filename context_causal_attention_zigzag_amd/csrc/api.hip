@@ -196,7 +196,7 @@ size_t cpattn_tile_fwd_workspace_bytes(const cpattn_attn_desc* desc, int32_t n_e
   size_t need = 0;
   int e = 0;
   while (next_edge_batch(a, n_edges, q_blocks, segs, nullptr, nullptr, e)) {
-    const size_t b = plan_fwd(a, desc->d, desc->dtype, cus, true);
+    const size_t b = plan_fwd(a, desc->d, desc->dtype, cus, true, 0);
     need = b > need ? b : need;
   }
   return need;
@@ -220,8 +220,8 @@ int cpattn_tile_fwd(const cpattn_attn_desc* desc, int32_t n_edges, const cpattn_
   const int cus = device_cus();
   int e = 0;
   while (next_edge_batch(a, n_edges, q_blocks, segs, o_parts, lse_parts, e)) {
-    size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr);
-    if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false);  // too small: no split
+    size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr, 0);
+    if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false, 0);  // too small: no split
     if (need > 0) assign_fwd_workspace(a, desc->d, workspace);
     st = hip_status(launch_fwd(a, desc->d, desc->dtype, true, reinterpret_cast<hipStream_t>(stream)));
     if (st != CPATTN_OK) return st;
@@ -256,7 +256,7 @@ size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpa
   FwdArgs a{};
   fill_common(a, desc);
   fill_stream_job(a, q, n_segs, segs, nullptr, nullptr);
-  return plan_fwd(a, desc->d, desc->dtype, device_cus(), true);
+  return plan_fwd(a, desc->d, desc->dtype, device_cus(), true, 0);
 }
 
 int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -276,8 +276,8 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   fill_common(a, desc);
   fill_stream_job(a, q, n_segs, segs, o_out, lse_out);
   const int cus = device_cus();
-  size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr);
-  if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false);  // too small: no split
+  size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr, 0);
+  if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false, 0);  // too small: no split
   if (need > 0) assign_fwd_workspace(a, desc->d, workspace);
   return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -343,9 +343,9 @@ hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
   const int cus = device_cus();
-  size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true);
+  size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true, 4);
   if (need > 0 && (workspace == nullptr || need > workspace_bytes))
-    need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false);  // too small: no split
+    need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false, 4);  // too small: no split
   if (need > 0) assign_fwd_workspace(f, desc->d, workspace);
   return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, stream);
 }
@@ -382,7 +382,7 @@ size_t bwd_dq_split_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
   FwdArgs f{};
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);
-  return plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true);
+  return plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true, 4);
 }
 
 }  // namespace

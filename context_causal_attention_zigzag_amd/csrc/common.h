@@ -243,6 +243,7 @@ struct FwdArgs {
   float scale_log2;      // softmax scale times log2(e)
   int32_t total_wgs;     // logical work-groups
   int32_t padded_wgs;    // grid size (multiple of 8)
+  int32_t wg_waves;      // waves per work-group of the launch (32 query rows each)
 };
 
 struct BwdArgs {
@@ -276,7 +277,9 @@ hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool partial_out, hipStream_t stream);
 // Split plan for forward jobs: fills n_split / tiles_per_split / n_tiles of each job and
 // the segments' tile offsets; returns the workspace bytes the plan needs.
-size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split);
+// waves: work-group size of the kernel the plan is for (4 or 8), or 0 to let the
+// forward choose (8 when the query tiles alone fill the CUs once, else 4).
+size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int waves);
 // Points the split jobs' partial buffers into a workspace of plan_fwd's size.
 void assign_fwd_workspace(FwdArgs& a, int d, void* ws);
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,

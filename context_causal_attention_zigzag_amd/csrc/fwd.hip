@@ -50,101 +50,179 @@ using namespace kv;
 template <int D>
 using FwdSmem = KvSmem<D, D + 8, D + 24>;
 
-// Visibility of this lane's 32 raw scores of a partially visible tile (positions kp /
-// documents kd in LDS, klen keys) for query position qpos / document qdoc: invisible
-// scores become -inf.  Branch-free (the document image is read even when documents
-// are off; its value is then ignored).
-__device__ __forceinline__ void mask_scores(float (&x)[32], const int32_t* kp, const int32_t* kd, int klen,
-                                            int qpos, int qdoc, int mask, int h) {
+// Work-group of the bf16 kernel: NW waves of 32 query rows share each K/V tile; 8
+// waves (one work-group per CU, half the tile fills per query row) for launches whose
+// query tiles fill the CUs, 4 (two work-groups per CU) with KV splits for small ones.
+constexpr int wg_per_cu(int nw) { return nw == 8 ? 1 : 2; }
+
+// Visibility of this lane's 16 raw scores of key half kb (keys 32 kb .. 32 kb + 31) of
+// a partially visible tile (positions kp / documents kd in LDS, klen keys) for query
+// position qpos / document qdoc: invisible scores become -inf.  Branch-free (the
+// document image is read even when documents are off; its value is then ignored).
+__device__ __forceinline__ void mask_half(f32x16& x, const int32_t* kp, const int32_t* kd, int klen, int qpos,
+                                          int qdoc, int mask, int h, int kb) {
   const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
   const bool docm = mask == kMaskCausalDoc;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int g = 0; g < 4; ++g) {
+    const int base = kb * 32 + 8 * g + 4 * h;
+    const int4 kpv = *reinterpret_cast<const int4*>(kp + base);
+    const int4 kdv = *reinterpret_cast<const int4*>(kd + base);
+    const int kpa[4] = {kpv.x, kpv.y, kpv.z, kpv.w};
+    const int kda[4] = {kdv.x, kdv.y, kdv.z, kdv.w};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int base = kb * 32 + 8 * g + 4 * h;
-      const int4 kpv = *reinterpret_cast<const int4*>(kp + base);
-      const int4 kdv = *reinterpret_cast<const int4*>(kd + base);
-      const int kpa[4] = {kpv.x, kpv.y, kpv.z, kpv.w};
-      const int kda[4] = {kdv.x, kdv.y, kdv.z, kdv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
-        x[kb * 16 + g * 4 + e] = vis ? x[kb * 16 + g * 4 + e] : neg_inf();
-      }
+    for (int e = 0; e < 4; ++e) {
+      const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
+      x[g * 4 + e] = vis ? x[g * 4 + e] : neg_inf();
     }
   }
 }
 
-// One KV tile for one wave: S^T, (masked) online-softmax update, O^T += V^T P^T.  One
-// code path for both kinds of tile (only the mask is conditional), so that the
-// accumulators keep one register home across the loop.
+// V^T operand of O^T += V^T P^T for dims 32 db .. 32 db + 31 and key slice j (keys
+// 16 j .. 16 j + 15 in the order of P^T's rows): two transposing reads of row-major V.
+template <int D>
+__device__ __forceinline__ bf16x8 v_op(const bf16* vl, int db, int j) {
+  constexpr int kVS = FwdSmem<D>::kVS;
+  const bf16* p = vl + j * 16 * kVS + db * 32;
+  return concat(lds_read_tr4(p), lds_read_tr4(p + 8 * kVS));
+}
+
+// One KV tile for one wave: S^T, online-softmax update, O^T += V^T P^T, in four
+// phases over the tile's two key halves A (keys 0..31) and B (32..63):
+//   S_A;  S_B beside P_A;  O += V_A P_A beside P_B;  O += V_B P_B.
+// Each middle phase pairs matrix-core work with independent vector work, so the wave
+// keeps the matrix core busy while it exponentiates.  P of a half is computed against
+// the running maximum of the earlier tiles (mu); a score above mu + 2^8 (rare after
+// the first tile) sends the half through a rescale first: for half A before any of
+// the tile's products (the maximum then covers the whole tile), for half B after
+// the products of half A, which are still in the old scale and are rescaled with O.
+// One code path for full and partial tiles (only the mask is conditional), so that
+// the accumulators keep one register home across the loop.
 template <int D>
 __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf16* __restrict__ vs,
                                           bool masked, const int32_t* kpos, const int32_t* kdoc, int klen,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           float& m, float& l, int qpos, int qdoc, int mask,
                                           float scale_log2, int lane) {
-  constexpr int kKS = FwdSmem<D>::kKS, kVS = FwdSmem<D>::kVS;
+  constexpr int kKS = FwdSmem<D>::kKS;
+  constexpr int kSt = D / 16;   // stages of each middle phase (= S steps = PV products per half)
+  constexpr int kE = 16 / kSt;  // exponentials per stage
+  static_assert(16 % kSt == 0 && kSt >= 4, "whole exponentials per stage");
   const int r = lane & 31, h = lane >> 5;
-  f32x16 s0 = {}, s1 = {};
+  const bf16* ka = ks + r * kKS + h * 8;
+  const bf16* kb = ka + 32 * kKS;
+  const bf16* vl = vs + tr_lane_offset<4>(lane, FwdSmem<D>::kVS);
+  // product k of a PV phase: dims 32 (k / 2) .., key slice (k % 2) of the half
+  auto vop = [&](int half, int k) { return v_op<D>(vl, k >> 1, 2 * half + (k & 1)); };
+  auto kop = [&](const bf16* base, int ds) { return *reinterpret_cast<const bf16x8*>(base + ds * 16); };
+
+  // S_A (raw scores; the softmax scale times log2 e is applied inside the exp argument)
+  f32x16 sa = {}, sb = {};
 #pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + r * kKS + ds * 16 + h * 8);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + (32 + r) * kKS + ds * 16 + h * 8);
-    s0 = mfma32x32x16(a0, qf[ds], s0);
-    s1 = mfma32x32x16(a1, qf[ds], s1);
+  for (int ds = 0; ds < kSt; ++ds) sa = mfma32x32x16(kop(ka, ds), qf[ds], sa);
+  // operands of the next phase's first two steps, two steps ahead from there on
+  bf16x8 op[2] = {kop(kb, 0), kop(kb, 1)};
+  if (masked) mask_half(sa, kpos, kdoc, klen, qpos, qdoc, mask, h, 0);
+  float mu = (m == neg_inf()) ? 0.0f : m;
+
+  // S_B beside P_A
+  bf16x8 pf[4];
+  float rs = 0.0f, mta = neg_inf();
+#pragma unroll
+  for (int k = 0; k < kSt; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    sb = mfma32x32x16(op[k & 1], qf[k], sb);
+    op[k & 1] = k + 2 < kSt ? kop(kb, k + 2) : vop(0, k + 2 - kSt);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int i = k * kE + e;
+      const float p = fast_exp2(fmaf(sa[i], scale_log2, -mu));
+      rs += p;
+      pf[i >> 3][i & 7] = (bf16)p;
+      mta = fmaxf(mta, sa[i]);
+    }
   }
-  // raw scores; the softmax scale (times log2 e) is applied inside the exp argument
-  float x[32];
+  // keep P_A in its phase (it is used only after the branches below)
+  asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(rs), "v"(mta));
+  __builtin_amdgcn_sched_barrier(0);
+  if (masked) mask_half(sb, kpos, kdoc, klen, qpos, qdoc, mask, h, 1);
+  mta = half_max(mta) * scale_log2;  // -inf stays -inf (scale > 0)
+  if (__any(mta > m + kTau)) {
+    // the maximum moved in half A: rescale against the maximum of the whole tile (so
+    // that half B cannot move it again), P_A again
+    float mt = neg_inf();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = s0[i];
-    x[16 + i] = s1[i];
-  }
-  if (masked) mask_scores(x, kpos, kdoc, klen, qpos, qdoc, mask, h);
-  float mt = x[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-  mt = half_max(mt) * scale_log2;  // -inf stays -inf (scale > 0)
-  const float m_new = fmaxf(m, mt);
-  const bool need = m_new > m + kTau;
-  if (__any(need)) {
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sb[i]);
+    mt = fmaxf(mta, half_max(mt) * scale_log2);
+    const float m_new = fmaxf(m, mt);
+    const bool need = m_new > m + kTau;
     const float c = need ? fast_exp2(m - m_new) : 1.0f;
     if (need) m = m_new;
+    mu = (m == neg_inf()) ? 0.0f : m;
     l *= c;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] *= c;
-  }
-  const float mu = (m == neg_inf()) ? 0.0f : m;
-  float rs = 0.0f;
-  bf16x8 pf[4];
+    rs = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(fmaf(x[j * 8 + e], scale_log2, -mu));
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sa[i], scale_log2, -mu));
       rs += p;
-      pf[j][e] = (bf16)p;
+      pf[i >> 3][i & 7] = (bf16)p;
     }
   }
   l += rs;
-  // O^T += V^T P^T: the V^T operand of key slice j (keys 16j..16j+15, in the order
-  // of P^T's rows) for dims 32db..32db+31 is two transposing reads of row-major V.
-  const bf16* vl = vs + tr_lane_offset<4>(lane, kVS);
+
+  // O += V_A P_A beside P_B
+  float mtb = neg_inf();
+  rs = 0.0f;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int k = 0; k < kSt; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    o[k >> 1] = mfma32x32x16(op[k & 1], pf[k & 1], o[k >> 1]);
+    op[k & 1] = k + 2 < kSt ? vop(0, k + 2) : vop(1, k + 2 - kSt);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16* p = vl + j * 16 * kVS + db * 32;
-      const bf16x8 a = concat(lds_read_tr4(p), lds_read_tr4(p + 8 * kVS));
-      o[db] = mfma32x32x16(a, pf[j], o[db]);
+    for (int e = 0; e < kE; ++e) {
+      const int i = k * kE + e;
+      const float p = fast_exp2(fmaf(sb[i], scale_log2, -mu));
+      rs += p;
+      pf[2 + (i >> 3)][i & 7] = (bf16)p;
+      mtb = fmaxf(mtb, sb[i]);
     }
+  }
+  asm volatile("" ::"v"(pf[2]), "v"(pf[3]), "v"(rs), "v"(mtb));
+  __builtin_amdgcn_sched_barrier(0);
+  mtb = half_max(mtb) * scale_log2;
+  if (__any(mtb > m + kTau)) {
+    // the maximum moved in half B: O (with the products of half A, in the old scale)
+    // and l follow, P_B again
+    const float m_new = fmaxf(m, mtb);
+    const bool need = m_new > m + kTau;
+    const float c = need ? fast_exp2(m - m_new) : 1.0f;
+    if (need) m = m_new;
+    mu = (m == neg_inf()) ? 0.0f : m;
+    l *= c;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= c;
+    rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sb[i], scale_log2, -mu));
+      rs += p;
+      pf[2 + (i >> 3)][i & 7] = (bf16)p;
+    }
+  }
+  l += rs;
+
+  // O += V_B P_B
+#pragma unroll
+  for (int k = 0; k < kSt; ++k) {
+    o[k >> 1] = mfma32x32x16(op[k & 1], pf[2 + (k & 1)], o[k >> 1]);
+    if (k + 2 < kSt) op[k & 1] = vop(1, k + 2);
   }
 }
 
-template <int D, bool PARTIAL_OUT>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, bool PARTIAL_OUT, int NW>
+__global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(FwdArgs a) {
   using Sm = FwdSmem<D>;
   __shared__ Sm sm;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
@@ -157,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int hpw = a.heads_per_wg;
-  const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
+  const int qt_rows = NW * kRowsPerWave / hpw;
   const int n_qt = (job.len + qt_rows - 1) / qt_rows;
   const int nsplit = job.n_split;
   const int local = logical - job.wg_begin;
@@ -229,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   const uint32_t rs = (uint32_t)a.hkv * D;  // elements between consecutive keys
-  FillOffs<D, Sm> fo;
+  FillOffs<D, Sm, NW> fo;
   fo.init(wave, lane, rs);
   TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
   if (cur.seg >= 0) {
@@ -382,7 +460,8 @@ template <int D>
 hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t stream) {
   if (dtype == 0) {
     const int hpw = a.heads_per_wg;
-    const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
+    const int nw = a.wg_waves == 8 ? 8 : 4;
+    const int qt_rows = nw * kRowsPerWave / hpw;
     int total = 0;
     for (int j = 0; j < a.n_jobs; ++j) {
       a.jobs[j].wg_begin = total;
@@ -392,10 +471,18 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
     a.total_wgs = total;
     a.padded_wgs = (total + 7) & ~7;
     if (total == 0) return hipSuccess;
-    if (partial_out)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.padded_wgs), dim3(kThreads), 0, stream, a);
+    const dim3 grid(a.padded_wgs), block(nw * kWave);
+    if (nw == 8) {
+      if (partial_out)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 8>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 8>), grid, block, 0, stream, a);
+    } else {
+      if (partial_out)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 4>), grid, block, 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // log-sum-exp merge of the KV splits of every split job, one launch
@@ -430,13 +517,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// KV-split plan.  A launch needs on the order of 4 work-groups per compute unit (two
-// resident per CU, two rounds) to fill the chip; when the query tiles alone give fewer,
-// each job's visible KV tiles are cut into splits of tiles_per_split tiles so that
+// KV-split plan.  A launch needs on the order of two rounds of resident work-groups
+// (wg_per_cu of the chosen size per compute unit) to fill the chip; when the query
+// tiles alone give fewer, each job's visible KV tiles are cut into splits of tiles_per_split tiles so that
 // the expected number of busy work-groups (causal: about half of a job's tiles are
 // visible to an average query tile) reaches that target.  Jobs spanning more than
 // 256 KV tiles are never split (they already carry enough work per query tile).
-size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split) {
+size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int waves) {
   for (int j = 0; j < a.n_jobs; ++j) {
     JobDesc& jb = a.jobs[j];
     int off = 0;
@@ -450,12 +537,18 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split) {
     jb.ws_o = nullptr;
     jb.ws_lse = nullptr;
   }
-  if (dtype != 0 || !allow_split) return 0;
   const int hpw = a.heads_per_wg;
-  const int qt_rows = (kThreads / kWave) * kRowsPerWave / hpw;
-  int64_t base = 0;
-  for (int j = 0; j < a.n_jobs; ++j) base += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw);
-  const int64_t target = 4LL * num_cu;
+  auto query_wgs = [&](int nw) {
+    const int qt_rows = nw * kRowsPerWave / hpw;
+    int64_t n = 0;
+    for (int j = 0; j < a.n_jobs; ++j) n += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw);
+    return n;
+  };
+  if (waves == 0) waves = query_wgs(8) >= num_cu ? 8 : 4;
+  a.wg_waves = waves;
+  if (dtype != 0 || !allow_split) return 0;
+  const int64_t base = query_wgs(waves);
+  const int64_t target = 2LL * wg_per_cu(waves) * num_cu;
   if (base == 0 || base >= target) return 0;
   size_t bytes = 0;
   for (int j = 0; j < a.n_jobs; ++j) {

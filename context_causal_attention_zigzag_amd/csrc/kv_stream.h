@@ -238,47 +238,47 @@ __device__ __forceinline__ KvTile iter_tile(const TileIter& it, TileRef r, int s
 // fixed element offset (key row * row stride + column) clamped to
 // last * stride + D - 8: rows up to the tile's last key stay exact, rows after it
 // (ragged tile) read the last chunk of key `last` (finite data; those keys are masked).
-template <int D, class Smem>
+template <int D, class Smem, int kWaves = 4>
 struct FillOffs {
   static constexpr int kKSlots = Smem::kKS / 8;
   static constexpr int kVSlots = Smem::kVS / 8;
   static constexpr int kKInst = kBK * kKSlots / kWave;
   static constexpr int kVInst = kBK * kVSlots / kWave;
-  static constexpr int kKPer = (kKInst + 3) / 4;  // per wave (4 waves)
-  static constexpr int kVPer = (kVInst + 3) / 4;
+  static constexpr int kKPer = (kKInst + kWaves - 1) / kWaves;  // per wave
+  static constexpr int kVPer = (kVInst + kWaves - 1) / kWaves;
   static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
   uint32_t ko[kKPer], vo[kVPer];
 
   __device__ __forceinline__ void init(int wave, int lane, uint32_t rs) {
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
+      const int slot = kWave * (wave + kWaves * j) + lane;
       const int c = slot % kKSlots;
-      ko[j] = (uint32_t)(slot / kKSlots) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
+      ko[j] = (uint32_t)min(slot / kKSlots, kBK - 1) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
     }
 #pragma unroll
     for (int j = 0; j < kVPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
+      const int slot = kWave * (wave + kWaves * j) + lane;
       const int c = slot % kVSlots;
-      vo[j] = (uint32_t)(slot / kVSlots) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
+      vo[j] = (uint32_t)min(slot / kVSlots, kBK - 1) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
     }
   }
 };
 
-template <int D, class Smem>
+template <int D, class Smem, int kWaves>
 __device__ __forceinline__ void fill_tile(Smem& sm, int buf, const KvTile& t, uint32_t rs, bool doc, int wave,
-                                          int lane, const FillOffs<D, Smem>& fo) {
-  using FO = FillOffs<D, Smem>;
+                                          int lane, const FillOffs<D, Smem, kWaves>& fo) {
+  using FO = FillOffs<D, Smem, kWaves>;
   const uint32_t cap = (uint32_t)t.last * rs + D - 8;
   const uint32_t kl = lds_offset(sm.k[buf]), vl = lds_offset(sm.v[buf]);
 #pragma unroll
   for (int j = 0; j < FO::kKPer; ++j) {
-    const int jj = wave + 4 * j;
+    const int jj = wave + kWaves * j;
     if (jj < FO::kKInst) fill16_untracked(t.k + min(fo.ko[j], cap), kl + jj * kWave * 16);
   }
 #pragma unroll
   for (int j = 0; j < FO::kVPer; ++j) {
-    const int jj = wave + 4 * j;
+    const int jj = wave + kWaves * j;
     if (jj < FO::kVInst) fill16_untracked(t.v + min(fo.vo[j], cap), vl + jj * kWave * 16);
   }
   if (wave == 0) fill4_untracked(t.pos + min(lane, t.last), lds_offset(sm.kpos[buf]));
