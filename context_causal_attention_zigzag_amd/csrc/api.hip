@@ -343,9 +343,9 @@ hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
   const int cus = device_cus();
-  size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true, 4);
+  size_t need = plan_fwd(f, desc->d, CPATTN_BF16, cus, true, 0);
   if (need > 0 && (workspace == nullptr || need > workspace_bytes))
-    need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false, 4);  // too small: no split
+    need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false, 0);  // too small: no split
   if (need > 0) assign_fwd_workspace(f, desc->d, workspace);
   return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, stream);
 }
@@ -382,7 +382,7 @@ size_t bwd_dq_split_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
   FwdArgs f{};
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);
-  return plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true, 4);
+  return plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), true, 0);
 }
 
 }  // namespace

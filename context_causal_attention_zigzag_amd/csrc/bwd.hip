@@ -73,67 +73,96 @@ struct DqExtra {
   float scale;         // softmax scale (factor of dS)
 };
 
-// One 64-key tile for one wave of the dQ pass.
+// One 64-key tile for one wave of the dQ pass, in four phases over the tile's key
+// halves A (keys 0..31) and B (32..63):
+//   S_A, dP_A;  S_B, dP_B beside dS_A;  dQ += K_A^T dS_A beside dS_B;  dQ += K_B^T dS_B,
+// so that the matrix core has independent work while the wave computes
+// dS = P (dP - D) scale with P = exp(S - LSE).  Operands are read two steps ahead.
 template <int D>
 __device__ __forceinline__ void dq_step(const bf16* __restrict__ ks, const bf16* __restrict__ vs,
                                         const int32_t* kpos, const int32_t* kdoc, int klen,
                                         const bf16x8 (&qf)[D / 16], const bf16x8 (&of)[D / 16],
                                         f32x16 (&dq)[D / 32], float lse2, float dl, int qpos, int qdoc,
                                         bool masked, int mask, float scale, float scale_log2, int lane) {
+  using namespace kv;
   constexpr int kKS = DqSmem<D>::kKS, kVS = DqSmem<D>::kVS;
+  constexpr int kSt = D / 16;   // stages of each middle phase
+  constexpr int kE = 16 / kSt;  // dS values per stage
+  static_assert(16 % kSt == 0 && kSt >= 4, "whole dS values per stage");
   const int r = lane & 31, h = lane >> 5;
+  const bf16* ka = ks + r * kKS + h * 8;
+  const bf16* va = vs + r * kVS + h * 8;
+  const bf16* kl = ks + tr_lane_offset<4>(lane, kKS);
+  auto row = [&](const bf16* base, int ds) { return *reinterpret_cast<const bf16x8*>(base + ds * 16); };
+  // K^T operand of product k of a dQ phase: dims 32 (k / 2) .., key slice (k % 2) of the half
+  auto ktr = [&](int half, int k) {
+    const bf16* p = kl + (2 * half + (k & 1)) * 16 * kKS + (k >> 1) * 32;
+    return concat(lds_read_tr4(p), lds_read_tr4(p + 8 * kKS));
+  };
   bf16x8 dsf[4];  // dS^T as B operands of the four 16-key slices
+  auto ds_val = [&](const f32x16& sv, const f32x16& pv, int i) {
+    const float p = fast_exp2(fmaf(sv[i], scale_log2, -lse2));
+    return (bf16)(p * (pv[i] - dl) * scale);
+  };
+
+  // S_A, dP_A
+  f32x16 sa = {}, pa = {}, sb = {}, pb = {};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 s = {}, dp = {};
+  for (int ds = 0; ds < kSt; ++ds) {
+    sa = mfma32x32x16(row(ka, ds), qf[ds], sa);
+    pa = mfma32x32x16(row(va, ds), of[ds], pa);
+  }
+  bf16x8 ko[2] = {row(ka + 32 * kKS, 0), row(ka + 32 * kKS, 1)};
+  bf16x8 vo[2] = {row(va + 32 * kVS, 0), row(va + 32 * kVS, 1)};
+  if (masked) mask_half(sa, kpos, kdoc, klen, qpos, qdoc, mask, h, 0);
+
+  // S_B, dP_B beside dS_A
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + r) * kKS + ds * 16 + h * 8);
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + (kb * 32 + r) * kVS + ds * 16 + h * 8);
-      s = mfma32x32x16(ak, qf[ds], s);
-      dp = mfma32x32x16(av, of[ds], dp);
+  for (int k = 0; k < kSt; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    sb = mfma32x32x16(ko[k & 1], qf[k], sb);
+    pb = mfma32x32x16(vo[k & 1], of[k], pb);
+    if (k + 2 < kSt) {
+      ko[k & 1] = row(ka + 32 * kKS, k + 2);
+      vo[k & 1] = row(va + 32 * kVS, k + 2);
+    } else {
+      ko[k & 1] = ktr(0, k + 2 - kSt);
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int base = kb * 32 + 8 * g + 4 * h;
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[4 * g + e], scale_log2, -lse2));
-      if (masked) {  // branch-free; the document image is ignored without documents
-        const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
-        const bool docm = mask == kMaskCausalDoc;
-        const int4 kp = *reinterpret_cast<const int4*>(kpos + base);
-        const int4 kd = *reinterpret_cast<const int4*>(kdoc + base);
-        const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
-        const int kda[4] = {kd.x, kd.y, kd.z, kd.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
-          p[e] = vis ? p[e] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int a = 4 * g + e;
-        dsf[kb * 2 + (a >> 3)][a & 7] = (bf16)(p[e] * (dp[a] - dl) * scale);
-      }
+    for (int e = 0; e < kE; ++e) {
+      const int i = k * kE + e;
+      dsf[i >> 3][i & 7] = ds_val(sa, pa, i);
     }
   }
-  // dQ^T += K^T dS^T: K^T slices by transposing reads in the rows order of dS^T
-  const bf16* kl = ks + tr_lane_offset<4>(lane, kKS);
+  asm volatile("" ::"v"(dsf[0]), "v"(dsf[1]));
+  __builtin_amdgcn_sched_barrier(0);
+  if (masked) mask_half(sb, kpos, kdoc, klen, qpos, qdoc, mask, h, 1);
+
+  // dQ += K_A^T dS_A beside dS_B
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int k = 0; k < kSt; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    dq[k >> 1] = mfma32x32x16(ko[k & 1], dsf[k & 1], dq[k >> 1]);
+    ko[k & 1] = k + 2 < kSt ? ktr(0, k + 2) : ktr(1, k + 2 - kSt);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16* p = kl + j * 16 * kKS + db * 32;
-      const bf16x8 a = concat(lds_read_tr4(p), lds_read_tr4(p + 8 * kKS));
-      dq[db] = mfma32x32x16(a, dsf[j], dq[db]);
+    for (int e = 0; e < kE; ++e) {
+      const int i = k * kE + e;
+      dsf[2 + (i >> 3)][i & 7] = ds_val(sb, pb, i);
     }
+  }
+  asm volatile("" ::"v"(dsf[2]), "v"(dsf[3]));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // dQ += K_B^T dS_B
+#pragma unroll
+  for (int k = 0; k < kSt; ++k) {
+    dq[k >> 1] = mfma32x32x16(ko[k & 1], dsf[2 + (k & 1)], dq[k >> 1]);
+    if (k + 2 < kSt) ko[k & 1] = ktr(1, k + 2);
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra x) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(FwdArgs a, DqExtra x) {
   using namespace kv;
   __shared__ DqSmem<D> sm;
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
@@ -145,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hpw = a.heads_per_wg;
-  const int qt_rows = (kv::kThreads / kWave) * kRowsPerWave / hpw;
+  const int qt_rows = NW * kRowsPerWave / hpw;
   const int n_qt = (job.len + qt_rows - 1) / qt_rows;
   const int nsplit = job.n_split;
   const int local = logical - job.wg_begin;
@@ -224,8 +253,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(FwdArgs a, DqExtra 
 
   using Sm = DqSmem<D>;
   const uint32_t rstride = (uint32_t)a.hkv * D;  // elements between consecutive keys
-  FillOffs<D, Sm> fo;
-  fo.init(wave, lane, rstride);
+  FillOffs<D, Sm, NW> fo;
+  fo.init(wave, lane);
   const bool doc = mask == kMaskCausalDoc;
   TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
   if (cur.seg >= 0) {
@@ -780,8 +809,9 @@ hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64
 hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* delta, float scale, int d,
                          hipStream_t stream) {
   FwdArgs f = args;
-  // work-groups as in the forward kernel
-  const int qt_rows = (kv::kThreads / kWave) * kv::kRowsPerWave / f.heads_per_wg;
+  // work-groups as in the forward kernel (wave count chosen by the plan)
+  const int nw = f.wg_waves == 8 ? 8 : 4;
+  const int qt_rows = nw * kv::kRowsPerWave / f.heads_per_wg;
   int total = 0;
   for (int j = 0; j < f.n_jobs; ++j) {
     f.jobs[j].wg_begin = total;
@@ -791,10 +821,18 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   f.total_wgs = total;
   f.padded_wgs = (total + 7) & ~7;
   const DqExtra x{dout, delta, scale};
-  if (d == 64)
-    hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(f.padded_wgs), dim3(kThreads), 0, stream, f, x);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(f.padded_wgs), dim3(kThreads), 0, stream, f, x);
+  const dim3 grid(f.padded_wgs), block(nw * kWave);
+  if (d == 64) {
+    if (nw == 8)
+      hipLaunchKernelGGL((bwd_dq_kernel<64, 8>), grid, block, 0, stream, f, x);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<64, 4>), grid, block, 0, stream, f, x);
+  } else {
+    if (nw == 8)
+      hipLaunchKernelGGL((bwd_dq_kernel<128, 8>), grid, block, 0, stream, f, x);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<128, 4>), grid, block, 0, stream, f, x);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int j = 0; j < f.n_jobs; ++j)

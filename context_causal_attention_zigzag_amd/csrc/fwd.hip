@@ -55,29 +55,6 @@ using FwdSmem = KvSmem<D, D + 8, D + 24>;
 // query tiles fill the CUs, 4 (two work-groups per CU) with KV splits for small ones.
 constexpr int wg_per_cu(int nw) { return nw == 8 ? 1 : 2; }
 
-// Visibility of this lane's 16 raw scores of key half kb (keys 32 kb .. 32 kb + 31) of
-// a partially visible tile (positions kp / documents kd in LDS, klen keys) for query
-// position qpos / document qdoc: invisible scores become -inf.  Branch-free (the
-// document image is read even when documents are off; its value is then ignored).
-__device__ __forceinline__ void mask_half(f32x16& x, const int32_t* kp, const int32_t* kd, int klen, int qpos,
-                                          int qdoc, int mask, int h, int kb) {
-  const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
-  const bool docm = mask == kMaskCausalDoc;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int base = kb * 32 + 8 * g + 4 * h;
-    const int4 kpv = *reinterpret_cast<const int4*>(kp + base);
-    const int4 kdv = *reinterpret_cast<const int4*>(kd + base);
-    const int kpa[4] = {kpv.x, kpv.y, kpv.z, kpv.w};
-    const int kda[4] = {kdv.x, kdv.y, kdv.z, kdv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
-      x[g * 4 + e] = vis ? x[g * 4 + e] : neg_inf();
-    }
-  }
-}
-
 // V^T operand of O^T += V^T P^T for dims 32 db .. 32 db + 31 and key slice j (keys
 // 16 j .. 16 j + 15 in the order of P^T's rows): two transposing reads of row-major V.
 template <int D>
@@ -308,7 +285,7 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
 
   const uint32_t rs = (uint32_t)a.hkv * D;  // elements between consecutive keys
   FillOffs<D, Sm, NW> fo;
-  fo.init(wave, lane, rs);
+  fo.init(wave, lane);
   TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
   if (cur.seg >= 0) {
     KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);

@@ -233,9 +233,32 @@ __device__ __forceinline__ KvTile iter_tile(const TileIter& it, TileRef r, int s
   return t;
 }
 
+// Visibility of this lane's 16 raw scores of key half kb (keys 32 kb .. 32 kb + 31) of
+// a partially visible tile (positions kp / documents kd in LDS, klen keys) for query
+// position qpos / document qdoc: invisible scores become -inf.  Branch-free (the
+// document image is read even when documents are off; its value is then ignored).
+__device__ __forceinline__ void mask_half(f32x16& x, const int32_t* kp, const int32_t* kd, int klen, int qpos,
+                                          int qdoc, int mask, int h, int kb) {
+  const int qp = mask == kMaskNone ? 0x7fffffff : qpos;
+  const bool docm = mask == kMaskCausalDoc;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int base = kb * 32 + 8 * g + 4 * h;
+    const int4 kpv = *reinterpret_cast<const int4*>(kp + base);
+    const int4 kdv = *reinterpret_cast<const int4*>(kd + base);
+    const int kpa[4] = {kpv.x, kpv.y, kpv.z, kpv.w};
+    const int kda[4] = {kdv.x, kdv.y, kdv.z, kdv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool vis = (base + e < klen) & (kpa[e] <= qp) & (!docm | (kda[e] == qdoc));
+      x[g * 4 + e] = vis ? x[g * 4 + e] : neg_inf();
+    }
+  }
+}
+
 // Direct global->LDS fill of one KV tile into a KvSmem image (see FillPlan for the
 // slot layout), from a resolved tile.  Per fill instruction each lane's source is a
-// fixed element offset (key row * row stride + column) clamped to
+// fixed element offset (key row * row stride + column), clamped to
 // last * stride + D - 8: rows up to the tile's last key stay exact, rows after it
 // (ragged tile) read the last chunk of key `last` (finite data; those keys are masked).
 template <int D, class Smem, int kWaves = 4>
@@ -247,21 +270,28 @@ struct FillOffs {
   static constexpr int kKPer = (kKInst + kWaves - 1) / kWaves;  // per wave
   static constexpr int kVPer = (kVInst + kWaves - 1) / kWaves;
   static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
-  uint32_t ko[kKPer], vo[kVPer];
+  static_assert(D <= 256, "column offsets fit a byte");
+  // per fill instruction, 16 bits: key row (bits 8..13) and element column (bits 0..7);
+  // two per register (the offset is formed at fill time: row * stride + column)
+  uint32_t kp[(kKPer + 1) / 2], vp[(kVPer + 1) / 2];
 
-  __device__ __forceinline__ void init(int wave, int lane, uint32_t rs) {
+  static __device__ __forceinline__ uint32_t entry(int slot, int slots) {
+    const int c = slot % slots;
+    return (uint32_t)min(slot / slots, kBK - 1) << 8 | (uint32_t)(c < D / 8 ? c * 8 : 0);
+  }
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int slot = kWave * (wave + kWaves * j) + lane;
-      const int c = slot % kKSlots;
-      ko[j] = (uint32_t)min(slot / kKSlots, kBK - 1) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
-    }
+    for (int j = 0; j < (kKPer + 1) / 2; ++j) kp[j] = 0;
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int slot = kWave * (wave + kWaves * j) + lane;
-      const int c = slot % kVSlots;
-      vo[j] = (uint32_t)min(slot / kVSlots, kBK - 1) * rs + (uint32_t)(c < D / 8 ? c * 8 : 0);
-    }
+    for (int j = 0; j < (kVPer + 1) / 2; ++j) vp[j] = 0;
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) kp[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kKSlots) << (16 * (j & 1));
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) vp[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kVSlots) << (16 * (j & 1));
+  }
+  static __device__ __forceinline__ uint32_t offset(const uint32_t* packed, int j, uint32_t rs) {
+    const uint32_t e = (packed[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    return __umul24(e >> 8, rs) + (e & 0xffu);
   }
 };
 
@@ -274,12 +304,12 @@ __device__ __forceinline__ void fill_tile(Smem& sm, int buf, const KvTile& t, ui
 #pragma unroll
   for (int j = 0; j < FO::kKPer; ++j) {
     const int jj = wave + kWaves * j;
-    if (jj < FO::kKInst) fill16_untracked(t.k + min(fo.ko[j], cap), kl + jj * kWave * 16);
+    if (jj < FO::kKInst) fill16_untracked(t.k + min(FO::offset(fo.kp, j, rs), cap), kl + jj * kWave * 16);
   }
 #pragma unroll
   for (int j = 0; j < FO::kVPer; ++j) {
     const int jj = wave + kWaves * j;
-    if (jj < FO::kVInst) fill16_untracked(t.v + min(fo.vo[j], cap), vl + jj * kWave * 16);
+    if (jj < FO::kVInst) fill16_untracked(t.v + min(FO::offset(fo.vp, j, rs), cap), vl + jj * kWave * 16);
   }
   if (wave == 0) fill4_untracked(t.pos + min(lane, t.last), lds_offset(sm.kpos[buf]));
   if (wave == 1 && doc) fill4_untracked(t.doc + min(lane, t.last), lds_offset(sm.kdoc[buf]));
