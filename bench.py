@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "context_causal_attention_zigzag_amd", "csrc")
 # kernel -> (source files it is built from, counter summary under profiles/)
 # timed call -> the kernel it launches (rocprofv3 names it with its template arguments)
 KERNEL_OF = {"partition": "partition_kernel", "merge": "merge_kernel<true>", "bwd_delta": "bwd_delta_kernel<{d}>",
-             "bwd_dkdv": "bwd_dkdv_kernel<{d}>", "tile_fwd": "fwd_bf16_kernel<{d}, ...>",
-             "stream_fwd": "fwd_bf16_kernel<{d}, ...>", "bwd_dq": "bwd_dq_kernel<{d}>"}
+             "bwd_dkdv": "bwd_dkdv_kernel<{d}, ...>", "tile_fwd": "fwd_bf16_kernel<{d}, ...>",
+             "stream_fwd": "fwd_bf16_kernel<{d}, ...>", "bwd_dq": "bwd_dq_kernel<{d}, ...>"}
 TRAFFIC = {"bwd_dkdv": (("bwd.hip", "kv_stream.h", "common.h"), "bwd_dkdv_kernel_{w}_traffic.txt")}
 
 
