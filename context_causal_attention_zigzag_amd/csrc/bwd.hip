@@ -588,9 +588,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   while (s + 1 < a.n_segs && a.seg_wg_begin[s + 1] <= logical) ++s;
   const SegDesc& sg = a.segs[s];
   const int n_kt = (sg.len + kBKV - 1) / kBKV;
+  const int n_pair = (n_kt + 1) / 2;
   const int local = logical - a.seg_wg_begin[s];
-  const int kvh = local / n_kt;
-  const int kt = local - kvh * n_kt;
+  const int kvh = local / n_pair;
+  const int jp = local - kvh * n_pair;
+  // a work-group takes key tiles jp and n_kt - 1 - jp of its segment in turn: under
+  // causal masking their visible query counts roughly add up to a constant (a zigzag
+  // segment's early tiles see the most queries, its late ones the fewest), so the
+  // work-groups carry even work
+  for (int pass = 0; pass < 2; ++pass) {
+  const int kt = pass == 0 ? jp : n_kt - 1 - jp;
+  if (pass == 1) {
+    if (kt <= jp) break;
+    // every wave is done with the LDS images of the first tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+  }
   const int k0 = kt * kBKV, k1 = min(sg.len, k0 + kBKV);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -788,6 +801,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   }
+  }  // key tile pass
 }
 
 }  // namespace
@@ -845,7 +859,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& args, int d, hipStream_t stream) {
   int total = 0;
   for (int s = 0; s < a.n_segs; ++s) {
     a.seg_wg_begin[s] = total;
-    total += ((a.segs[s].len + kBKV - 1) / kBKV) * a.hkv;
+    total += ((a.segs[s].len + kBKV - 1) / kBKV + 1) / 2 * a.hkv;  // pairs of key tiles
   }
   a.seg_wg_begin[a.n_segs] = total;
   a.total_wgs = total;
