@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   const bool row_ok = myrow < wr1;
   const int mask = a.mask;
 
-  const int qmin = job.pos[r0], qmax = job.pos[r1 - 1];
+  const int qmax = job.pos[r1 - 1];
   int qdmin = 0, qdmax = 0, wqdmin = 0, wqdmax = 0;
   if (mask == kMaskCausalDoc) {
     qdmin = job.doc[r0];
@@ -238,17 +238,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   // tiles of the walk, and per wave the skipped and the fully visible ones, from one
   // binary search per segment (kv_stream.h); the loop reads no segment table
   TileIter it;
-  it.mask_mode = nsplit > 1;
   iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax);
-  if (nsplit > 1) {
-    iter_init_masks(it, a, job, lane, qmin, qmax, qdmin, qdmax);
-    const int total = iter_count(it);
-    const int first = split * job.tiles_per_split;
-    if (first >= total) {  // nothing in this split: mark its partial empty
-      if (row_ok && (lane >> 5) == 0) flag_dst[(int64_t)myrow * a.hq + head] = neg_inf();
-      return;
-    }
-    iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
+  if (nsplit == 1) {
+    iter_walk_all(it, job);
+  } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
+    // nothing in this split: mark its partial empty
+    if (row_ok && (lane >> 5) == 0) flag_dst[(int64_t)myrow * a.hq + head] = neg_inf();
+    return;
   }
 
   using Sm = DqSmem<D>;
@@ -256,14 +252,14 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   FillOffs<D, Sm, NW> fo;
   fo.init(wave, lane);
   const bool doc = mask == kMaskCausalDoc;
-  TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
+  TileRef cur = iter_next(it, job, TileRef{-1, 0});
   if (cur.seg >= 0) {
     KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);
     fill_tile<D, Sm>(sm, 0, tc, rstride, doc, wave, lane, fo);
     fill_barrier();
     int buf = 0;
     while (true) {
-      const TileRef nxt = iter_next<true>(it, a, job, cur, 0, 0, 0, 0);
+      const TileRef nxt = iter_next(it, job, cur);
       KvTile tn = tc;
       if (nxt.seg >= 0) {
         tn = iter_tile(it, nxt, job.seg_begin, kvh, a.hkv, D);

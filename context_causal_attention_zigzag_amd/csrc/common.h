@@ -210,7 +210,6 @@ struct SegDesc {
   const int32_t* pos;
   const int32_t* doc;
   int32_t len;
-  int32_t tile_off;  // index of this segment's first KV tile in its job's tile sequence
 };
 
 struct JobDesc {

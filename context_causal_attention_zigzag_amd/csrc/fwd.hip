@@ -270,30 +270,26 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
   float* lse_dst = nsplit > 1 ? job.ws_lse + (int64_t)split * job.len * a.hq : job.lse;
 
   TileIter it;
-  it.mask_mode = nsplit > 1;
   iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax);
-  if (nsplit > 1) {
-    iter_init_masks(it, a, job, lane, job.pos[r0], qmax, qdmin, qdmax);
-    const int total = iter_count(it);
-    const int first = split * job.tiles_per_split;
-    if (first >= total) {  // nothing to do in this split: an empty partial state
-      if (row_ok && h == 0) lse_dst[(int64_t)myrow * a.hq + head] = neg_inf();
-      return;
-    }
-    iter_seek(it, first, min(total - first, job.tiles_per_split), job.seg_begin);
+  if (nsplit == 1) {
+    iter_walk_all(it, job);
+  } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
+    // nothing to do in this split: an empty partial state
+    if (row_ok && h == 0) lse_dst[(int64_t)myrow * a.hq + head] = neg_inf();
+    return;
   }
 
   const uint32_t rs = (uint32_t)a.hkv * D;  // elements between consecutive keys
   FillOffs<D, Sm, NW> fo;
   fo.init(wave, lane);
-  TileRef cur = iter_next<true>(it, a, job, TileRef{-1, 0}, 0, 0, 0, 0);
+  TileRef cur = iter_next(it, job, TileRef{-1, 0});
   if (cur.seg >= 0) {
     KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);
     fill_tile<D, Sm>(sm, 0, tc, rs, doc, wave, lane, fo);
     fill_barrier();
     int buf = 0;
     while (true) {
-      const TileRef nxt = iter_next<true>(it, a, job, cur, 0, 0, 0, 0);
+      const TileRef nxt = iter_next(it, job, cur);
       KvTile tn = tc;
       // the other buffer was released by every wave at the previous barrier
       if (nxt.seg >= 0) {
@@ -483,7 +479,7 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
   return hipGetLastError();
 }
 
-constexpr int kMaxSplitTiles = 256;   // tiles a split job may span (four ballot masks)
+constexpr int kMaxSplitTiles = 256;   // jobs longer than this carry enough work per query tile
 // 1024 keys per split at least: each split writes an fp32 partial output of its query
 // tile (4*d bytes per row) for 4*d flops per row and key, so shorter runs would turn
 // the kernel into a writer of partial states
@@ -504,10 +500,7 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
   for (int j = 0; j < a.n_jobs; ++j) {
     JobDesc& jb = a.jobs[j];
     int off = 0;
-    for (int s = jb.seg_begin; s < jb.seg_end; ++s) {
-      a.segs[s].tile_off = off;
-      off += (a.segs[s].len + kBK - 1) / kBK;
-    }
+    for (int s = jb.seg_begin; s < jb.seg_end; ++s) off += (a.segs[s].len + kBK - 1) / kBK;
     jb.n_tiles = off;
     jb.n_split = 1;
     jb.tiles_per_split = off;

@@ -34,93 +34,23 @@ struct KvSmem {
 };
 
 
-// Iterator over the KV tiles one work-group processes.  Scan mode: positions (and
-// documents) are non-decreasing inside a segment, so the tiles a query range can see
-// are one contiguous range per segment; lane s finds segment s's range once by binary
-// search (iter_init_ranges) and the walk itself touches no memory.  Mask mode (KV
-// split across work-groups) first classifies every tile of the job lane-parallel into
-// four 64-bit ballot masks over the job's tile sequence, then yields the visible tiles
-// of rank [first, first + count).
+// Iterator over the KV tiles one work-group processes.  Positions (and documents) are
+// non-decreasing inside a segment, so the tiles a query range can see are one
+// contiguous range per segment: lane s of each wave finds segment s's range once by
+// binary search (iter_init_lanes), together with a copy of the segment's descriptor,
+// and the walk then touches no memory: it reads both back with readlane.  A KV split
+// walks the visible tiles of rank [first, first + count) in the same order.
 struct TileIter {
-  bool mask_mode;
-  int rlo, rhi;  // scan mode, lane s: visible tiles [rlo, rhi) of segment seg_begin + s
-  // optional per-lane copy of the job's segment table (lane s: segment seg_begin + s),
-  // read back with readlane so that a tile loop issues no scalar memory loads, and
-  // that segment's visibility ranges for one wave's rows (iter_init_lanes)
-  uint32_t k_lo, k_hi, v_lo, v_hi, p_lo, p_hi, d_lo, d_hi;
-  int len, toff, wlo, whi, flo, fhi;
-  uint64_t v0, v1, v2, v3;
-  uint64_t m;   // unvisited bits of the current word
-  int w;        // current word
-  int left;     // tiles still to yield
-  int seg;      // segment of the last yielded tile
-  __device__ __forceinline__ uint64_t word(int i) const {
-    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
-  }
+  // lane s: segment seg_begin + s
+  int rlo, rhi;  // the work-group's visible tiles [rlo, rhi)
+  int wlo, whi;  // the tiles this wave computes [wlo, whi)
+  int flo, fhi;  // the whole tiles fully visible to every row of the wave [flo, fhi)
+  uint32_t k_lo, k_hi, v_lo, v_hi, p_lo, p_hi, d_lo, d_hi;  // descriptor pointers
+  int len;
+  // walk state (wave-uniform)
+  int seg0, tile0;  // first tile of the walk
+  int left;         // tiles still to yield
 };
-
-__device__ __forceinline__ void iter_init_masks(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
-                                                int qmin, int qmax, int qdmin, int qdmax) {
-  uint64_t v[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    bool vis = false;
-    const int g = 64 * w + lane;
-    if (64 * w < job.n_tiles) {
-      for (int s = job.seg_begin; s < job.seg_end; ++s) {
-        const int len = a.segs[s].len;
-        const int t = g - a.segs[s].tile_off;
-        if (t >= 0 && t * kBK < len) {
-          const int k0 = t * kBK, k1 = min(len, k0 + kBK) - 1;
-          const int32_t* pos = a.segs[s].pos;
-          int kdmin = 0, kdmax = 0;
-          if (a.mask == kMaskCausalDoc) {
-            kdmin = a.segs[s].doc[k0];
-            kdmax = a.segs[s].doc[k1];
-          }
-          vis = classify(a.mask, qmin, qmax, qdmin, qdmax, pos[k0], pos[k1], kdmin, kdmax) != kTileEmpty;
-        }
-      }
-    }
-    v[w] = __ballot(vis);
-  }
-  it.v0 = v[0];
-  it.v1 = v[1];
-  it.v2 = v[2];
-  it.v3 = v[3];
-}
-
-__device__ __forceinline__ void iter_init_ranges(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
-                                                 int qmin, int qmax, int qdmin, int qdmax) {
-  int lo = 0, hi = 0;
-  if (lane < job.seg_end - job.seg_begin) {
-    const SegDesc& sg = a.segs[job.seg_begin + lane];
-    const int nt = (sg.len + kBK - 1) / kBK;
-    hi = nt;
-    if (a.mask != kMaskNone && nt > 0) {
-      const bool docm = a.mask == kMaskCausalDoc;
-      // hi: first tile whose first key lies after the last query (or in a later document)
-      int l0 = 0, h0 = nt;
-      while (l0 < h0) {
-        const int t = (l0 + h0) >> 1;
-        const bool after = sg.pos[t * kBK] > qmax || (docm && sg.doc[t * kBK] > qdmax);
-        if (after) h0 = t; else l0 = t + 1;
-      }
-      hi = l0;
-      // lo: first tile whose last key is in the first query document or later
-      if (docm) {
-        int l1 = 0, h1 = hi;
-        while (l1 < h1) {
-          const int t = (l1 + h1) >> 1;
-          if (sg.doc[min(sg.len, t * kBK + kBK) - 1] >= qdmin) h1 = t; else l1 = t + 1;
-        }
-        lo = l1;
-      }
-    }
-  }
-  it.rlo = lo;
-  it.rhi = hi;
-}
 
 // Scan ranges, per-lane segment table and per-wave visibility ranges in one pass.
 // Lane s binary-searches segment seg_begin + s for six boundaries at once, each a
@@ -142,13 +72,12 @@ struct VisRanges {
 __device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
                                                 int qmax, int qdmin, int qdmax, bool wave_rows, int wqmin,
                                                 int wqmax, int wqdmin, int wqdmax) {
-  int len = 0, toff = 0;
+  int len = 0;
   uint64_t kp = 0, vp = 0, pp = 0, dp = 0;
   VisRanges r = {0, 0, 0, 0, 0, 0};
   if (lane < job.seg_end - job.seg_begin) {
     const SegDesc& sg = a.segs[job.seg_begin + lane];
     len = sg.len;
-    toff = sg.tile_off;
     kp = reinterpret_cast<uint64_t>(sg.k);
     vp = reinterpret_cast<uint64_t>(sg.v);
     pp = reinterpret_cast<uint64_t>(sg.pos);
@@ -191,7 +120,6 @@ __device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, 
   it.flo = r.flo;
   it.fhi = r.fhi;
   it.len = len;
-  it.toff = toff;
   it.k_lo = (uint32_t)kp;
   it.k_hi = (uint32_t)(kp >> 32);
   it.v_lo = (uint32_t)vp;
@@ -256,11 +184,14 @@ __device__ __forceinline__ void mask_half(f32x16& x, const int32_t* kp, const in
   }
 }
 
-// Direct global->LDS fill of one KV tile into a KvSmem image (see FillPlan for the
-// slot layout), from a resolved tile.  Per fill instruction each lane's source is a
-// fixed element offset (key row * row stride + column), clamped to
-// last * stride + D - 8: rows up to the tile's last key stay exact, rows after it
-// (ragged tile) read the last chunk of key `last` (finite data; those keys are masked).
+// Direct global->LDS fill of one KV tile into a KvSmem image, from a resolved tile.
+// The image is a sequence of 16-byte slots (row-major, kKS / 8 or kVS / 8 slots per
+// key row, the last ones padding); fill instruction jj of the work-group writes slots
+// 64 jj .. 64 jj + 63, lane l slot 64 jj + l.  Per fill instruction each lane's source
+// is a fixed element offset (key row * row stride + column; padding slots load a valid
+// dummy chunk), clamped to last * stride + D - 8: rows up to the tile's last key stay
+// exact, rows after it (ragged tile) read the last chunk of key `last` (finite data;
+// those keys are masked).
 template <int D, class Smem, int kWaves = 4>
 struct FillOffs {
   static constexpr int kKSlots = Smem::kKS / 8;
@@ -315,119 +246,45 @@ __device__ __forceinline__ void fill_tile(Smem& sm, int buf, const KvTile& t, ui
   if (wave == 1 && doc) fill4_untracked(t.doc + min(lane, t.last), lds_offset(sm.kdoc[buf]));
 }
 
-__device__ __forceinline__ int iter_count(const TileIter& it) {
-  return __popcll(it.v0) + __popcll(it.v1) + __popcll(it.v2) + __popcll(it.v3);
+// Walk every visible tile of the job.
+__device__ __forceinline__ void iter_walk_all(TileIter& it, const JobDesc& job) {
+  it.seg0 = job.seg_begin;
+  it.tile0 = __builtin_amdgcn_readlane(it.rlo, 0);
+  it.left = 0x7fffffff;
 }
 
-// Position the iterator before the visible tile of rank `first`, to yield `count`.
-__device__ __forceinline__ void iter_seek(TileIter& it, int first, int count, int seg_begin) {
-  int w = 0, rank = 0;
-  while (w < 3 && rank + __popcll(it.word(w)) <= first) {
-    rank += __popcll(it.word(w));
-    ++w;
-  }
-  uint64_t m = it.word(w);
-  for (; rank < first; ++rank) m &= m - 1;
-  it.w = w;
-  it.m = m;
-  it.left = count;
-  it.seg = seg_begin;
-}
-
-// kLanes: the per-lane segment table is loaded (iter_init_lanes); the walk then
-// reads no kernel arguments either.
-template <bool kLanes = false>
-__device__ __forceinline__ TileRef iter_next(TileIter& it, const FwdArgs& a, const JobDesc& job, TileRef prev,
-                                             int qmin, int qmax, int qdmin, int qdmax) {
-  if (!it.mask_mode) {
-    int s = prev.seg < 0 ? job.seg_begin : prev.seg;
-    int t = prev.seg < 0 ? __builtin_amdgcn_readlane(it.rlo, 0) : prev.tile + 1;
-    while (s < job.seg_end) {
-      if (t < __builtin_amdgcn_readlane(it.rhi, s - job.seg_begin)) return {s, t};
-      ++s;
-      if (s < job.seg_end) t = __builtin_amdgcn_readlane(it.rlo, s - job.seg_begin);
+// Walk the visible tiles of rank [first, first + count) (in segment, then tile order);
+// false when there are not more than `first` of them.
+__device__ __forceinline__ bool iter_walk_split(TileIter& it, const JobDesc& job, int first, int count) {
+  int before = 0;
+  for (int s = job.seg_begin; s < job.seg_end; ++s) {
+    const int lo = __builtin_amdgcn_readlane(it.rlo, s - job.seg_begin);
+    const int n = max(0, __builtin_amdgcn_readlane(it.rhi, s - job.seg_begin) - lo);
+    if (first < before + n) {
+      it.seg0 = s;
+      it.tile0 = lo + (first - before);
+      it.left = count;
+      return true;
     }
-    return {-1, 0};
+    before += n;
   }
+  return false;
+}
+
+// Next tile after `prev` ({-1, 0}: the first), or {-1, 0} at the end of the walk.
+__device__ __forceinline__ TileRef iter_next(TileIter& it, const JobDesc& job, TileRef prev) {
   if (it.left == 0) return {-1, 0};
-  while (it.m == 0) {
-    ++it.w;
-    it.m = it.word(it.w);
-  }
-  const int g = 64 * it.w + __builtin_ctzll(it.m);
-  it.m &= it.m - 1;
-  --it.left;
-  if (kLanes) {
-    while (it.seg + 1 < job.seg_end && __builtin_amdgcn_readlane(it.toff, it.seg + 1 - job.seg_begin) <= g) ++it.seg;
-    return {it.seg, g - __builtin_amdgcn_readlane(it.toff, it.seg - job.seg_begin)};
-  }
-  while (it.seg + 1 < job.seg_end && a.segs[it.seg + 1].tile_off <= g) ++it.seg;
-  return {it.seg, g - a.segs[it.seg].tile_off};
-}
-
-// Direct global->LDS fill of one KV tile.  The tile's LDS image is a sequence of
-// 16-byte slots (row-major, kKS/8 or kVS/8 slots per key row, the last ones padding);
-// fill instruction jj of the work-group writes slots 64*jj .. 64*jj+63, lane l slot
-// 64*jj + l.  Each lane's (key row, column) per instruction is fixed for the kernel;
-// padding slots load a valid dummy chunk and key rows past a ragged tile's end are
-// clamped to its last key (those keys are masked).
-template <int D, class Smem>
-struct FillPlan {
-  static constexpr int kKSlots = Smem::kKS / 8;
-  static constexpr int kVSlots = Smem::kVS / 8;
-  static constexpr int kKInst = kBK * kKSlots / kWave;
-  static constexpr int kVInst = kBK * kVSlots / kWave;
-  static constexpr int kKPer = (kKInst + 3) / 4;  // per wave (4 waves)
-  static constexpr int kVPer = (kVInst + 3) / 4;
-  static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
-  // per fill instruction: key row in the high half, element column in the low half
-  uint32_t kslot[kKPer], vslot[kVPer];
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
-      const int c = slot % kKSlots;
-      kslot[j] = (uint32_t)(slot / kKSlots) << 16 | (uint32_t)(c < D / 8 ? c * 8 : 0);
+  int s = prev.seg < 0 ? it.seg0 : prev.seg;
+  int t = prev.seg < 0 ? it.tile0 : prev.tile + 1;
+  while (s < job.seg_end) {
+    if (t < __builtin_amdgcn_readlane(it.rhi, s - job.seg_begin)) {
+      --it.left;
+      return {s, t};
     }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int slot = kWave * (wave + 4 * j) + lane;
-      const int c = slot % kVSlots;
-      vslot[j] = (uint32_t)(slot / kVSlots) << 16 | (uint32_t)(c < D / 8 ? c * 8 : 0);
-    }
+    ++s;
+    if (s < job.seg_end) t = __builtin_amdgcn_readlane(it.rlo, s - job.seg_begin);
   }
-};
-
-template <int D, class Smem>
-__device__ __forceinline__ void fill_tile(Smem& sm, int buf, const SegDesc& sg, int tile, int kvh,
-                                          int hkv, int mask, int wave, int lane, const FillPlan<D, Smem>& fp) {
-  using FP = FillPlan<D, Smem>;
-  const int k0 = tile * kBK;
-  const int last = min(kBK, sg.len - k0) - 1;
-  const uint32_t rs = (uint32_t)hkv * D;  // elements between consecutive keys
-  const bf16* kb = reinterpret_cast<const bf16*>(sg.k) + ((int64_t)k0 * hkv + kvh) * D;
-  const bf16* vb = reinterpret_cast<const bf16*>(sg.v) + ((int64_t)k0 * hkv + kvh) * D;
-  char* kl = reinterpret_cast<char*>(sm.k[buf]);
-  char* vl = reinterpret_cast<char*>(sm.v[buf]);
-#pragma unroll
-  for (int j = 0; j < FP::kKPer; ++j) {
-    const int jj = wave + 4 * j;
-    if (jj < FP::kKInst) {
-      const uint32_t row = min(fp.kslot[j] >> 16, (uint32_t)last);
-      global_to_lds16(kb + row * rs + (fp.kslot[j] & 0xffffu), kl + jj * kWave * 16);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < FP::kVPer; ++j) {
-    const int jj = wave + 4 * j;
-    if (jj < FP::kVInst) {
-      const uint32_t row = min(fp.vslot[j] >> 16, (uint32_t)last);
-      global_to_lds16(vb + row * rs + (fp.vslot[j] & 0xffffu), vl + jj * kWave * 16);
-    }
-  }
-  if (wave == 0) global_to_lds4(sg.pos + k0 + min(lane, last), sm.kpos[buf]);
-  if (wave == 1 && mask == kMaskCausalDoc) global_to_lds4(sg.doc + k0 + min(lane, last), sm.kdoc[buf]);
+  return {-1, 0};
 }
 
 }  // namespace kv
