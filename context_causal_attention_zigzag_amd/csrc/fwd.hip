@@ -490,12 +490,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// KV-split plan.  A launch needs on the order of two rounds of resident work-groups
-// (wg_per_cu of the chosen size per compute unit) to fill the chip; when the query
-// tiles alone give fewer, each job's visible KV tiles are cut into splits of tiles_per_split tiles so that
-// the expected number of busy work-groups (causal: about half of a job's tiles are
-// visible to an average query tile) reaches that target.  Jobs spanning more than
-// 256 KV tiles are never split (they already carry enough work per query tile).
+// KV-split plan.  When the query tiles alone give fewer work-groups than the chip
+// holds at once (wg_per_cu of the chosen size per compute unit), each job's visible KV
+// tiles are cut into splits of tiles_per_split tiles, sized so that the busy
+// work-groups fit one round: a query tile with V visible tiles takes ceil(V / u)
+// work-groups, about V / u + 1/2, and under causal masking an average query tile sees
+// about half of its job's tiles, so u = (sum of V) / (slots - query tiles / 2).  Jobs
+// spanning more than 256 KV tiles are never split (they carry enough work per query
+// tile).
 size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int waves) {
   for (int j = 0; j < a.n_jobs; ++j) {
     JobDesc& jb = a.jobs[j];
@@ -518,13 +520,19 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
   a.wg_waves = waves;
   if (dtype != 0 || !allow_split) return 0;
   const int64_t base = query_wgs(waves);
-  const int64_t target = 2LL * wg_per_cu(waves) * num_cu;
-  if (base == 0 || base >= target) return 0;
+  const int64_t slots = (int64_t)wg_per_cu(waves) * num_cu;
+  if (base == 0 || base >= slots) return 0;
+  const int qt_rows = waves * kRowsPerWave / hpw;
+  int64_t visible = 0;  // expected visible (query tile, KV tile) pairs over all work-groups
+  for (int j = 0; j < a.n_jobs; ++j)
+    visible += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw) * a.jobs[j].n_tiles / 2;
+  const int64_t room = slots - base / 2;
+  const int64_t u_all = (visible + room - 1) / room;
   size_t bytes = 0;
   for (int j = 0; j < a.n_jobs; ++j) {
     JobDesc& jb = a.jobs[j];
     if (jb.n_tiles > kMaxSplitTiles || jb.n_tiles < 2 * kMinTilesPerSplit) continue;
-    int64_t u = (base * jb.n_tiles + 2 * target - 1) / (2 * target);
+    int64_t u = u_all;
     if (u < kMinTilesPerSplit) u = kMinTilesPerSplit;
     int ns = (int)((jb.n_tiles + u - 1) / u);
     if (ns > kMaxSplits) {
