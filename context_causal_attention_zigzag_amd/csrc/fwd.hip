@@ -531,7 +531,7 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
   size_t bytes = 0;
   for (int j = 0; j < a.n_jobs; ++j) {
     JobDesc& jb = a.jobs[j];
-    if (jb.n_tiles > kMaxSplitTiles || jb.n_tiles < 2 * kMinTilesPerSplit) continue;
+    if (jb.n_tiles > kMaxSplitTiles || jb.n_tiles <= 2 * kMinTilesPerSplit) continue;
     int64_t u = u_all;
     if (u < kMinTilesPerSplit) u = kMinTilesPerSplit;
     int ns = (int)((jb.n_tiles + u - 1) / u);
