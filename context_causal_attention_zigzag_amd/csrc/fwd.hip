@@ -102,7 +102,9 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   if (masked) mask_half(sa, kpos, kdoc, klen, qpos, qdoc, mask, h, 0);
   float mu = (m == neg_inf()) ? 0.0f : m;
 
-  // S_B beside P_A
+  // S_B beside P_A (at raised wave priority: the two middle phases feed the matrix core
+  // while the other wave of the SIMD is in a phase without contractions)
+  __builtin_amdgcn_s_setprio(1);
   bf16x8 pf[4];
   float rs = 0.0f, mta = neg_inf();
 #pragma unroll
@@ -122,6 +124,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   // keep P_A in its phase (it is used only after the branches below)
   asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(rs), "v"(mta));
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   if (masked) mask_half(sb, kpos, kdoc, klen, qpos, qdoc, mask, h, 1);
   mta = half_max(mta) * scale_log2;  // -inf stays -inf (scale > 0)
   if (__any(mta > m + kTau)) {
@@ -150,6 +153,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   l += rs;
 
   // O += V_A P_A beside P_B
+  __builtin_amdgcn_s_setprio(1);
   float mtb = neg_inf();
   rs = 0.0f;
 #pragma unroll
@@ -168,6 +172,7 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   }
   asm volatile("" ::"v"(pf[2]), "v"(pf[3]), "v"(rs), "v"(mtb));
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   mtb = half_max(mtb) * scale_log2;
   if (__any(mtb > m + kTau)) {
     // the maximum moved in half B: O (with the products of half A, in the old scale)
