@@ -5,8 +5,10 @@
 // Calls are asynchronous on the given stream and keep no state between calls.
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "../../include/cpattn.h"
+
 #include "common.h"
 
 using namespace cpattn;
@@ -79,7 +81,13 @@ size_t bwd_delta_bytes(const cpattn_attn_desc* desc, int64_t q_len) {
 }
 
 // Compute units of the current device (256 when no device is visible, for planning).
+// Compute units the launch plans assume: the device's, unless CPATTN_NUM_CUS names a
+// positive count (tests use a small count to reach the eight-wave plans on small shapes).
 int device_cus() {
+  if (const char* e = getenv("CPATTN_NUM_CUS")) {
+    const int v = atoi(e);
+    if (v > 0) return v;
+  }
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;

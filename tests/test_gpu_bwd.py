@@ -115,6 +115,17 @@ def test_bwd_small_shapes_and_owner_sums(seq, cp, hq, hkv, d):
     assert_close(dv_sum, dv_f, TOL_BF16, f"bwd{seq} owner-summed dV")
 
 
+def test_bwd_eight_wave_plans(monkeypatch):
+    # plans for 2 compute units: the dQ pass runs its eight-wave work-groups
+    monkeypatch.setenv("CPATTN_NUM_CUS", "2")
+    q = workloads.randn((800, 4, 128), 24, "bf16", 0)
+    k = workloads.randn((800, 2, 128), 24, "bf16", 1)
+    v = workloads.randn((800, 2, 128), 24, "bf16", 2)
+    g = workloads.randn((800, 4, 128), 24, "bf16", 3)
+    for r in range(4):
+        check_bwd("bwd8w", q, k, v, g, 4, r)
+
+
 def test_bwd_packed_small():
     lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520]
     cu = workloads.cu_seqlens_from_lengths(lengths)

@@ -81,6 +81,37 @@ def test_small_shapes(seq, cp, hq, hkv, d, dtype):
         check_share(f"small{seq}x{hq}/{hkv}x{d}{dtype}", q, k, v, cp, r)
 
 
+@pytest.fixture
+def few_cus(monkeypatch):
+    """Plans computed for 2 compute units: query tiles alone fill them, so the bf16
+    kernels run their eight-wave work-groups (the ping-pong forward step) on small shapes."""
+    monkeypatch.setenv("CPATTN_NUM_CUS", "2")
+
+
+@pytest.mark.parametrize("seq,cp,hq,hkv,d", [
+    (800, 4, 4, 2, 128),   # ragged query and key tiles, GQA group 2
+    (512, 2, 8, 1, 64),    # d=64, 8 query heads on one kv head
+    (384, 2, 12, 4, 128),  # group 3
+])
+def test_small_shapes_eight_wave(few_cus, seq, cp, hq, hkv, d):
+    q = workloads.randn((seq, hq, d), 14, "bf16", 0)
+    k = workloads.randn((seq, hkv, d), 14, "bf16", 1)
+    v = workloads.randn((seq, hkv, d), 14, "bf16", 2)
+    for r in range(cp):
+        check_share(f"small8w{seq}x{hq}/{hkv}x{d}", q, k, v, cp, r)
+
+
+def test_packed_documents_eight_wave(few_cus):
+    lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520]
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    q = workloads.randn((total, 4, 128), 15, "bf16", 0)
+    k = workloads.randn((total, 2, 128), 15, "bf16", 1)
+    v = workloads.randn((total, 2, 128), 15, "bf16", 2)
+    for r in range(2):
+        check_share("packed8w", q, k, v, 2, r, cu=cu, granularities=("owner",))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_packed_documents_small(dtype):
     lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520]
