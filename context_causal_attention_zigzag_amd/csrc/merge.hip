@@ -27,6 +27,75 @@ struct MergeArgs {
   int32_t d;
 };
 
+// One thread's 4-float slice of the merge of n parts, in one pass over the parts with
+// a running maximum (the same sums as the definition, rescaled as the maximum grows).
+// Parts are taken kU at a time with all their loads issued before any is used; a part's
+// O slice is loaded whatever its LSE and discarded when the LSE is -inf (its memory is
+// in bounds but may never have been written).  SUM: the plain sum of the parts whose
+// LSE is not -inf.
+template <bool SUM, class L, class O>
+__device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse_out) {
+  constexpr int kU = 4;
+  float m = neg_inf(), s = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < n; p0 += kU) {
+    float lv[kU];
+    f32x4 ov[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = min(p0 + u, n - 1);
+      lv[u] = p0 + u < n ? lse_of(p) : neg_inf();
+      ov[u] = o_of(p);
+    }
+    if (SUM) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (lv[u] != neg_inf()) acc += ov[u];
+      continue;
+    }
+    float bm = lv[0];
+#pragma unroll
+    for (int u = 1; u < kU; ++u) bm = fmaxf(bm, lv[u]);
+    const float m_new = fmaxf(m, bm);
+    if (m_new == neg_inf()) continue;
+    const float c = fast_exp2((m - m_new) * kLog2e);  // 0 while m is -inf
+    s *= c;
+    acc *= c;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool live = lv[u] != neg_inf();
+      const float w = live ? fast_exp2((lv[u] - m_new) * kLog2e) : 0.0f;
+      s += w;
+      if (live) acc += w * ov[u];
+    }
+    m = m_new;
+  }
+  if (SUM) {
+    lse_out = 0.0f;
+    return acc;
+  }
+  if (!(s > 0.0f)) {
+    lse_out = neg_inf();
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  lse_out = m + fast_log2(s) * kLn2;
+  return acc * (1.0f / s);
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_slice(void* o, int64_t off, f32x4 v) {
+  if (OUT_BF16) {
+    bf16x4 r;
+    r[0] = (bf16)v[0];
+    r[1] = (bf16)v[1];
+    r[2] = (bf16)v[2];
+    r[3] = (bf16)v[3];
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(o) + off) = r;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + off) = v;
+  }
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int tpp = a.d >> 2;  // threads per (row, head) pair
@@ -34,34 +103,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int64_t pair = gid / tpp;
   const int c = (int)(gid - pair * tpp);
   if (pair >= a.pairs) return;
-
-  float mx = neg_inf();
-  for (int j = 0; j < a.n; ++j) mx = fmaxf(mx, a.lse[j][pair]);
   const int64_t off = pair * a.d + 4 * c;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lse = neg_inf();
-  if (mx != neg_inf()) {
-    float sum = 0.f;
-    for (int j = 0; j < a.n; ++j) sum += fast_exp2((a.lse[j][pair] - mx) * kLog2e);
-    lse = mx + fast_log2(sum) * kLn2;
-    for (int j = 0; j < a.n; ++j) {
-      const float lj = a.lse[j][pair];
-      if (lj == neg_inf()) continue;
-      const float w = fast_exp2((lj - lse) * kLog2e);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.o[j] + off);
-      acc += w * v;
-    }
-  }
-  if (OUT_BF16) {
-    bf16x4 r;
-    r[0] = (bf16)acc[0];
-    r[1] = (bf16)acc[1];
-    r[2] = (bf16)acc[2];
-    r[3] = (bf16)acc[3];
-    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o_out) + off) = r;
-  } else {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o_out) + off) = acc;
-  }
+  float lse;
+  const f32x4 v = merge_slice<false>(
+      a.n, [&](int j) { return a.lse[j][pair]; },
+      [&](int j) { return *reinterpret_cast<const f32x4*>(a.o[j] + off); }, lse);
+  store_slice<OUT_BF16>(a.o_out, off, v);
   if (c == 0) a.lse_out[pair] = lse;
 }
 
@@ -93,38 +140,18 @@ __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
   const int64_t stride = a.pair_begin[j + 1] - a.pair_begin[j];  // len * hq
   const int n = a.n[j];
   const float* lp = a.ws_lse[j] + pair;
+  const float* op = a.ws_o[j] + pair * a.d + 4 * c;
+  const int64_t ostride = stride * a.d;
+  float lse;
+  const f32x4 v = merge_slice<SUM>(
+      n, [&](int p) { return lp[p * stride]; },
+      [&](int p) { return *reinterpret_cast<const f32x4*>(op + p * ostride); }, lse);
   const int64_t off = pair * a.d + 4 * c;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (SUM) {
-    for (int p = 0; p < n; ++p)
-      if (lp[p * stride] != neg_inf()) acc += *reinterpret_cast<const f32x4*>(a.ws_o[j] + p * stride * a.d + off);
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o[j]) + off) = acc;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o[j]) + off) = v;
     return;
   }
-  float mx = neg_inf();
-  for (int p = 0; p < n; ++p) mx = fmaxf(mx, lp[p * stride]);
-  float lse = neg_inf();
-  if (mx != neg_inf()) {
-    float sum = 0.f;
-    for (int p = 0; p < n; ++p) sum += fast_exp2((lp[p * stride] - mx) * kLog2e);
-    lse = mx + fast_log2(sum) * kLn2;
-    for (int p = 0; p < n; ++p) {
-      const float lj = lp[p * stride];
-      if (lj == neg_inf()) continue;
-      const float w = fast_exp2((lj - lse) * kLog2e);
-      acc += w * *reinterpret_cast<const f32x4*>(a.ws_o[j] + p * stride * a.d + off);
-    }
-  }
-  if (OUT_BF16) {
-    bf16x4 r;
-    r[0] = (bf16)acc[0];
-    r[1] = (bf16)acc[1];
-    r[2] = (bf16)acc[2];
-    r[3] = (bf16)acc[3];
-    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o[j]) + off) = r;
-  } else {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o[j]) + off) = acc;
-  }
+  store_slice<OUT_BF16>(a.o[j], off, v);
   if (c == 0) a.lse[j][pair] = lse;
 }
 
