@@ -55,58 +55,51 @@ __device__ __forceinline__ void local_to_global(const PartArgs& a, int64_t t, in
   docid = lo;
 }
 
-// grid.y selects the tensor (or, with no tensors, only the index output); every
-// thread moves kVecPerThread 16-byte vectors of one destination row segment.
+// grid.y selects the tensor (or, with no tensors, only the index output).  A block
+// moves kVecPerThread * kThreads consecutive 16-byte vectors of the destination; thread
+// k takes vectors k, k + kThreads, ..., so every load and store instruction of a wave
+// covers 1 KiB of consecutive destination bytes (and of source bytes within a row).
 __global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
   const int g = blockIdx.y;
   const int vpr = a.n_gather > 0 ? a.vpr[g] : 1;
   const int64_t nvec = a.local * vpr;
-  const int64_t v0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVecPerThread;
-  if (v0 >= nvec) return;
-  int64_t row;
-  int32_t d;
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kVecPerThread + threadIdx.x;
   if (a.n_gather == 0) {  // indices only: one row per vector
-    for (int i = 0; i < kVecPerThread && v0 + i < nvec; ++i) {
-      local_to_global(a, v0 + i, row, d);
-      a.idx[v0 + i] = (int32_t)row;
-      if (a.doc) a.doc[v0 + i] = d;
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int64_t t = base + (int64_t)i * kThreads;
+      if (t >= nvec) break;
+      int64_t row;
+      int32_t d;
+      local_to_global(a, t, row, d);
+      a.idx[t] = (int32_t)row;
+      if (a.doc) a.doc[t] = d;
     }
     return;
   }
   const u32x4* src = reinterpret_cast<const u32x4*>(a.src[g]);
   u32x4* dst = reinterpret_cast<u32x4*>(a.dst[g]);
-  int64_t t = v0 / vpr;
-  int c = (int)(v0 - t * vpr);
-  local_to_global(a, t, row, d);
-  if (g == 0 && c == 0) {
-    a.idx[t] = (int32_t)row;
-    if (a.doc) a.doc[t] = d;
-  }
   u32x4 buf[kVecPerThread];
-  int64_t drow[kVecPerThread];
-  int cc[kVecPerThread];
-  int n = 0;
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
-    if (v0 + i >= nvec) break;
-    if (c == vpr) {  // next destination row
-      ++t;
-      c = 0;
-      local_to_global(a, t, row, d);
-      if (g == 0) {
-        a.idx[t] = (int32_t)row;
-        if (a.doc) a.doc[t] = d;
-      }
+    const int64_t v = base + (int64_t)i * kThreads;
+    if (v >= nvec) break;
+    const int64_t t = v / vpr;
+    const int c = (int)(v - t * vpr);
+    int64_t row;
+    int32_t d;
+    local_to_global(a, t, row, d);
+    if (g == 0 && c == 0) {
+      a.idx[t] = (int32_t)row;
+      if (a.doc) a.doc[t] = d;
     }
-    drow[i] = t;
-    cc[i] = c;
     buf[i] = __builtin_nontemporal_load(&src[row * vpr + c]);
-    ++c;
-    ++n;
   }
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i)
-    if (i < n) dst[drow[i] * vpr + cc[i]] = buf[i];
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const int64_t v = base + (int64_t)i * kThreads;
+    if (v < nvec) dst[v] = buf[i];
+  }
 }
 
 }  // namespace
