@@ -390,15 +390,19 @@ __device__ __forceinline__ void fill_qtile(DkdvSmem<D>& sm, RowSmem& rsm, int bu
   const int64_t base = ((int64_t)r0 * a.hq + head) * D;
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + base;
   const bf16* ob = reinterpret_cast<const bf16*>(a.dout) + base;
+  // byte offsets of every fill first, each in its own register, then the burst
+  uint32_t offs[Sm::kBigPer];
+#pragma unroll
+  for (int j = 0; j < Sm::kBigPer; ++j) offs[j] = (min(fp.slot[j] >> 16, last) * rs + (fp.slot[j] & 0xffffu)) * 2;
 #pragma unroll
   for (int j = 0; j < Sm::kBigPer; ++j) {
     const int jj = wave + 4 * j;
     const bool isq = jj < Sm::kTileInst;
-    const uint32_t row = min(fp.slot[j] >> 16, last);
-    const bf16* src = (isq ? qb : ob) + (row * rs + (fp.slot[j] & 0xffffu));
     const uint32_t dst = lds_offset(isq ? sm.qs[buf] : sm.dos[buf]) + (isq ? jj : jj - Sm::kTileInst) * kWave * 16;
-    fill16_untracked(src, dst);
+    fill16_off(isq ? qb : ob, offs[j], dst);
   }
+#pragma unroll
+  for (int j = 0; j < Sm::kBigPer; ++j) asm volatile("" ::"v"(offs[j]));
   // per-row values: wave 1 positions (lanes 0..31) and document ids (32..63), the
   // others log-sum-exp (0..31) and delta (32..63) (identical data)
   const int q = r0 + (int)min((uint32_t)(lane & 31), last);
@@ -717,26 +721,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int b1 = b0 == kQBufs - 1 ? 0 : b0 + 1;
       const int b2 = b1 == kQBufs - 1 ? 0 : b1 + 1;
       const int b3 = b2 == kQBufs - 1 ? 0 : b2 + 1;
+      // this iteration's LDS reads first (tile i's row values and range, the first
+      // operands of tiles i+1 and i-1): their latency then overlaps the fill issue
+      RowVals<DOC> rv;
+      load_rows<DOC>(rs, b0, h, rv);
+      RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
+      TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
+      const QRange q = qrange(rs, cur.qt);
+      __builtin_amdgcn_sched_barrier(0);
       // fill of tile i+3 (its buffers held tile i-2, released at the last barrier)
       const bool issued = nf.hh >= 0;
       if (issued) fill_qtile<D, DOC>(sm, rs, b3, a, fp, nf, kvh, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
       int kpos_eff = kpos_mask;
       {
-        const QRange q = qrange(rs, cur.qt);
         const int cls = classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, wkmin, wkmax, wkdmin, wkdmax);
         // fully visible tiles skip the position test (ragged tiles never count as full)
         if (wave_keys && cls == kTileFull && wk1 - wk0 == 32 && a.q_len - cur.qt * kBQ >= kBQ)
           kpos_eff = INT32_MIN + 1;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      RowVals<DOC> rv;
-      load_rows<DOC>(rs, b0, h, rv);
       // S / dP of tile i, computed last iteration
       f32x16 scur = sv, dpcur = dpv;
       asm volatile("" : "+v"(scur), "+v"(dpcur));
       bf16x8 pf[2], dsf[2];
-      RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
-      TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
       sv = f32x16{};
       dpv = f32x16{};
       // stage k: the contractions of pair k and the operand reads of pair k + 2 (stage

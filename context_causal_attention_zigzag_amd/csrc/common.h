@@ -118,6 +118,17 @@ __device__ __forceinline__ void fill16_untracked(const void* g, uint32_t lds_off
                : "s"(lds_off), "v"(g)
                : "memory", "m0");
 }
+// The same from base + off: base wave-uniform (scalar registers), off a per-lane byte
+// offset.  Callers compute the offsets of a burst of fills into distinct registers
+// before issuing any: an instruction that overwrites the address register of a fill
+// still waiting for the memory pipeline to read it stalls until that read, which
+// serialises a burst that reuses one register.
+__device__ __forceinline__ void fill16_off(const void* base, uint32_t off, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(off), "s"(base)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void fill4_untracked(const void* g, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
