@@ -133,9 +133,12 @@ def test_forward_workspace_plan():
     qbig = qb(8192)
     assert C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(big), ctypes.byref(qbig), 4, segs) == 0
     assert C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(desc(dtype=C.F32)), ctypes.byref(q), 4, segs) == 0
+    # edges of 64 KV tiles are split; edges of 32 tiles or fewer never are
     qa = (C.cpattn_q_block * 2)(qb(1024), qb(1024))
-    sa = (C.cpattn_kv_seg * 2)(sg(2048), sg(2048))
+    sa = (C.cpattn_kv_seg * 2)(sg(4096), sg(4096))
     assert C.lib.cpattn_tile_fwd_workspace_bytes(ctypes.byref(d), 2, qa, sa) > 0
+    sa32 = (C.cpattn_kv_seg * 2)(sg(2048), sg(2048))
+    assert C.lib.cpattn_tile_fwd_workspace_bytes(ctypes.byref(d), 2, qa, sa32) == 0
 
 
 def test_bwd_validation_and_workspace():
