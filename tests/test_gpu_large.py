@@ -1,6 +1,8 @@
 """Full-size workloads in the launch configuration the benchmark times, checked on
 sampled rows against the oracle (which evaluates those rows against every key), and
-the two forward forms checked against each other on every row."""
+the two forward forms checked against each other on every row.  The 128K backward is
+checked on sampled query rows (dQ) and, for dK / dV, through two identities of the
+softmax Jacobian that hold at any size."""
 import numpy as np
 import pytest
 import torch
@@ -9,6 +11,7 @@ from context_causal_attention_zigzag_amd.rank_share import build_rank_share
 import oracle
 import workloads
 from gpu_common import (DEV, TOL_BF16, TOL_LSE_BF16, assert_close, oracle_fwd_rows, say)
+from oracle import attention as OA
 
 pytestmark = pytest.mark.gpu
 
@@ -77,3 +80,45 @@ def test_thd64k_rank1_sampled():
     assert_close(o2[li], o_ref, TOL_BF16, "thd64k tile O (sampled)")
     assert_close(o2, o.float(), TOL_BF16, "thd64k tile vs stream O (all rows)")
     assert_close(l2, lse, TOL_LSE_BF16, "thd64k tile vs stream LSE (all rows)")
+
+
+def test_s128k_rank0_bwd_sampled():
+    w = workloads.WORKLOADS["s128k"]
+    say("s128k bwd: generating inputs")
+    q, k, v = workloads.full_qkv(w)
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), w.cp, 0)
+    n = rs.q.shape[0]
+    g = workloads.randn((n, w.hq, w.d), w.seed, "bf16", 3)
+    say("s128k bwd: stream forward + backward (chunk segments, as timed)")
+    o, lse = rs.stream_fwd("chunk")
+    dq, dk, dv = rs.bwd(o, lse, g.to(DEV), granularity="chunk")
+    torch.cuda.synchronize()
+    # dQ of sampled rows: the oracle runs those rows' own forward and backward over
+    # every key
+    local = sample_local_rows(n, 13, 5)
+    rows = rs.q_idx.cpu().numpy()[local]
+    say(f"s128k bwd: oracle dQ on {len(local)} rows")
+    dq_r, _, _ = OA.attention_bwd(q[torch.as_tensor(rows)], k, v, g[torch.as_tensor(local)], rows,
+                                  np.arange(w.seq))
+    assert_close(dq[torch.as_tensor(local, device=DEV)], dq_r, TOL_BF16, "s128k dQ (sampled)")
+    # Every visible row's probabilities sum to 1, so the dV rows of all keys of a kv
+    # head sum to the upstream gradient summed over the local rows and the head's query
+    # group.  The kernels round P to bf16 (relative error <= 2^-9 per probability, of
+    # either sign), which moves a row's sum by at most 2^-9; over the rows these errors
+    # add like a random walk, so each element may differ by 3 * 2^-9 * sqrt(sum G^2).
+    grp = w.hq // w.hkv
+    g64 = g.double().reshape(n, w.hkv, grp, w.d)
+    g_sum = g64.sum((0, 2))
+    dv_tol = 3 * 2.0 ** -9 * g64.pow(2).sum((0, 2)).sqrt()
+    dv_sum = sum(x.double().sum(0) for x in dv).cpu()
+    dv_excess = float(((dv_sum - g_sum).abs() - dv_tol).max())
+    # Every row of dS sums to 0 except for D, which uses O rounded to bf16: per row
+    # G.(O - bf16(O)) is at most 2^-9 |G||O|; times the scale and the row's q, summed
+    # over the rows like a random walk, that is far below 0.5 (the sums of wrong dK
+    # rows are of the order of sqrt(rows) = 256).
+    dk_sum = sum(x.double().sum(0) for x in dk).cpu()
+    dk_max = float(dk_sum.abs().max())
+    say(f"s128k bwd: sum dV vs sum G max err {float((dv_sum - g_sum).abs().max()):.3e} "
+        f"(tolerance >= {float(dv_tol.min()):.3f}); |sum dK| max {dk_max:.3e}")
+    assert dv_excess <= 0.0, dv_excess
+    assert dk_max <= 0.5, dk_max
