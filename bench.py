@@ -13,7 +13,11 @@ zigzag rank; forward 4*d per pair per head (QK^T and PV), backward 10*d (five
 contractions).  value = useful FLOPs of the step (two forwards + one backward) / time.
 The backward runs as its three calls (delta, dQ, dK/dV) so each is timed on its own.
 
-Prints one JSON line (rank 0).  ``--workload s128k`` runs the 128K share instead.
+Prints one JSON line (rank 0).  ``--workload s128k`` runs the 128K share instead;
+``--workload thd64k`` a packed stream of 65536 tokens in documents of lognormal
+lengths, split per document (zigzag inside each document, cp=4, rank 1 by default),
+with the document mask; its visible pairs are counted per row from the partition's
+position and document outputs.
 ``--copy-mib N`` only runs a plain device copy of N MiB (``--steps`` times): the
 known-size reference that calibrates the FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -83,8 +87,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="s8k", choices=["s8k", "s128k"])
-    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--workload", default="s8k", choices=["s8k", "s128k", "thd64k"])
+    ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0)
     args = ap.parse_args()
@@ -106,11 +110,14 @@ def main():
 
     dev = "cuda"
     w = workloads.WORKLOADS[args.workload]
-    r = args.rank
+    r = w.ranks[0] if args.rank is None else args.rank
     q, k, v = workloads.full_qkv(w)
     gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
-    gran = "owner" if args.workload == "s8k" else "chunk"
-    rs = build_rank_share(gq, gk, gv, w.cp, r)
+    gran = w.kv_granularity
+    cu = workloads.cu_seqlens_from_lengths(workloads.thd_lengths(w.seed)) if w.packed else None
+    cu_dev = torch.as_tensor(cu, dtype=torch.int32, device=dev) if w.packed else None
+    part_mode = C.PART_THD if w.packed else C.PART_ZIGZAG
+    rs = build_rank_share(gq, gk, gv, w.cp, r, cu)
     n_local = w.seq // w.cp
     g = workloads.randn((n_local, w.hq, w.d), 5, "bf16", 3).to(dev)
     edges, parts = rs.alloc_tile_buffers(gran)
@@ -128,6 +135,7 @@ def main():
     ws_stream = rs.stream_workspace(gran)
     # partition outputs of this rank (Q and its own K/V shard), rewritten every step
     p_idx = torch.empty(n_local, dtype=torch.int32, device=dev)
+    p_doc = torch.empty(n_local, dtype=torch.int32, device=dev) if w.packed else None
     p_out = [torch.empty((n_local,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in (gq, gk, gv)]
 
     names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
@@ -143,7 +151,7 @@ def main():
                 marks.append(e)
 
         mark()
-        C.cpattn_partition(C.PART_ZIGZAG, w.seq, w.cp, r, p_idx, None, [gq, gk, gv], p_out)
+        C.cpattn_partition(part_mode, w.seq, w.cp, r, p_idx, p_doc, [gq, gk, gv], p_out, cu, cu_dev)
         mark()
         rs.tile_fwd(edges, parts, workspace=ws_tile)
         mark()
@@ -173,7 +181,13 @@ def main():
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
     step_ms = sum(ms.values())
     bwd_ms = ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"]
-    pairs = w.seq * (w.seq + 1) // (2 * w.cp)
+    if w.packed:
+        # a row at position p of a document starting at c sees p - c + 1 keys
+        pos = rs.q_idx.cpu().numpy().astype(np.int64)
+        start = np.asarray(cu, dtype=np.int64)[rs.q_doc.cpu().numpy()]
+        pairs = int(np.sum(pos - start + 1))
+    else:
+        pairs = w.seq * (w.seq + 1) // (2 * w.cp)
     unit = w.d * w.hq * pairs            # (visible pair, head, head-dim element) units
     f_fwd = 4.0 * unit
     f_bwd = 10.0 * unit
@@ -182,7 +196,7 @@ def main():
     gbs = lambda b, t_ms: b / (t_ms * 1e-3) / 1e9  # noqa: E731
     # algorithmic bytes of the bandwidth-bound steps
     elt = 2
-    part_bytes = 2 * n_local * (w.hq + 2 * w.hkv) * w.d * elt + 4 * n_local
+    part_bytes = 2 * n_local * (w.hq + 2 * w.hkv) * w.d * elt + 4 * n_local * (1 + w.packed)
     n_parts = [sum(1 for e in edges if e[0] == ch) for ch in rs.q_chunks()]
     merge_bytes = sum(n * (n_local // 2) * w.hq * (w.d * 4 + 4) for n in n_parts) + n_local * w.hq * (w.d * elt + 4)
     delta_bytes = n_local * w.hq * (2 * w.d * elt + 4)
@@ -211,6 +225,8 @@ def main():
     _, bound, work = calls[dom]
     peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
     achieved = tflops(work, ms[dom]) if bound == "mfma" else gbs(work, ms[dom])
+    share = (f"packed-document ({len(cu) - 1} documents, per-document zigzag)" if w.packed
+             else "zigzag")
     out = {
         "metric": "causal attn TFLOP/s per rank-share (fwd, bwd) at 1 MI355X; % bf16 MFMA peak",
         "value": round(tflops(step_flops, step_ms), 3),
@@ -225,7 +241,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: one zigzag rank share, S={w.seq}, cp={w.cp}, rank={r}, "
+        "config": {"workload": f"{args.workload}: one {share} rank share, S={w.seq}, cp={w.cp}, rank={r}, "
                                f"Hq={w.hq}, Hkv={w.hkv}, d={w.d}, bf16; KV segments in ring order",
                    "seq_len": w.seq, "cp": w.cp, "rank": r, "hq": w.hq, "hkv": w.hkv, "d": w.d,
                    "visible_pairs_per_head": pairs},
@@ -240,15 +256,16 @@ def main():
                      "algorithmic": work},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(q, k, v, w, r)
+        out["cpu_baseline"] = cpu_baseline(q, k, v, w, r, cu)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(q, k, v, w, r, min_seconds=12.0, max_reps=8):
+def cpu_baseline(q, k, v, w, r, cu=None, min_seconds=12.0, max_reps=8):
     """The float64 oracle, as it stands, on a bounded sample of the same share: forward and
     backward of the rank's query rows against all keys, repeated until about
     ``min_seconds`` of CPU work (the 8K share is small); for larger shares an evenly
-    spaced subset of the rows, sized for one repetition of about that length."""
+    spaced subset of the rows, sized for one repetition of about that length.  A packed
+    share passes every row's and key's document id with the document mask."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -256,21 +273,28 @@ def cpu_baseline(q, k, v, w, r, min_seconds=12.0, max_reps=8):
     import oracle
     from oracle import attention as OA
 
-    rows = oracle.zigzag_indices(w.seq, w.cp, r)
+    rows = oracle.thd_indices(cu, w.cp, r) if w.packed else oracle.zigzag_indices(w.seq, w.cp, r)
     if w.seq > 8192:
         rows = rows[:: max(1, len(rows) // 64)]
     g = torch.randn((len(rows), w.hq, w.d), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
     qr = q[torch.as_tensor(rows)]
     keys = np.arange(w.seq)
+    docs = {}
+    if w.packed:
+        docs = {"q_doc": oracle.thd_doc_ids(cu, rows), "k_doc": oracle.thd_doc_ids(cu, keys),
+                "mask": OA.MASK_CAUSAL_DOC}
     reps, t0 = 0, time.perf_counter()
     while True:
-        OA.attention_fwd(qr, k, v, rows, keys)
-        OA.attention_bwd(qr, k, v, g, rows, keys)
+        OA.attention_fwd(qr, k, v, rows, keys, **docs)
+        OA.attention_bwd(qr, k, v, g, rows, keys, **docs)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps or w.seq > 8192:
             break
-    pairs = int(np.sum(rows + 1))
+    if w.packed:
+        pairs = int(np.sum(rows - np.asarray(cu, dtype=np.int64)[docs["q_doc"]] + 1))
+    else:
+        pairs = int(np.sum(rows + 1))
     flops = reps * (4.0 + 10.0) * w.d * w.hq * pairs
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",

@@ -161,27 +161,22 @@ __device__ __forceinline__ void dq_step(const bf16* __restrict__ ks, const bf16*
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(FwdArgs a, DqExtra x) {
   using namespace kv;
   __shared__ DqSmem<D> sm;
-  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
-  if (logical >= a.total_wgs) return;
-  int j = 0;
-  while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
-  const JobDesc& job = a.jobs[j];
+  static_assert(sizeof(sm) >= (kMaxRankedTiles + 1) * sizeof(int), "ranking scratch");
+  const int hpw = a.heads_per_wg;
+  const int qt_rows = NW * kRowsPerWave / hpw;
+  const WorkItem wi = RANKED ? ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm))
+                             : indexed_work_item(a, qt_rows);
+  if (wi.job < 0) return;
+  const JobDesc& job = a.jobs[wi.job];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hpw = a.heads_per_wg;
-  const int qt_rows = NW * kRowsPerWave / hpw;
-  const int n_qt = (job.len + qt_rows - 1) / qt_rows;
   const int nsplit = job.n_split;
-  const int local = logical - job.wg_begin;
-  const int split = local % nsplit;
-  const int rest = local / nsplit;
-  const int hg = rest / n_qt;
-  const int qt = n_qt - 1 - (rest - hg * n_qt);
+  const int split = wi.split, hg = wi.hg, qt = wi.qt;
   const int r0 = qt * qt_rows, r1 = min(job.len, r0 + qt_rows);
   const int head = hg * hpw + wave % hpw;
   const int kvh = (hg * hpw) / a.group;
@@ -823,6 +818,14 @@ hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64
   return hipGetLastError();
 }
 
+template <int D, int NW>
+void launch_dq(bool ranked, dim3 grid, dim3 block, hipStream_t stream, const FwdArgs& f, const DqExtra& x) {
+  if (ranked)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), grid, block, 0, stream, f, x);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), grid, block, 0, stream, f, x);
+}
+
 hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* delta, float scale, int d,
                          hipStream_t stream) {
   FwdArgs f = args;
@@ -839,16 +842,17 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   f.padded_wgs = (total + 7) & ~7;
   const DqExtra x{dout, delta, scale};
   const dim3 grid(f.padded_wgs), block(nw * kWave);
+  const bool ranked = kv::ranked_plan(f, qt_rows);
   if (d == 64) {
     if (nw == 8)
-      hipLaunchKernelGGL((bwd_dq_kernel<64, 8>), grid, block, 0, stream, f, x);
+      launch_dq<64, 8>(ranked, grid, block, stream, f, x);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<64, 4>), grid, block, 0, stream, f, x);
+      launch_dq<64, 4>(ranked, grid, block, stream, f, x);
   } else {
     if (nw == 8)
-      hipLaunchKernelGGL((bwd_dq_kernel<128, 8>), grid, block, 0, stream, f, x);
+      launch_dq<128, 8>(ranked, grid, block, stream, f, x);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<128, 4>), grid, block, 0, stream, f, x);
+      launch_dq<128, 4>(ranked, grid, block, stream, f, x);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

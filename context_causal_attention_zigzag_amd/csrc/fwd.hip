@@ -203,28 +203,23 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ ks, const bf1
   }
 }
 
-template <int D, bool PARTIAL_OUT, int NW>
+template <int D, bool PARTIAL_OUT, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(FwdArgs a) {
   using Sm = FwdSmem<D>;
   __shared__ Sm sm;
-  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
-  if (logical >= a.total_wgs) return;
-  int j = 0;
-  while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
-  const JobDesc& job = a.jobs[j];
+  static_assert(sizeof(Sm) >= (kMaxRankedTiles + 1) * sizeof(int), "ranking scratch");
+  const int hpw = a.heads_per_wg;
+  const int qt_rows = NW * kRowsPerWave / hpw;
+  const WorkItem wi = RANKED ? ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm))
+                             : indexed_work_item(a, qt_rows);
+  if (wi.job < 0) return;
+  const JobDesc& job = a.jobs[wi.job];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
-  const int hpw = a.heads_per_wg;
-  const int qt_rows = NW * kRowsPerWave / hpw;
-  const int n_qt = (job.len + qt_rows - 1) / qt_rows;
   const int nsplit = job.n_split;
-  const int local = logical - job.wg_begin;
-  const int split = local % nsplit;
-  const int rest = local / nsplit;
-  const int hg = rest / n_qt;
-  const int qt = n_qt - 1 - (rest - hg * n_qt);  // heaviest (latest) query tiles first
+  const int split = wi.split, hg = wi.hg, qt = wi.qt;
   const int r0 = qt * qt_rows, r1 = min(job.len, r0 + qt_rows);
   const int head = hg * hpw + wave % hpw;
   const int kvh = (hg * hpw) / a.group;
@@ -434,6 +429,14 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdArgs a) {
   job.lse[(int64_t)row * a.hq + head] = live ? m + logf(l) : neg_inf();
 }
 
+template <int D, bool PARTIAL_OUT, int NW>
+void launch_fwd_bf16(bool ranked, dim3 grid, dim3 block, hipStream_t stream, const FwdArgs& a) {
+  if (ranked)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, PARTIAL_OUT, NW, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, PARTIAL_OUT, NW, false>), grid, block, 0, stream, a);
+}
+
 template <int D>
 hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t stream) {
   if (dtype == 0) {
@@ -450,16 +453,17 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
     a.padded_wgs = (total + 7) & ~7;
     if (total == 0) return hipSuccess;
     const dim3 grid(a.padded_wgs), block(nw * kWave);
+    const bool ranked = ranked_plan(a, qt_rows);
     if (nw == 8) {
       if (partial_out)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 8>), grid, block, 0, stream, a);
+        launch_fwd_bf16<D, true, 8>(ranked, grid, block, stream, a);
       else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 8>), grid, block, 0, stream, a);
+        launch_fwd_bf16<D, false, 8>(ranked, grid, block, stream, a);
     } else {
       if (partial_out)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4>), grid, block, 0, stream, a);
+        launch_fwd_bf16<D, true, 4>(ranked, grid, block, stream, a);
       else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 4>), grid, block, 0, stream, a);
+        launch_fwd_bf16<D, false, 4>(ranked, grid, block, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -287,5 +287,136 @@ __device__ __forceinline__ TileRef iter_next(TileIter& it, const JobDesc& job, T
   return {-1, 0};
 }
 
+// ---------------------------------------------------------------------------
+// Work-group -> work item (job, head group, query tile, KV split).
+struct WorkItem {
+  int job, hg, qt, split;
+};
+
+// Index order.  The launch hands each XCD one contiguous logical range (xcd_remap) and
+// each XCD's dispatcher starts its work-groups in logical order as CUs free up.  Inside
+// a job the head groups are outermost and the query tiles run latest first: in a
+// causal zigzag share the later tiles see more keys, so every XCD starts its heaviest
+// tiles first.  job = -1: a padding work-group.
+__device__ __forceinline__ WorkItem indexed_work_item(const FwdArgs& a, int qt_rows) {
+  WorkItem w{-1, 0, 0, 0};
+  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
+  if (logical >= a.total_wgs) return w;
+  int j = 0;
+  while (j + 1 < a.n_jobs && a.jobs[j + 1].wg_begin <= logical) ++j;
+  const JobDesc& job = a.jobs[j];
+  const int n_qt = (job.len + qt_rows - 1) / qt_rows;
+  const int nsplit = job.n_split;
+  const int local = logical - job.wg_begin;
+  w.job = j;
+  w.split = local % nsplit;
+  const int rest = local / nsplit;
+  w.hg = rest / n_qt;
+  w.qt = n_qt - 1 - (rest - w.hg * n_qt);
+  return w;
+}
+
+// Ranked order, for packed documents: a query tile's work follows the lengths of the
+// documents it falls in, not its index.
+constexpr int kMaxRankedTiles = 1024;
+
+// The launch ranks when the head groups split evenly over the 8 XCDs, no job has KV
+// splits and the jobs hold 1..kMaxRankedTiles query tiles in all; then every logical
+// work item is one (head group, job, query tile) and the grid needs no padding.
+inline bool ranked_plan(const FwdArgs& a, int qt_rows) {
+  if (a.mask != kMaskCausalDoc || (a.hq / a.heads_per_wg) % 8 != 0) return false;
+  int n_all = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    if (a.jobs[j].n_split != 1) return false;
+    n_all += (a.jobs[j].len + qt_rows - 1) / qt_rows;
+  }
+  return n_all > 0 && n_all <= kMaxRankedTiles;
+}
+
+// KV tiles the work-group of query rows [r0, r1) walks in one segment: from the first
+// tile that reaches the rows' first document to the first tile past their last
+// position or document (the boundaries the tile iterators find for the work-group).
+__device__ __forceinline__ int seg_walk_tiles(const SegDesc& sg, int qmax, int qdmin, int qdmax) {
+  const int len = sg.len, nt = (len + kBK - 1) / kBK;
+  int l0 = 0, h0 = nt, l1 = 0, h1 = nt;
+  while (l0 < h0 || l1 < h1) {
+    const int m0 = (l0 + h0) >> 1, m1 = (l1 + h1) >> 1;
+    if (l0 < h0) {
+      if (sg.pos[m0 * kBK] > qmax || sg.doc[m0 * kBK] > qdmax) h0 = m0; else l0 = m0 + 1;
+    }
+    if (l1 < h1) {
+      if (sg.doc[min(len, m1 * kBK + kBK) - 1] >= qdmin) h1 = m1; else l1 = m1 + 1;
+    }
+  }
+  return max(0, l0 - l1);
+}
+
+// Work-group b runs on XCD b % 8, which takes head groups [x*hpx, (x+1)*hpx) of every
+// job, hpx = head groups / 8.  Every work-group counts, for every query tile of every
+// job, the KV tiles that tile's work-group walks, ranks the (job, tile) pairs by that
+// count (most first; ties: the later pair first) and takes the pair of rank (b / 8) /
+// hpx, head group (b / 8) % hpx of its XCD's block: each XCD's list is then the
+// longest-processing-time-first schedule of its share, its head groups inner.  Every
+// thread of the work-group calls this; scratch holds kMaxRankedTiles + 1 ints of LDS
+// that nothing else uses yet.
+template <int NT>
+__device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_rows, int* scratch) {
+  const int b = blockIdx.x;
+  const int hpx = (a.hq / a.heads_per_wg) >> 3;
+  const int i = b >> 3;
+  const int rank = i / hpx;
+  WorkItem w;
+  w.split = 0;
+  w.hg = (b & 7) * hpx + (i - rank * hpx);
+  const int tid = threadIdx.x;
+  int n_all = 0, n_pairs = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    n_all += n_qt;
+    n_pairs += n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
+  }
+  for (int t = tid; t < n_all; t += NT) scratch[t] = 0;
+  __syncthreads();
+  // one (job, query tile, segment) search per thread, all jobs at once
+  for (int k = tid; k < n_pairs; k += NT) {
+    int j = 0, kk = k, base = 0;
+    while (true) {
+      const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+      const int n = n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
+      if (kk < n) break;
+      kk -= n;
+      base += n_qt;
+      ++j;
+    }
+    const JobDesc& job = a.jobs[j];
+    const int n_seg = job.seg_end - job.seg_begin;
+    const int q = kk / n_seg, s = kk - q * n_seg;
+    const int r0 = q * qt_rows, r1 = min(job.len, r0 + qt_rows);
+    const int c = seg_walk_tiles(a.segs[job.seg_begin + s], job.pos[r1 - 1], job.doc[r0], job.doc[r1 - 1]);
+    if (c) atomicAdd(&scratch[base + q], c);
+  }
+  __syncthreads();
+  for (int t = tid; t < n_all; t += NT) {
+    const int c = scratch[t];
+    int r = 0;
+    for (int p = 0; p < n_all; ++p) {
+      const int cp = scratch[p];
+      r += (cp > c) | ((cp == c) & (p > t));
+    }
+    if (r == rank) scratch[n_all] = t;
+  }
+  __syncthreads();
+  int t = scratch[n_all];
+  __syncthreads();  // scratch free again
+  int j = 0;
+  while (t >= (a.jobs[j].len + qt_rows - 1) / qt_rows) {
+    t -= (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    ++j;
+  }
+  w.job = j;
+  w.qt = t;
+  return w;
+}
+
 }  // namespace kv
 }  // namespace cpattn

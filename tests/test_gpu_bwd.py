@@ -138,6 +138,19 @@ def test_bwd_packed_small():
         check_bwd("bwd-packed", q, k, v, g, 2, r, cu)
 
 
+def test_bwd_packed_ranked_order():
+    # eight head groups: the dQ launch orders query tiles by the KV tiles they walk
+    lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520, 1024, 40, 4, 300]
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    q = workloads.randn((total, 8, 128), 23, "bf16", 0)
+    k = workloads.randn((total, 8, 128), 23, "bf16", 1)
+    v = workloads.randn((total, 8, 128), 23, "bf16", 2)
+    g = workloads.randn((total, 8, 128), 23, "bf16", 3)
+    for r in range(2):
+        check_bwd("bwd-ranked", q, k, v, g, 2, r, cu)
+
+
 def test_bwd_fully_masked_rows_give_zero_gradients():
     import context_causal_attention_zigzag_amd as C
     tq, tk, h, d = 40, 64, 2, 128

@@ -112,6 +112,34 @@ def test_packed_documents_eight_wave(few_cus):
         check_share("packed8w", q, k, v, 2, r, cu=cu, granularities=("owner",))
 
 
+# Head groups divisible by 8 with the document mask: the bf16 launches order the query
+# tiles by the KV tiles their work-groups walk (each XCD takes a block of head groups
+# of every job).  Documents of mixed lengths, ragged against the 64-key and 128/256-row
+# tiles, and an empty one.
+RANKED_LENGTHS = [8, 64, 136, 0, 16, 256, 8, 32, 520, 1024, 40, 4, 300]
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 8, 64), (16, 16, 128)])
+def test_packed_documents_ranked_order(hq, hkv, d):
+    cu = workloads.cu_seqlens_from_lengths(RANKED_LENGTHS)
+    total = int(cu[-1])
+    q = workloads.randn((total, hq, d), 16, "bf16", 0)
+    k = workloads.randn((total, hkv, d), 16, "bf16", 1)
+    v = workloads.randn((total, hkv, d), 16, "bf16", 2)
+    for r in range(2):
+        check_share(f"ranked{hq}/{hkv}x{d}", q, k, v, 2, r, cu=cu, granularities=("owner", "chunk"))
+
+
+def test_packed_documents_ranked_order_eight_wave(few_cus):
+    cu = workloads.cu_seqlens_from_lengths(RANKED_LENGTHS)
+    total = int(cu[-1])
+    q = workloads.randn((total, 8, 128), 17, "bf16", 0)
+    k = workloads.randn((total, 8, 128), 17, "bf16", 1)
+    v = workloads.randn((total, 8, 128), 17, "bf16", 2)
+    for r in range(2):
+        check_share("ranked8w", q, k, v, 2, r, cu=cu, granularities=("owner",))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_packed_documents_small(dtype):
     lengths = [8, 64, 136, 0, 16, 256, 8, 32, 520]
