@@ -3,7 +3,7 @@
 // "Context Parallelism (CP)", section 2.2: for one query row,
 //   L = log sum_j exp(L_j),   O = sum_j exp(L_j - L) O_j,
 // valid in any order and grouping.  Parts with L_j = -inf (no visible key) carry no
-// weight and their O_j is not read; a row whose parts are all -inf becomes (0, -inf).
+// weight; a row whose parts are all -inf becomes (0, -inf).
 //
 // Bandwidth-bound: each (row, head) pair is handled by d/4 threads that each own a
 // 16-byte slice of the head vector, so the n partial outputs stream through in
@@ -29,13 +29,15 @@ struct MergeArgs {
 
 // One thread's 4-float slice of the merge of n parts, in one pass over the parts with
 // a running maximum (the same sums as the definition, rescaled as the maximum grows).
-// Parts are taken kU at a time with all their loads issued before any is used; a part's
-// O slice is loaded whatever its LSE and discarded when the LSE is -inf (its memory is
-// in bounds but may never have been written).  SUM: the plain sum of the parts whose
-// LSE is not -inf.
-template <bool SUM, class L, class O>
+// Parts are taken kU at a time.  Eager (LAZY false): the LSE and O loads of a group are
+// issued together, one memory round trip per group, and a part's O slice is loaded
+// whatever its LSE and discarded when the LSE is -inf (its memory is in bounds but may
+// never have been written) -- for edge partials, which are nearly all live.  LAZY: the
+// group's LSEs first, then only the O slices of live parts, two round trips per group
+// -- for KV-split partials, where the splits past a light query tile's visible keys
+// are empty.  SUM: the plain sum of the parts whose LSE is not -inf.
+template <bool SUM, int kU, bool LAZY, class L, class O>
 __device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse_out) {
-  constexpr int kU = 4;
   float m = neg_inf(), s = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < n; p0 += kU) {
@@ -45,7 +47,12 @@ __device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse
     for (int u = 0; u < kU; ++u) {
       const int p = min(p0 + u, n - 1);
       lv[u] = p0 + u < n ? lse_of(p) : neg_inf();
-      ov[u] = o_of(p);
+      if (!LAZY) ov[u] = o_of(p);
+    }
+    if (LAZY) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        ov[u] = lv[u] != neg_inf() ? o_of(min(p0 + u, n - 1)) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (SUM) {
 #pragma unroll
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (pair >= a.pairs) return;
   const int64_t off = pair * a.d + 4 * c;
   float lse;
-  const f32x4 v = merge_slice<false>(
+  const f32x4 v = merge_slice<false, 4, false>(
       a.n, [&](int j) { return a.lse[j][pair]; },
       [&](int j) { return *reinterpret_cast<const f32x4*>(a.o[j] + off); }, lse);
   store_slice<OUT_BF16>(a.o_out, off, v);
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
   const float* op = a.ws_o[j] + pair * a.d + 4 * c;
   const int64_t ostride = stride * a.d;
   float lse;
-  const f32x4 v = merge_slice<SUM>(
+  const f32x4 v = merge_slice<SUM, 8, true>(
       n, [&](int p) { return lp[p * stride]; },
       [&](int p) { return *reinterpret_cast<const f32x4*>(op + p * ostride); }, lse);
   const int64_t off = pair * a.d + 4 * c;
