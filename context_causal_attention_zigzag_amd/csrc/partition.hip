@@ -39,11 +39,12 @@ __device__ __forceinline__ void local_to_global(const PartArgs& a, int64_t t, in
   int64_t start = 0, len = a.total;
   int lo = 0;
   if (a.cu != nullptr) {
-    // largest k with cu[k]/cp <= t (cu[n_docs]/cp == local > t)
+    // largest k with cu[k]/cp <= t, i.e. cu[k] <= (t+1)*cp - 1 (cu[n_docs]/cp == local > t)
+    const int64_t lim = (t + 1) * a.cp - 1;
     int hi = a.n_docs;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if ((int64_t)a.cu[mid] / a.cp <= t) lo = mid; else hi = mid;
+      if ((int64_t)a.cu[mid] <= lim) lo = mid; else hi = mid;
     }
     start = a.cu[lo];
     len = (int64_t)a.cu[lo + 1] - start;
@@ -56,49 +57,55 @@ __device__ __forceinline__ void local_to_global(const PartArgs& a, int64_t t, in
 }
 
 // grid.y selects the tensor (or, with no tensors, only the index output).  A block
-// moves kVecPerThread * kThreads consecutive 16-byte vectors of the destination; thread
-// k takes vectors k, k + kThreads, ..., so every load and store instruction of a wave
-// covers 1 KiB of consecutive destination bytes (and of source bytes within a row).
+// moves kPerBlock consecutive 16-byte vectors of the destination; thread k takes
+// vectors k, k + kThreads, ..., so every load and store instruction of a wave covers
+// 1 KiB of consecutive destination bytes (and of source bytes within a row).  The
+// block's local rows (at most kPerBlock + 1) are mapped to global rows once, into LDS,
+// by one thread each; that thread also writes the index and document outputs when the
+// row's first vector belongs to the block (tensor 0 only).
+constexpr int kPerBlock = kThreads * kVecPerThread;
+
 __global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
+  __shared__ int64_t rows[kPerBlock + 1];
   const int g = blockIdx.y;
   const int vpr = a.n_gather > 0 ? a.vpr[g] : 1;
   const int64_t nvec = a.local * vpr;
-  const int64_t base = (int64_t)blockIdx.x * kThreads * kVecPerThread + threadIdx.x;
-  if (a.n_gather == 0) {  // indices only: one row per vector
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-      const int64_t t = base + (int64_t)i * kThreads;
-      if (t >= nvec) break;
-      int64_t row;
-      int32_t d;
-      local_to_global(a, t, row, d);
-      a.idx[t] = (int32_t)row;
-      if (a.doc) a.doc[t] = d;
-    }
-    return;
-  }
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.src[g]);
-  u32x4* dst = reinterpret_cast<u32x4*>(a.dst[g]);
-  u32x4 buf[kVecPerThread];
-#pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
-    const int64_t v = base + (int64_t)i * kThreads;
-    if (v >= nvec) break;
-    const int64_t t = v / vpr;
-    const int c = (int)(v - t * vpr);
+  const int64_t v0 = (int64_t)blockIdx.x * kPerBlock;
+  if (v0 >= nvec) return;  // a smaller tensor than the grid is sized for
+  const int64_t vlast = min(nvec, v0 + kPerBlock) - 1;
+  const int64_t t0 = v0 / vpr;
+  const int nrows = (int)(vlast / vpr - t0 + 1);
+  for (int i = threadIdx.x; i < nrows; i += kThreads) {
+    const int64_t t = t0 + i;
     int64_t row;
     int32_t d;
     local_to_global(a, t, row, d);
-    if (g == 0 && c == 0) {
+    rows[i] = row;
+    if (g == 0 && t * vpr >= v0) {
       a.idx[t] = (int32_t)row;
       if (a.doc) a.doc[t] = d;
     }
-    buf[i] = __builtin_nontemporal_load(&src[row * vpr + c]);
+  }
+  if (a.n_gather == 0) return;
+  __syncthreads();
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.src[g]);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.dst[g]);
+  // vector v lies in local row t0 + w / vpr, column w % vpr, with w = v - t0*vpr
+  // (w < vpr + kPerBlock, so 32-bit arithmetic suffices)
+  const uint32_t w0 = (uint32_t)(v0 - t0 * vpr) + threadIdx.x;
+  u32x4 buf[kVecPerThread];
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i) {
+    if (v0 + threadIdx.x + (int64_t)i * kThreads > vlast) break;
+    const uint32_t w = w0 + i * kThreads;
+    const uint32_t lt = w / (uint32_t)vpr;
+    const uint32_t c = w - lt * (uint32_t)vpr;
+    buf[i] = __builtin_nontemporal_load(&src[rows[lt] * vpr + c]);
   }
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
-    const int64_t v = base + (int64_t)i * kThreads;
-    if (v < nvec) dst[v] = buf[i];
+    const int64_t v = v0 + threadIdx.x + (int64_t)i * kThreads;
+    if (v <= vlast) dst[v] = buf[i];
   }
 }
 
@@ -127,8 +134,7 @@ hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int
   a.rank = rank;
   a.n_gather = n_gather;
   if (a.local == 0) return hipSuccess;
-  const int64_t per_block = (int64_t)kThreads * kVecPerThread;
-  const int64_t blocks = (max_vec + per_block - 1) / per_block;
+  const int64_t blocks = (max_vec + kPerBlock - 1) / kPerBlock;
   hipLaunchKernelGGL(partition_kernel, dim3((unsigned)blocks, n_gather > 0 ? n_gather : 1), dim3(kThreads),
                      0, stream, a);
   return hipGetLastError();

@@ -56,3 +56,26 @@ def test_empty_partition_is_noop():
     idx = torch.empty(0, dtype=torch.int32, device=DEV)
     C.cpattn_partition(C.PART_ZIGZAG, 0, 4, 1, idx)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", ["zigzag", "thd"])
+def test_indices_only(mode):
+    # no tensors to gather: the kernel writes the index (and document) outputs alone,
+    # over several blocks of rows
+    if mode == "zigzag":
+        total, cp, cu, cu_dev = 3000, 4, None, None
+    else:
+        cu = workloads.cu_seqlens_from_lengths([8, 64, 136, 0, 16, 256, 8, 32, 2040])
+        total, cp = int(cu[-1]), 2
+        cu_dev = torch.as_tensor(cu, dtype=torch.int32, device=DEV)
+    for r in range(cp):
+        say(f"partition indices only {mode} total={total} cp={cp} rank={r}")
+        idx = torch.empty(total // cp, dtype=torch.int32, device=DEV)
+        doc = torch.empty(total // cp, dtype=torch.int32, device=DEV) if cu is not None else None
+        C.cpattn_partition(C.PART_THD if cu is not None else C.PART_ZIGZAG, total, cp, r, idx, doc,
+                           (), (), None if cu is None else cu.tolist(), cu_dev)
+        torch.cuda.synchronize()
+        want = oracle.thd_indices(cu, cp, r) if cu is not None else oracle.zigzag_indices(total, cp, r)
+        assert np.array_equal(idx.cpu().numpy(), want)
+        if cu is not None:
+            assert np.array_equal(doc.cpu().numpy(), oracle.thd_doc_ids(cu, want))
