@@ -1,8 +1,8 @@
 """Full-size workloads in the launch configuration the benchmark times, checked on
 sampled rows against the oracle (which evaluates those rows against every key), and
-the two forward forms checked against each other on every row.  The 128K backward is
-checked on sampled query rows (dQ) and, for dK / dV, through two identities of the
-softmax Jacobian that hold at any size."""
+the two forward forms checked against each other on every row.  The 128K and packed
+backward passes are checked on sampled query rows (dQ) and, for dK / dV, through two
+identities of the softmax Jacobian that hold at any size (per document when packed)."""
 import numpy as np
 import pytest
 import torch
@@ -120,5 +120,53 @@ def test_s128k_rank0_bwd_sampled():
     dk_max = float(dk_sum.abs().max())
     say(f"s128k bwd: sum dV vs sum G max err {float((dv_sum - g_sum).abs().max()):.3e} "
         f"(tolerance >= {float(dv_tol.min()):.3f}); |sum dK| max {dk_max:.3e}")
+    assert dv_excess <= 0.0, dv_excess
+    assert dk_max <= 0.5, dk_max
+
+
+def test_thd64k_rank1_bwd_sampled():
+    w = workloads.WORKLOADS["thd64k"]
+    cu = workloads.cu_seqlens_from_lengths(workloads.thd_lengths(w.seed))
+    say("thd64k bwd: generating inputs")
+    q, k, v = workloads.full_qkv(w)
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), w.cp, 1, cu)
+    n = rs.q.shape[0]
+    g = workloads.randn((n, w.hq, w.d), w.seed, "bf16", 3)
+    say("thd64k bwd: stream forward + backward (owner segments, as timed)")
+    o, lse = rs.stream_fwd("owner")
+    dq, dk, dv = rs.bwd(o, lse, g.to(DEV), granularity="owner")
+    torch.cuda.synchronize()
+    rows_all = rs.q_idx.cpu().numpy()
+    q_docs = rs.q_doc.cpu().numpy()
+    all_docs = oracle.thd_doc_ids(cu, np.arange(w.seq))
+    # dQ of sampled rows (both ends of every document's slices among them) against the
+    # oracle over every key with the document mask
+    ends = np.flatnonzero(np.diff(q_docs))
+    local = np.unique(np.concatenate([sample_local_rows(n, 13, 6), ends, ends + 1]))
+    rows = rows_all[local]
+    say(f"thd64k bwd: oracle dQ on {len(local)} rows")
+    dq_r, _, _ = OA.attention_bwd(q[torch.as_tensor(rows)], k, v, g[torch.as_tensor(local)], rows,
+                                  np.arange(w.seq), q_docs[local], all_docs, mask=OA.MASK_CAUSAL_DOC)
+    assert_close(dq[torch.as_tensor(local, device=DEV)], dq_r, TOL_BF16, "thd64k dQ (sampled)")
+    # Per document: a row sees keys of its own document only and its probabilities sum
+    # to 1, so the dV rows of a document's keys (over all owners) sum to G summed over
+    # the local rows of that document, and its dK rows to 0 (the tolerances are those
+    # of the 128K test, per document).
+    n_docs = len(cu) - 1
+    dv_doc = torch.zeros((n_docs, w.hkv, w.d), dtype=torch.float64)
+    dk_doc = torch.zeros_like(dv_doc)
+    for (seg, (owner, _), (a, b)), dk_s, dv_s in zip(rs.segments("owner"), dk, dv):
+        kd = torch.as_tensor(rs.owners[owner].doc[a:b].cpu().numpy(), dtype=torch.long)
+        dv_doc.index_add_(0, kd, dv_s.double().cpu())
+        dk_doc.index_add_(0, kd, dk_s.double().cpu())
+    qd = torch.as_tensor(q_docs, dtype=torch.long)
+    g64 = g.double().reshape(n, w.hkv, w.hq // w.hkv, w.d).sum(2)
+    g_doc = torch.zeros_like(dv_doc).index_add_(0, qd, g64)
+    g2_doc = torch.zeros_like(dv_doc).index_add_(0, qd, g.double().reshape(n, w.hkv, -1, w.d).pow(2).sum(2))
+    dv_tol = 3 * 2.0 ** -9 * g2_doc.sqrt()
+    dv_excess = float(((dv_doc - g_doc).abs() - dv_tol).max())
+    dk_max = float(dk_doc.abs().max())
+    say(f"thd64k bwd: per-document sum dV vs sum G max err {float((dv_doc - g_doc).abs().max()):.3e}; "
+        f"|sum dK| max {dk_max:.3e}")
     assert dv_excess <= 0.0, dv_excess
     assert dk_max <= 0.5, dk_max
