@@ -577,16 +577,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using Sm = DkdvSmem<D>;
   __shared__ Sm sm;
   __shared__ RowSmem rs;
-  const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
-  if (logical >= a.total_wgs) return;
-  int s = 0;
-  while (s + 1 < a.n_segs && a.seg_wg_begin[s + 1] <= logical) ++s;
+  int s = 0, kvh, jp;
+  if constexpr (DOC) {
+    if ((a.hkv & 7) == 0) {
+      // Packed documents: a key tile's work follows its documents, not its index, so
+      // instead of contiguous ranges every XCD (b % 8) takes kv heads [x*hpx, (x+1)*hpx)
+      // of every segment: an equal share of each segment's work, its items segment by
+      // segment, tile pairs in order, heads inner.  The launch has no padding here.
+      const int hpx = a.hkv >> 3;
+      int i = blockIdx.x >> 3;
+      while (true) {
+        const int np = ((a.segs[s].len + kBKV - 1) / kBKV + 1) / 2;
+        if (i < np * hpx) break;
+        i -= np * hpx;
+        ++s;
+      }
+      jp = i / hpx;
+      kvh = (blockIdx.x & 7) * hpx + (i - jp * hpx);
+    }
+  }
+  if (!DOC || (a.hkv & 7) != 0) {
+    const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
+    if (logical >= a.total_wgs) return;
+    while (s + 1 < a.n_segs && a.seg_wg_begin[s + 1] <= logical) ++s;
+    const int n_pair = ((a.segs[s].len + kBKV - 1) / kBKV + 1) / 2;
+    const int local = logical - a.seg_wg_begin[s];
+    kvh = local / n_pair;
+    jp = local - kvh * n_pair;
+  }
   const SegDesc& sg = a.segs[s];
   const int n_kt = (sg.len + kBKV - 1) / kBKV;
-  const int n_pair = (n_kt + 1) / 2;
-  const int local = logical - a.seg_wg_begin[s];
-  const int kvh = local / n_pair;
-  const int jp = local - kvh * n_pair;
   // a work-group takes key tiles jp and n_kt - 1 - jp of its segment in turn: under
   // causal masking their visible query counts roughly add up to a constant (a zigzag
   // segment's early tiles see the most queries, its late ones the fewest), so the
