@@ -578,25 +578,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ Sm sm;
   __shared__ RowSmem rs;
   int s = 0, kvh, jp;
-  if constexpr (DOC) {
-    if ((a.hkv & 7) == 0) {
-      // Packed documents: a key tile's work follows its documents, not its index, so
-      // instead of contiguous ranges every XCD (b % 8) takes kv heads [x*hpx, (x+1)*hpx)
-      // of every segment: an equal share of each segment's work, its items segment by
-      // segment, tile pairs in order, heads inner.  The launch has no padding here.
-      const int hpx = a.hkv >> 3;
-      int i = blockIdx.x >> 3;
-      while (true) {
-        const int np = ((a.segs[s].len + kBKV - 1) / kBKV + 1) / 2;
-        if (i < np * hpx) break;
-        i -= np * hpx;
-        ++s;
-      }
-      jp = i / hpx;
-      kvh = (blockIdx.x & 7) * hpx + (i - jp * hpx);
+  if ((a.hkv & 7) == 0) {
+    // Every XCD (b % 8) takes kv heads [x*hpx, (x+1)*hpx) of every segment, its items
+    // segment by segment, tile pairs in order, heads inner: an equal share of each
+    // segment's work (with packed documents a key tile's work follows its documents,
+    // not its index), and each kv head's Q / dO stream stays on one XCD's L2.  The
+    // launch has no padding here.
+    const int hpx = a.hkv >> 3;
+    int i = blockIdx.x >> 3;
+    while (true) {
+      const int np = ((a.segs[s].len + kBKV - 1) / kBKV + 1) / 2;
+      if (i < np * hpx) break;
+      i -= np * hpx;
+      ++s;
     }
-  }
-  if (!DOC || (a.hkv & 7) != 0) {
+    jp = i / hpx;
+    kvh = (blockIdx.x & 7) * hpx + (i - jp * hpx);
+  } else {
     const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
     if (logical >= a.total_wgs) return;
     while (s + 1 < a.n_segs && a.seg_wg_begin[s + 1] <= logical) ++s;
