@@ -293,13 +293,36 @@ struct WorkItem {
   int job, hg, qt, split;
 };
 
-// Index order.  The launch hands each XCD one contiguous logical range (xcd_remap) and
-// each XCD's dispatcher starts its work-groups in logical order as CUs free up.  Inside
-// a job the head groups are outermost and the query tiles run latest first: in a
-// causal zigzag share the later tiles see more keys, so every XCD starts its heaviest
-// tiles first.  job = -1: a padding work-group.
+// Index order.  The dispatcher hands work-group b to XCD b % 8, and each XCD starts its
+// work-groups in order as CUs free up.  Inside a job the head groups are outermost and
+// the query tiles run latest first: in a causal zigzag share the later tiles see more
+// keys, so every XCD starts its heaviest tiles first.  When the head groups divide by 8
+// (no padding then), XCD x takes head groups [x*hpx, (x+1)*hpx) of every job, so a
+// launch of several jobs of unequal weight (the edges of the tile form) gives every
+// XCD the same share of each; otherwise each XCD takes one contiguous logical range
+// (xcd_remap).  For a single job the two orders coincide.  job = -1: a padding
+// work-group.
 __device__ __forceinline__ WorkItem indexed_work_item(const FwdArgs& a, int qt_rows) {
   WorkItem w{-1, 0, 0, 0};
+  const int n_hg = a.hq / a.heads_per_wg;
+  if ((n_hg & 7) == 0) {
+    const int hpx = n_hg >> 3;
+    int i = blockIdx.x >> 3, j = 0, n_qt, nsplit;
+    while (true) {
+      n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+      nsplit = a.jobs[j].n_split;
+      if (i < n_qt * nsplit * hpx) break;
+      i -= n_qt * nsplit * hpx;
+      ++j;
+    }
+    const int hl = i / (n_qt * nsplit);
+    const int k = i - hl * (n_qt * nsplit);
+    w.job = j;
+    w.split = k % nsplit;
+    w.qt = n_qt - 1 - k / nsplit;
+    w.hg = (blockIdx.x & 7) * hpx + hl;
+    return w;
+  }
   const int logical = xcd_remap(blockIdx.x, a.padded_wgs);
   if (logical >= a.total_wgs) return w;
   int j = 0;
