@@ -578,12 +578,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ Sm sm;
   __shared__ RowSmem rs;
   int s = 0, kvh, jp;
-  if ((a.hkv & 7) == 0) {
-    // Every XCD (b % 8) takes kv heads [x*hpx, (x+1)*hpx) of every segment, its items
-    // segment by segment, tile pairs in order, heads inner: an equal share of each
-    // segment's work (with packed documents a key tile's work follows its documents,
-    // not its index), and each kv head's Q / dO stream stays on one XCD's L2.  The
-    // launch has no padding here.
+  if (DOC && (a.hkv & 7) == 0) {
+    // Packed documents: a key tile's work follows its documents, not its index, so
+    // every XCD (b % 8) takes kv heads [x*hpx, (x+1)*hpx) of every segment, an equal
+    // share of each segment's work: segment by segment, tile pairs in order, heads
+    // inner.  The launch has no padding here.  (Zigzag shares keep contiguous ranges,
+    // whose consecutive items share a segment and so its query rows in L2.)
     const int hpx = a.hkv >> 3;
     int i = blockIdx.x >> 3;
     while (true) {
