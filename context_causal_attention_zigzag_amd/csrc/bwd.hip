@@ -168,9 +168,17 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   static_assert(sizeof(sm) >= (kMaxRankedTiles + 1) * sizeof(int), "ranking scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
-  const WorkItem wi = RANKED ? ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm))
-                             : indexed_work_item(a, qt_rows);
-  if (wi.job < 0) return;
+  TileTab tt{0, 0};
+  WorkItem wi;
+  if constexpr (RANKED) {
+    int s1 = 0;
+    for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
+    tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
+    wi = ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
+  } else {
+    wi = indexed_work_item(a, qt_rows);
+    if (wi.job < 0) return;
+  }
   const JobDesc& job = a.jobs[wi.job];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -233,7 +241,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   // tiles of the walk, and per wave the skipped and the fully visible ones, from one
   // binary search per segment (kv_stream.h); the loop reads no segment table
   TileIter it;
-  iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax);
+  if (!RANKED && a.mask != kMaskNone) tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
+  iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax, sm, tt);
   if (nsplit == 1) {
     iter_walk_all(it, job);
   } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {

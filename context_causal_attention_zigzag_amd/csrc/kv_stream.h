@@ -69,9 +69,89 @@ struct TileIter {
 struct VisRanges {
   int lo, hi, wlo, whi, flo, fhi;
 };
+
+// Tile boundary table: for every KV tile m of segments [s0, s0 + n) the positions of its
+// first and last key and their documents, in the second K/V buffer of the LDS image,
+// which nothing writes before the walk's first barrier (every wave reaches it only after
+// its boundary searches).  Segment s's tiles start at (s - s0) * stride.  One round of
+// independent loads fills it, and the boundary searches then read LDS instead of
+// chasing global memory one dependent load at a time.  stride 0: no table (more tiles
+// than fit); the searches then read global memory.
+struct TileTab {
+  int s0;
+  int stride;
+};
+
+template <class Sm>
+struct TabLds {
+  static constexpr int kCap = (sizeof(Sm::k) < sizeof(Sm::v) ? sizeof(Sm::k) : sizeof(Sm::v)) / 2 / 8;
+  __device__ static int32_t* fpos(Sm& sm) { return reinterpret_cast<int32_t*>(sm.k[1]); }
+  __device__ static int32_t* lpos(Sm& sm) { return reinterpret_cast<int32_t*>(sm.k[1]) + kCap; }
+  __device__ static int32_t* fdoc(Sm& sm) { return reinterpret_cast<int32_t*>(sm.v[1]); }
+  __device__ static int32_t* ldoc(Sm& sm) { return reinterpret_cast<int32_t*>(sm.v[1]) + kCap; }
+};
+
+// Every thread of the work-group calls this with the same arguments.
+template <int NT, class Sm>
+__device__ __forceinline__ TileTab load_tile_table(Sm& sm, const FwdArgs& a, int s0, int s1) {
+  using T = TabLds<Sm>;
+  int stride = 0;
+  for (int s = s0; s < s1; ++s) stride = max(stride, (a.segs[s].len + kBK - 1) / kBK);
+  if (stride == 0 || (s1 - s0) * stride > T::kCap) return {s0, 0};
+  const bool docm = a.mask == kMaskCausalDoc;
+  for (int i = threadIdx.x; i < (s1 - s0) * stride; i += NT) {
+    const int sl = i / stride, m = i - sl * stride;
+    const SegDesc& sg = a.segs[s0 + sl];
+    if (m * kBK < sg.len) {
+      const int f = m * kBK, l = min(sg.len, f + kBK) - 1;
+      T::fpos(sm)[i] = sg.pos[f];
+      T::lpos(sm)[i] = sg.pos[l];
+      if (docm) {
+        T::fdoc(sm)[i] = sg.doc[f];
+        T::ldoc(sm)[i] = sg.doc[l];
+      }
+    }
+  }
+  __syncthreads();
+  return {s0, stride};
+}
+
+// The six boundaries of one segment (see iter_init_lanes) over accessors of its tiles'
+// first / last key positions and documents (fp, lp, fd, ld; lp and ld of a full tile are
+// its key kBK - 1).
+template <class FP, class LP, class FD, class LD>
+__device__ __forceinline__ VisRanges vis_search(int nt, int nf, bool docm, int qmax, int qdmin, int qdmax,
+                                                bool wave_rows, int wqmin, int wqmax, int wqdmin, int wqdmax,
+                                                FP fp, LP lp, FD fd, LD ld) {
+  const int wnt = wave_rows ? nt : 0;
+  const int wnf = wave_rows && (!docm || wqdmin == wqdmax) ? nf : 0;
+  // [l, h) search intervals; the document-only searches start empty without documents
+  int l0 = 0, h0 = nt, l1 = 0, h1 = docm ? nt : 0, l2 = 0, h2 = wnt, l3 = 0, h3 = docm ? wnt : 0;
+  int l4 = 0, h4 = wnf, l5 = 0, h5 = docm ? wnf : 0;
+  while (l0 < h0 || l1 < h1 || l2 < h2 || l3 < h3 || l4 < h4 || l5 < h5) {
+    const int m0 = (l0 + h0) >> 1, m1 = (l1 + h1) >> 1, m2 = (l2 + h2) >> 1;
+    const int m3 = (l3 + h3) >> 1, m4 = (l4 + h4) >> 1, m5 = (l5 + h5) >> 1;
+    bool p0 = false, p1 = false, p2 = false, p3 = false, p4 = false, p5 = false;
+    if (l0 < h0) p0 = fp(m0) > qmax || (docm && fd(m0) > qdmax);
+    if (l1 < h1) p1 = ld(m1) >= qdmin;
+    if (l2 < h2) p2 = fp(m2) > wqmax || (docm && fd(m2) > wqdmax);
+    if (l3 < h3) p3 = ld(m3) >= wqdmin;
+    if (l4 < h4) p4 = lp(m4) > wqmin || (docm && ld(m4) > wqdmin);
+    if (l5 < h5) p5 = fd(m5) >= wqdmin;
+    if (l0 < h0) { if (p0) h0 = m0; else l0 = m0 + 1; }
+    if (l1 < h1) { if (p1) h1 = m1; else l1 = m1 + 1; }
+    if (l2 < h2) { if (p2) h2 = m2; else l2 = m2 + 1; }
+    if (l3 < h3) { if (p3) h3 = m3; else l3 = m3 + 1; }
+    if (l4 < h4) { if (p4) h4 = m4; else l4 = m4 + 1; }
+    if (l5 < h5) { if (p5) h5 = m5; else l5 = m5 + 1; }
+  }
+  return {l1, l0, l3, l2, l5, l4};
+}
+
+template <class Sm>
 __device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
                                                 int qmax, int qdmin, int qdmax, bool wave_rows, int wqmin,
-                                                int wqmax, int wqdmin, int wqdmax) {
+                                                int wqmax, int wqdmin, int wqdmax, Sm& sm, TileTab tt) {
   int len = 0;
   uint64_t kp = 0, vp = 0, pp = 0, dp = 0;
   VisRanges r = {0, 0, 0, 0, 0, 0};
@@ -84,33 +164,27 @@ __device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, 
     dp = reinterpret_cast<uint64_t>(sg.doc);
     const int nt = (len + kBK - 1) / kBK, nf = len / kBK;
     const bool docm = a.mask == kMaskCausalDoc;
-    const int32_t* pos = sg.pos;
-    const int32_t* dc = sg.doc;
     const int wnt = wave_rows ? nt : 0;
     const int wnf = wave_rows && (!docm || wqdmin == wqdmax) ? nf : 0;
     r = {0, nt, 0, wnt, 0, wnf};
     if (a.mask != kMaskNone) {
-      // [l, h) search intervals; the document-only searches start empty without documents
-      int l0 = 0, h0 = nt, l1 = 0, h1 = docm ? nt : 0, l2 = 0, h2 = wnt, l3 = 0, h3 = docm ? wnt : 0;
-      int l4 = 0, h4 = wnf, l5 = 0, h5 = docm ? wnf : 0;
-      while (l0 < h0 || l1 < h1 || l2 < h2 || l3 < h3 || l4 < h4 || l5 < h5) {
-        const int m0 = (l0 + h0) >> 1, m1 = (l1 + h1) >> 1, m2 = (l2 + h2) >> 1;
-        const int m3 = (l3 + h3) >> 1, m4 = (l4 + h4) >> 1, m5 = (l5 + h5) >> 1;
-        bool p0 = false, p1 = false, p2 = false, p3 = false, p4 = false, p5 = false;
-        if (l0 < h0) p0 = pos[m0 * kBK] > qmax || (docm && dc[m0 * kBK] > qdmax);
-        if (l1 < h1) p1 = dc[min(len, m1 * kBK + kBK) - 1] >= qdmin;
-        if (l2 < h2) p2 = pos[m2 * kBK] > wqmax || (docm && dc[m2 * kBK] > wqdmax);
-        if (l3 < h3) p3 = dc[min(len, m3 * kBK + kBK) - 1] >= wqdmin;
-        if (l4 < h4) p4 = pos[m4 * kBK + kBK - 1] > wqmin || (docm && dc[m4 * kBK + kBK - 1] > wqdmin);
-        if (l5 < h5) p5 = dc[m5 * kBK] >= wqdmin;
-        if (l0 < h0) { if (p0) h0 = m0; else l0 = m0 + 1; }
-        if (l1 < h1) { if (p1) h1 = m1; else l1 = m1 + 1; }
-        if (l2 < h2) { if (p2) h2 = m2; else l2 = m2 + 1; }
-        if (l3 < h3) { if (p3) h3 = m3; else l3 = m3 + 1; }
-        if (l4 < h4) { if (p4) h4 = m4; else l4 = m4 + 1; }
-        if (l5 < h5) { if (p5) h5 = m5; else l5 = m5 + 1; }
+      if (tt.stride > 0) {
+        using T = TabLds<Sm>;
+        const int b = (job.seg_begin + lane - tt.s0) * tt.stride;
+        const int32_t* f = T::fpos(sm) + b;
+        const int32_t* l = T::lpos(sm) + b;
+        const int32_t* fdc = T::fdoc(sm) + b;
+        const int32_t* ldc = T::ldoc(sm) + b;
+        r = vis_search(nt, nf, docm, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax,
+                       [&](int m) { return f[m]; }, [&](int m) { return l[m]; },
+                       [&](int m) { return fdc[m]; }, [&](int m) { return ldc[m]; });
+      } else {
+        const int32_t* pos = sg.pos;
+        const int32_t* dc = sg.doc;
+        r = vis_search(nt, nf, docm, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax,
+                       [&](int m) { return pos[m * kBK]; }, [&](int m) { return pos[min(len, m * kBK + kBK) - 1]; },
+                       [&](int m) { return dc[m * kBK]; }, [&](int m) { return dc[min(len, m * kBK + kBK) - 1]; });
       }
-      r = {l1, l0, l3, l2, l5, l4};
     }
   }
   it.rlo = r.lo;
@@ -356,19 +430,21 @@ inline bool ranked_plan(const FwdArgs& a, int qt_rows) {
   return n_all > 0 && n_all <= kMaxRankedTiles;
 }
 
-// KV tiles the work-group of query rows [r0, r1) walks in one segment: from the first
-// tile that reaches the rows' first document to the first tile past their last
-// position or document (the boundaries the tile iterators find for the work-group).
-__device__ __forceinline__ int seg_walk_tiles(const SegDesc& sg, int qmax, int qdmin, int qdmax) {
-  const int len = sg.len, nt = (len + kBK - 1) / kBK;
+// KV tiles the work-group of query rows [r0, r1) walks in one segment of nt tiles: from
+// the first tile that reaches the rows' first document to the first tile past their
+// last position or document (the boundaries the tile iterators find for the
+// work-group), over accessors of the tiles' first key position / document and last
+// key document.
+template <class FP, class FD, class LD>
+__device__ __forceinline__ int walk_tiles(int nt, int qmax, int qdmin, int qdmax, FP fp, FD fd, LD ld) {
   int l0 = 0, h0 = nt, l1 = 0, h1 = nt;
   while (l0 < h0 || l1 < h1) {
     const int m0 = (l0 + h0) >> 1, m1 = (l1 + h1) >> 1;
     if (l0 < h0) {
-      if (sg.pos[m0 * kBK] > qmax || sg.doc[m0 * kBK] > qdmax) h0 = m0; else l0 = m0 + 1;
+      if (fp(m0) > qmax || fd(m0) > qdmax) h0 = m0; else l0 = m0 + 1;
     }
     if (l1 < h1) {
-      if (sg.doc[min(len, m1 * kBK + kBK) - 1] >= qdmin) h1 = m1; else l1 = m1 + 1;
+      if (ld(m1) >= qdmin) h1 = m1; else l1 = m1 + 1;
     }
   }
   return max(0, l0 - l1);
@@ -382,8 +458,9 @@ __device__ __forceinline__ int seg_walk_tiles(const SegDesc& sg, int qmax, int q
 // longest-processing-time-first schedule of its share, its head groups inner.  Every
 // thread of the work-group calls this; scratch holds kMaxRankedTiles + 1 ints of LDS
 // that nothing else uses yet.
-template <int NT>
-__device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_rows, int* scratch) {
+template <int NT, class Sm>
+__device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_rows, int* scratch, Sm& sm,
+                                                     TileTab tt) {
   const int b = blockIdx.x;
   const int hpx = (a.hq / a.heads_per_wg) >> 3;
   const int i = b >> 3;
@@ -415,7 +492,23 @@ __device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_ro
     const int n_seg = job.seg_end - job.seg_begin;
     const int q = kk / n_seg, s = kk - q * n_seg;
     const int r0 = q * qt_rows, r1 = min(job.len, r0 + qt_rows);
-    const int c = seg_walk_tiles(a.segs[job.seg_begin + s], job.pos[r1 - 1], job.doc[r0], job.doc[r1 - 1]);
+    const SegDesc& sg = a.segs[job.seg_begin + s];
+    const int nt = (sg.len + kBK - 1) / kBK;
+    const int qmax = job.pos[r1 - 1], qdmin = job.doc[r0], qdmax = job.doc[r1 - 1];
+    int c;
+    if (tt.stride > 0) {
+      using T = TabLds<Sm>;
+      const int b = (job.seg_begin + s - tt.s0) * tt.stride;
+      const int32_t* f = T::fpos(sm) + b;
+      const int32_t* fdc = T::fdoc(sm) + b;
+      const int32_t* ldc = T::ldoc(sm) + b;
+      c = walk_tiles(nt, qmax, qdmin, qdmax, [&](int m) { return f[m]; }, [&](int m) { return fdc[m]; },
+                     [&](int m) { return ldc[m]; });
+    } else {
+      c = walk_tiles(nt, qmax, qdmin, qdmax, [&](int m) { return sg.pos[m * kBK]; },
+                     [&](int m) { return sg.doc[m * kBK]; },
+                     [&](int m) { return sg.doc[min(sg.len, m * kBK + kBK) - 1]; });
+    }
     if (c) atomicAdd(&scratch[base + q], c);
   }
   __syncthreads();
