@@ -173,3 +173,42 @@ def test_bwd_fully_masked_rows_give_zero_gradients():
     C.cpattn_bwd(desc, C.q_block(q, qpos), [C.kv_seg(k, v, kpos)], o, lse, g, dq, [dk], [dv], ws)
     torch.cuda.synchronize()
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+@pytest.mark.parametrize("n_keys,n_segs", [(60000, 10), (78000, 20)])
+def test_more_tiles_than_the_lds_boundary_table(n_keys, n_segs):
+    # The forward's and dQ's boundary searches read a table of every 64-key tile in LDS,
+    # 1152 tiles at d = 64: 60000 keys in 10 segments (940 tiles) fit it, 78000 keys in
+    # 20 segments (1220 tiles) do not, so the searches read global memory.  Both must
+    # match the oracle, forward and backward.
+    import context_causal_attention_zigzag_amd as C
+    hq, d = 1, 64
+    k = workloads.randn((n_keys, hq, d), 31, "bf16", 1)
+    v = workloads.randn((n_keys, hq, d), 31, "bf16", 2)
+    rng = np.random.default_rng(31)
+    qpos = np.sort(rng.choice(n_keys, 300, replace=False)).astype(np.int32)
+    q = workloads.randn((300, hq, d), 31, "bf16", 0)
+    g = workloads.randn((300, hq, d), 31, "bf16", 3)
+    gq, gk, gv, gg = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    kpos = torch.arange(n_keys, dtype=torch.int32, device=DEV)
+    qp = torch.as_tensor(qpos, device=DEV)
+    bounds = np.linspace(0, n_keys, n_segs + 1).astype(int)
+    segs = [C.kv_seg(gk[a:b], gv[a:b], kpos[a:b]) for a, b in zip(bounds[:-1], bounds[1:])]
+    desc = C.attn_desc(hq, hq, d)
+    qb = C.q_block(gq, qp)
+    say(f"{n_segs} segments of {n_keys // n_segs} keys: stream forward + backward")
+    o = torch.empty_like(gq)
+    lse = torch.empty((300, hq), dtype=torch.float32, device=DEV)
+    C.cpattn_stream_fwd(desc, qb, segs, o, lse)
+    dq = torch.empty((300, hq, d), dtype=torch.float32, device=DEV)
+    dk = [torch.empty((b - a, hq, d), dtype=torch.float32, device=DEV) for a, b in zip(bounds[:-1], bounds[1:])]
+    dv = [torch.empty_like(x) for x in dk]
+    ws = torch.empty(max(1, C.cpattn_bwd_workspace_bytes(desc, qb, segs)), dtype=torch.uint8, device=DEV)
+    C.cpattn_bwd(desc, qb, segs, o, lse, gg, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = OA.attention_fwd(q, k, v, qpos, np.arange(n_keys))
+    assert_close(o, o_ref, TOL_BF16, f"{n_segs}-seg O")
+    dq_r, dk_r, dv_r = OA.attention_bwd(q, k, v, g, qpos, np.arange(n_keys))
+    assert_close(dq, dq_r, TOL_BF16, f"{n_segs}-seg dQ")
+    assert_close(torch.cat(dk), dk_r, TOL_BF16, f"{n_segs}-seg dK")
+    assert_close(torch.cat(dv), dv_r, TOL_BF16, f"{n_segs}-seg dV")
