@@ -808,22 +808,47 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dkdv_acc_all<D>(sm, bp, ppf, pdsf, dk, dv, lane);
   }
 
-  // per-owner sums: this wave's 32 keys, all local queries and all heads of the group
-  if (key_ok) {
-    float* dkp = a.dk[s];
-    float* dvp = a.dv[s];
+  // per-owner sums: this wave's 32 keys, all local queries and all heads of the group.
+  // The accumulators give each lane 16-byte pieces of 32 different key rows; stored as
+  // they are, every instruction would leave its cache lines partly written.  Each wave
+  // therefore stages its rows in its own part of the (now idle) tile images and stores
+  // whole 512-byte rows, two per instruction.  LDS operations of one wave complete in
+  // order, so the dV rows may overwrite the dK rows as soon as their reads are issued.
+  // every wave is done with the tile images, and no fill into them is in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
+  {
+    constexpr int kRow = D + 4;  // staged row stride in floats (rows 16 bytes apart in the banks)
+    static_assert(sizeof(Sm) >= 4 * 32 * kRow * sizeof(float), "staging space");
+    float* stg = reinterpret_cast<float*>(&sm) + wave * 32 * kRow;
+    const int nrows = max(0, min(32, k1 - (k0 + wave * 32)));
     const float sc = a.scale;
-    const int64_t rowoff = ((int64_t)mykey * a.hkv + kvh) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * h;
-        *reinterpret_cast<f32x4*>(dkp + rowoff + d0) =
-            f32x4{dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc};
-        *reinterpret_cast<f32x4*>(dvp + rowoff + d0) =
-            f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * h;
+          const f32x16& acc = mat == 0 ? dk[db] : dv[db];
+          const float m = mat == 0 ? sc : 1.0f;
+          *reinterpret_cast<f32x4*>(stg + r * kRow + d0) =
+              f32x4{acc[4 * g] * m, acc[4 * g + 1] * m, acc[4 * g + 2] * m, acc[4 * g + 3] * m};
+        }
       }
+      __builtin_amdgcn_wave_barrier();
+      float* outp = mat == 0 ? a.dk[s] : a.dv[s];
+      constexpr int kPieces = D / 4;         // 16-byte pieces per row
+      constexpr int kRowsPer = kWave / kPieces;  // rows per store instruction
+#pragma unroll
+      for (int j = 0; j < 32 / kRowsPer; ++j) {
+        const int row = j * kRowsPer + lane / kPieces;
+        const int col = (lane % kPieces) * 4;
+        const f32x4 val = *reinterpret_cast<const f32x4*>(stg + row * kRow + col);
+        if (row < nrows)
+          *reinterpret_cast<f32x4*>(outp + ((int64_t)(k0 + wave * 32 + row) * a.hkv + kvh) * D + col) = val;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
   }  // key tile pass
