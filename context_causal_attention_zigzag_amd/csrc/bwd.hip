@@ -671,9 +671,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // per-query-tile position ranges in LDS (n_qt <= kMaxQTiles is checked on the host)
+  // per-query-tile position ranges in LDS (n_qt <= kMaxQTiles is checked on the host);
+  // they depend on the query block only, so the second pass keeps the first one's
   const int n_qt = (a.q_len + kBQ - 1) / kBQ;
-  for (int t = tid; t < n_qt; t += kThreads) {
+  for (int t = tid; pass == 0 && t < n_qt; t += kThreads) {
     const int q0 = t * kBQ, q1 = min(a.q_len, q0 + kBQ) - 1;
     rs.qtab[0][t] = a.qpos[q0];
     rs.qtab[1][t] = a.qpos[q1];
