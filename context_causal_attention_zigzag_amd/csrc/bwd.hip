@@ -622,8 +622,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kt = pass == 0 ? jp : n_kt - 1 - jp;
   if (pass == 1) {
     if (kt <= jp) break;
-    // every wave is done with the LDS images of the first tile
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // every wave is done with its staged rows of the first tile (no fill is in flight:
+    // the first pass waited for them before staging); its dK / dV stores may still be
+    // in flight and drain under this pass's setup
     lds_barrier();
   }
   const int k0 = kt * kBKV, k1 = min(sg.len, k0 + kBKV);
