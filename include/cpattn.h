@@ -27,6 +27,11 @@
  *    can see is validated first, and on any error nothing is enqueued.
  *  - Outputs are overwritten, never accumulated across calls.
  *  - A row that sees no key at all gets O = 0 and LSE = -inf (never NaN).
+ *  - Launch plans (work-group size, KV splits) follow the device's compute-unit
+ *    count; the environment variable CPATTN_NUM_CUS (a positive integer) replaces it.
+ *    A plan fixes the fp32 summation order, so results are bitwise repeatable for a
+ *    given plan; different plans agree to rounding.  The order in which work-groups
+ *    run does not change any result.
  *  - Status codes below; cpattn_strerror() names them.
  */
 #ifndef CPATTN_H
