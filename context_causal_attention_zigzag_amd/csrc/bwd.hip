@@ -639,16 +639,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // this wave's keys as B operands (lane: key 32*wave + r, dims 16*ds + 8*h .. +7)
   const int mykey = k0 + wave * 32 + r;
   const bool key_ok = mykey < k1;
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    // keys past the segment's end load the last key (their results are masked)
-    const int64_t base = ((int64_t)min(mykey, k1 - 1) * a.hkv + kvh) * D + h * 8;
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      kf[ds] = *reinterpret_cast<const bf16x8*>(kb + base + ds * 16);
-      vf[ds] = *reinterpret_cast<const bf16x8*>(vb + base + ds * 16);
-    }
-  }
   // effective key position of masked tiles (keys past the end are never visible)
   const int kpos_mask = key_ok ? (mask == kMaskNone ? INT32_MIN + 1 : sg.pos[mykey]) : INT32_MAX;
   const int kdoc = (key_ok && docmask) ? sg.doc[mykey] : 0;
@@ -681,6 +671,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     rs.qtab[1][t] = a.qpos[q1];
     rs.qtab[2][t] = docmask ? a.qdoc[q0] : 0;
     rs.qtab[3][t] = docmask ? a.qdoc[q1] : 0;
+  }
+  // the K/V loads go out after the range loads above: completions count in issue
+  // order, so the visible-range test below then waits for its own loads only
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    // keys past the segment's end load the last key (their results are masked)
+    const int64_t base = ((int64_t)min(mykey, k1 - 1) * a.hkv + kvh) * D + h * 8;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      kf[ds] = *reinterpret_cast<const bf16x8*>(kb + base + ds * 16);
+      vf[ds] = *reinterpret_cast<const bf16x8*>(vb + base + ds * 16);
+    }
   }
   __shared__ int vis_lo, vis_hi;
   if (tid == 0) {
