@@ -80,6 +80,16 @@ def visible_mask(q_pos, k_pos, q_doc=None, k_doc=None, mask=MASK_CAUSAL) -> np.n
     return vis
 
 
+def _seen_keys(vis):
+    """Columns of a visibility block that at least one of its rows can see.
+
+    Restricting a block of query rows to these keys drops only terms that are exactly
+    zero (masked probabilities), so every sum keeps its value; it only spares the
+    oracle the score rows of keys nobody in the block can see (for a causal share most
+    keys, for packed documents nearly all)."""
+    return np.flatnonzero(vis.any(axis=0))
+
+
 def _group(hq, hkv):
     if hq % hkv != 0:
         raise ValueError("hq must be a multiple of hkv")
@@ -112,17 +122,20 @@ def attention_fwd(q, k, v, q_pos=None, k_pos=None, q_doc=None, k_doc=None,
         r1 = min(tq, r0 + _BLOCK)
         vis = visible_mask(q_pos[r0:r1], k_pos,
                            None if q_doc is None else q_doc[r0:r1], k_doc, mask)
+        # the keys some row of the block can see (the others add exact zeros)
+        cols = _seen_keys(vis)
+        vis = vis[:, cols]
         any_vis = vis.any(axis=1)
         for h in range(hq):
             g = h // grp
-            s = scale * (q[r0:r1, h, :] @ k[:, g, :].T)
+            s = scale * (q[r0:r1, h, :] @ k[cols, g, :].T)
             s = np.where(vis, s, -np.inf)
-            m = np.max(s, axis=1)
+            m = np.max(s, axis=1) if len(cols) else np.full(r1 - r0, -np.inf)
             m_safe = np.where(any_vis, m, 0.0)
             p = np.where(vis, np.exp(s - m_safe[:, None]), 0.0)
             l = p.sum(axis=1)
             l_safe = np.where(any_vis, l, 1.0)
-            o[r0:r1, h, :] = np.where(any_vis[:, None], (p @ v[:, g, :]) / l_safe[:, None], 0.0)
+            o[r0:r1, h, :] = np.where(any_vis[:, None], (p @ v[cols, g, :]) / l_safe[:, None], 0.0)
             lse[r0:r1, h] = np.where(any_vis, m_safe + np.log(l_safe), -np.inf)
     return o, lse
 
@@ -221,17 +234,75 @@ def attention_bwd(q, k, v, g, q_pos=None, k_pos=None, q_doc=None, k_doc=None,
         r1 = min(tq, r0 + _BLOCK)
         vis = visible_mask(q_pos[r0:r1], k_pos,
                            None if q_doc is None else q_doc[r0:r1], k_doc, mask)
+        cols = _seen_keys(vis)
+        vis = vis[:, cols]
         for h in range(hq):
             kh = h // grp
             lse_h = lse[r0:r1, h]
             lse_safe = np.where(np.isneginf(lse_h), 0.0, lse_h)
-            s = scale * (q[r0:r1, h, :] @ k[:, kh, :].T)
+            s = scale * (q[r0:r1, h, :] @ k[cols, kh, :].T)
             p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
             gh = g[r0:r1, h, :]
             dd = np.sum(gh * o[r0:r1, h, :], axis=1)
-            dp = gh @ v[:, kh, :].T
+            dp = gh @ v[cols, kh, :].T
             ds = p * (dp - dd[:, None])
-            dq[r0:r1, h, :] += scale * (ds @ k[:, kh, :])
+            dq[r0:r1, h, :] += scale * (ds @ k[cols, kh, :])
+            dk[cols, kh, :] += scale * (ds.T @ q[r0:r1, h, :])
+            dv[cols, kh, :] += p.T @ gh
+    return dq, dk, dv
+
+
+def attention_bwd_keys(q, k, v, g, key_rows, q_pos=None, k_pos=None, q_doc=None, k_doc=None,
+                       mask=MASK_CAUSAL, scale=None, o=None, lse=None):
+    """dK and dV of sum(G ∘ O) at the chosen key rows only.  Returns ([n, Hkv, d], [n, Hkv, d]).
+
+    The same softmax derivative as ``attention_bwd``, evaluated for the keys
+    ``key_rows`` (indices into k / v) against every query row: each query row's
+    probabilities are rebuilt from its full-row log-sum-exp over all keys,
+    P_ij = exp(S_ij − LSE_i), with D_i = Σ_d G_i·O_i from the full-row output; then
+    dK_j = scale Σ_i P_ij (G_i·v_j − D_i) q_i and dV_j = Σ_i P_ij G_i, summed over the
+    query heads of each kv head (the per-owner sums of the teaching page, section 01,
+    for a subset of the owner's keys).  ``o`` / ``lse`` are the full-row forward
+    results of these queries over all of k / v (computed here when not given)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    grp = _group(hq, hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if q_pos is None:
+        q_pos = np.arange(tq)
+    if k_pos is None:
+        k_pos = np.arange(tk)
+    q_pos, k_pos = _i64(q_pos), _i64(k_pos)
+    q_doc, k_doc = _i64(q_doc), _i64(k_doc)
+    if o is None or lse is None:
+        o, lse = attention_fwd(q, k, v, q_pos, k_pos, q_doc, k_doc, mask, scale)
+    o, lse = _f64(o), _f64(lse)
+    sel = _i64(key_rows)
+    kj, vj = k[sel], v[sel]
+    kpos_j = k_pos[sel]
+    kdoc_j = None if k_doc is None else k_doc[sel]
+    dk = np.zeros((len(sel), hkv, d))
+    dv = np.zeros((len(sel), hkv, d))
+    if len(sel) == 0 or tq == 0:
+        return dk, dv
+    for r0 in range(0, tq, _BLOCK):
+        r1 = min(tq, r0 + _BLOCK)
+        vis = visible_mask(q_pos[r0:r1], kpos_j,
+                           None if q_doc is None else q_doc[r0:r1], kdoc_j, mask)
+        if not vis.any():
+            continue
+        for h in range(hq):
+            kh = h // grp
+            lse_h = lse[r0:r1, h]
+            lse_safe = np.where(np.isneginf(lse_h), 0.0, lse_h)
+            s = scale * (q[r0:r1, h, :] @ kj[:, kh, :].T)
+            p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
+            gh = g[r0:r1, h, :]
+            dd = np.sum(gh * o[r0:r1, h, :], axis=1)
+            dp = gh @ vj[:, kh, :].T
+            ds = p * (dp - dd[:, None])
             dk[:, kh, :] += scale * (ds.T @ q[r0:r1, h, :])
             dv[:, kh, :] += p.T @ gh
-    return dq, dk, dv
+    return dk, dv

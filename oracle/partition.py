@@ -13,9 +13,16 @@ Sources:
   mirrored back slice [len−(r+1)·seg, len−r·seg), seg = len/(2·cp), concatenated.
 * "Context Parallelism (CP)" page, section 4: with cp=2 the four chunks go
   (chunk0, chunk3) to rank 0 and (chunk1, chunk2) to rank 1.
+* "推理系统基础设施（二）：Sequence Parallelism + Ring Attention" (ring-attention
+  page), section 5: the interleaved assignment [0, 4, 8, ...], [1, 5, 9, ...] for four
+  ranks; "Context Parallelism (CP)" page, sections 2.4 and 4, names this striped
+  split as the other static balancer of the causal task graph.  Reading: the
+  interleave is per token (rank r holds the tokens whose index is r modulo cp), as
+  in the Striped Attention paper the CP page cites.
 
-Pins: tests/test_oracle_partition.py (the cp=2 assignment printed on the pages,
-permutation / balance invariants, a second formulation by reshaping each document).
+Pins: tests/test_oracle_partition.py (the cp=2 assignment and the cp=4 interleave
+printed on the pages, permutation / balance invariants and closed-form pair counts,
+a second formulation by reshaping each document).
 """
 from __future__ import annotations
 
@@ -36,6 +43,21 @@ def zigzag_indices(seq_len: int, cp: int, rank: int) -> np.ndarray:
     for c in (rank, 2 * cp - 1 - rank):
         for t in range(chunk):
             rows.append(c * chunk + t)
+    return np.asarray(rows, dtype=np.int64)
+
+
+def striped_indices(seq_len: int, cp: int, rank: int) -> np.ndarray:
+    """Global row indices held by ``rank`` under the striped (interleaved) split:
+    rank, rank + cp, rank + 2cp, ...  The length must be divisible by cp."""
+    if cp < 1 or not (0 <= rank < cp):
+        raise ValueError("rank out of range")
+    if seq_len % cp != 0:
+        raise ValueError("sequence length must be divisible by cp")
+    rows = []
+    t = rank
+    while t < seq_len:
+        rows.append(t)
+        t += cp
     return np.asarray(rows, dtype=np.int64)
 
 

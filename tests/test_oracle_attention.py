@@ -328,3 +328,72 @@ def test_packed_documents_do_not_interact():
     for a, b in zip(cu[:-1], cu[1:]):
         oo, ll = A.attention_fwd(q[a:b], k[a:b], v[a:b])
         assert np.max(np.abs(o[a:b] - oo)) < 1e-14 and np.max(np.abs(lse[a:b] - ll)) < 1e-14
+
+
+# ---------------------------------------------------------------- dK/dV at chosen keys
+def _torch_share_grads(q, k, v, g, qpos, kpos, qdoc=None, kdoc=None, scale=None):
+    """dK, dV of sum(G∘O) for queries at positions qpos against every key, by float64
+    autograd over an explicitly masked softmax (an independent formulation)."""
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    tk_ = torch.from_numpy(k).requires_grad_()
+    tv_ = torch.from_numpy(v).requires_grad_()
+    vis = torch.from_numpy(kpos)[None, :] <= torch.from_numpy(qpos)[:, None]
+    if qdoc is not None:
+        vis &= torch.from_numpy(kdoc)[None, :] == torch.from_numpy(qdoc)[:, None]
+    loss = 0.0
+    for h in range(hq):
+        s = scale * torch.from_numpy(q[:, h, :]) @ tk_[:, h // grp, :].T
+        s = s.masked_fill(~vis, -math.inf)
+        p = torch.softmax(s, dim=1).nan_to_num(0.0)
+        loss = loss + (p @ tv_[:, h // grp, :] * torch.from_numpy(g[:, h, :])).sum()
+    loss.backward()
+    return tk_.grad.numpy(), tv_.grad.numpy()
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 2)])
+def test_bwd_keys_against_autograd_for_a_rank_share(hq, hkv):
+    seq, cp, r, d = 48, 3, 1, 8
+    q, k, v = rnd((seq, hq, d), 51), rnd((seq, hkv, d), 52), rnd((seq, hkv, d), 53)
+    rows = P.zigzag_indices(seq, cp, r)
+    g = rnd((len(rows), hq, d), 54)
+    keys = np.array([0, 5, 8, 15, 16, 23, 31, 40, 47])   # the last ones no local query sees
+    dk, dv = A.attention_bwd_keys(q[rows], k, v, g, keys, rows, np.arange(seq))
+    dk_t, dv_t = _torch_share_grads(q[rows], k, v, g, rows, np.arange(seq))
+    assert np.max(np.abs(dk - dk_t[keys])) < 1e-12
+    assert np.max(np.abs(dv - dv_t[keys])) < 1e-12
+    # rank 1 of cp=3 holds chunks 1 and 4 (positions 8..15 and 32..39): keys after 39
+    # are seen by nobody, and their gradients are exactly zero
+    assert np.all(dk[-2:] == 0) and np.all(dv[-2:] == 0)
+    assert np.max(np.abs(dk[:3])) > 0.1
+
+
+def test_bwd_keys_document_mask_against_autograd():
+    rng = np.random.default_rng(61)
+    cu = [0, 16, 40, 48]
+    t, hq, hkv, d = 48, 2, 2, 4
+    q, k, v = (rng.standard_normal((t, h, d)) for h in (hq, hkv, hkv))
+    rows = P.thd_indices(cu, 2, 0)
+    qdoc = P.thd_doc_ids(cu, rows)
+    kdoc = P.thd_doc_ids(cu, np.arange(t))
+    g = rng.standard_normal((len(rows), hq, d))
+    keys = np.array([0, 3, 15, 16, 20, 39, 40, 47])
+    args = dict(q_doc=qdoc, k_doc=kdoc, mask=A.MASK_CAUSAL_DOC)
+    dk, dv = A.attention_bwd_keys(q[rows], k, v, g, keys, rows, np.arange(t), **args)
+    dk_t, dv_t = _torch_share_grads(q[rows], k, v, g, rows, np.arange(t), qdoc, kdoc)
+    assert np.max(np.abs(dk - dk_t[keys])) < 1e-12
+    assert np.max(np.abs(dv - dv_t[keys])) < 1e-12
+
+
+def test_bwd_keys_with_given_forward_matches_full_backward_rows():
+    seq, hq, hkv, d = 40, 2, 1, 4
+    q, k, v, g = rnd((seq, hq, d), 71), rnd((seq, hkv, d), 72), rnd((seq, hkv, d), 73), rnd((seq, hq, d), 74)
+    o, lse = A.attention_fwd(q, k, v)
+    keys = np.arange(0, seq, 3)
+    dk1, dv1 = A.attention_bwd_keys(q, k, v, g, keys, o=o, lse=lse)
+    dk2, dv2 = A.attention_bwd_keys(q, k, v, g, keys)
+    _, dk_f, dv_f = A.attention_bwd(q, k, v, g)
+    assert np.array_equal(dk1, dk2) and np.array_equal(dv1, dv2)
+    assert np.max(np.abs(dk1 - dk_f[keys])) < 1e-13 and np.max(np.abs(dv1 - dv_f[keys])) < 1e-13

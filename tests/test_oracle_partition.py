@@ -128,3 +128,44 @@ def test_thd_alignment_errors():
         P.thd_indices([0, 12], 4, 0)
     with pytest.raises(ValueError):
         P.thd_indices([0, 16, 8], 2, 0)
+
+
+# ---------------------------------------------------------------- striped split
+def test_striped_matches_printed_interleave():
+    g = json.load(open(os.path.join(GOLDEN, "striped_cp4.json")))
+    for r, prefix in g["printed_prefixes"].items():
+        got = P.striped_indices(64, g["cp"], int(r))
+        assert got[: len(prefix)].tolist() == prefix
+
+
+@pytest.mark.parametrize("seq,cp", [(64, 4), (8192, 4), (48, 3), (8, 1), (24, 8)])
+def test_striped_union_is_permutation_and_ascending(seq, cp):
+    parts = [P.striped_indices(seq, cp, r) for r in range(cp)]
+    assert all(np.all(np.diff(p) > 0) for p in parts)
+    assert all(len(p) == seq // cp for p in parts)
+    assert np.array_equal(np.sort(np.concatenate(parts)), np.arange(seq))
+
+
+@pytest.mark.parametrize("seq,cp", [(64, 4), (96, 3), (8192, 4)])
+def test_striped_pair_counts(seq, cp):
+    # rank r holds positions r + cp t, t < n = seq / cp; each sees its prefix of keys:
+    # n (r + 1) + cp n (n - 1) / 2 visible pairs, so rank r + 1 carries n more pairs
+    # than rank r (nearly balanced, unlike the exact balance of the zigzag split)
+    n = seq // cp
+    from oracle import attention as A
+    counts = []
+    for r in range(cp):
+        rows = P.striped_indices(seq, cp, r)
+        want = n * (r + 1) + cp * n * (n - 1) // 2
+        if seq <= 128:
+            assert int(A.visible_mask(rows, np.arange(seq)).sum()) == want
+        assert int(np.sum(rows + 1)) == want
+        counts.append(want)
+    assert counts[-1] - counts[0] == (cp - 1) * n
+
+
+def test_striped_alignment_errors():
+    with pytest.raises(ValueError):
+        P.striped_indices(10, 4, 0)
+    with pytest.raises(ValueError):
+        P.striped_indices(16, 4, 4)
