@@ -13,9 +13,11 @@ zigzag rank; forward 4*d per pair per head (QK^T and PV), backward 10*d (five
 contractions).  value = useful FLOPs of the step (two forwards + one backward) / time.
 The backward runs as its three calls (delta, dQ, dK/dV) so each is timed on its own.
 
-Prints one JSON line (rank 0).  ``--workload s128k`` runs the 128K share instead;
-``--workload thd64k`` a packed stream of 65536 tokens in documents of lognormal
-lengths, split per document (zigzag inside each document, cp=4, rank 1 by default),
+Prints one JSON line (rank 0); for the 8K share the other three ranks are timed the
+same way after it and reported as ``per_rank_tflops`` (min and mean over the ranks).
+``--workload s128k`` runs the 128K share instead; ``--workload thd64k`` a packed stream
+of 65536 tokens in documents of lognormal lengths, split per document (zigzag inside
+each document, cp=4, rank 1 by default),
 with the document mask; its visible pairs are counted per row from the partition's
 position and document outputs.
 ``--copy-mib N`` only runs a plain device copy of N MiB (``--steps`` times): the
@@ -117,67 +119,89 @@ def main():
     cu = workloads.cu_seqlens_from_lengths(workloads.thd_lengths(w.seed)) if w.packed else None
     cu_dev = torch.as_tensor(cu, dtype=torch.int32, device=dev) if w.packed else None
     part_mode = C.PART_THD if w.packed else C.PART_ZIGZAG
-    rs = build_rank_share(gq, gk, gv, w.cp, r, cu)
     n_local = w.seq // w.cp
-    g = workloads.randn((n_local, w.hq, w.d), 5, "bf16", 3).to(dev)
-    edges, parts = rs.alloc_tile_buffers(gran)
-    o_t = torch.empty_like(rs.q)
-    l_t = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
-    o_s = torch.empty_like(rs.q)
-    l_s = torch.empty_like(l_t)
-    dq, dk, dv, _ = rs.alloc_bwd_buffers(gran)
-    desc = rs.desc()
-    qblk = C.q_block(rs.q, rs.q_idx, rs.q_doc)
-    bsegs = [s_ for s_, _, _ in rs.segments(gran)]
-    delta = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
-    ws_dq = torch.empty(max(1, C.cpattn_bwd_dq_workspace_bytes(desc, qblk, bsegs)), dtype=torch.uint8, device=dev)
-    ws_tile = rs.tile_workspace(edges)
-    ws_stream = rs.stream_workspace(gran)
-    # partition outputs of this rank (Q and its own K/V shard), rewritten every step
-    p_idx = torch.empty(n_local, dtype=torch.int32, device=dev)
-    p_doc = torch.empty(n_local, dtype=torch.int32, device=dev) if w.packed else None
-    p_out = [torch.empty((n_local,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in (gq, gk, gv)]
-
     names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
-    ev = {n: [] for n in names}
 
-    def step(timed):
-        marks = []
+    def share_steps(rank):
+        """Buffers of one rank's share and the function running one step of it."""
+        rs = build_rank_share(gq, gk, gv, w.cp, rank, cu)
+        g = workloads.randn((n_local, w.hq, w.d), 5, "bf16", 3).to(dev)
+        edges, parts = rs.alloc_tile_buffers(gran)
+        o_t = torch.empty_like(rs.q)
+        l_t = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
+        o_s = torch.empty_like(rs.q)
+        l_s = torch.empty_like(l_t)
+        dq, dk, dv, _ = rs.alloc_bwd_buffers(gran)
+        desc = rs.desc()
+        qblk = C.q_block(rs.q, rs.q_idx, rs.q_doc)
+        bsegs = [s_ for s_, _, _ in rs.segments(gran)]
+        delta = torch.empty((n_local, w.hq), dtype=torch.float32, device=dev)
+        ws_dq = torch.empty(max(1, C.cpattn_bwd_dq_workspace_bytes(desc, qblk, bsegs)), dtype=torch.uint8,
+                            device=dev)
+        ws_tile = rs.tile_workspace(edges)
+        ws_stream = rs.stream_workspace(gran)
+        # partition outputs of this rank (Q and its own K/V shard), rewritten every step
+        p_idx = torch.empty(n_local, dtype=torch.int32, device=dev)
+        p_doc = torch.empty(n_local, dtype=torch.int32, device=dev) if w.packed else None
+        p_out = [torch.empty((n_local,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in (gq, gk, gv)]
+        ev = {n: [] for n in names}
 
-        def mark():
+        def step(timed):
+            marks = []
+
+            def mark():
+                if timed:
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record()
+                    marks.append(e)
+
+            mark()
+            C.cpattn_partition(part_mode, w.seq, w.cp, rank, p_idx, p_doc, [gq, gk, gv], p_out, cu, cu_dev)
+            mark()
+            rs.tile_fwd(edges, parts, workspace=ws_tile)
+            mark()
+            rs.merge(edges, parts, o_t, l_t)
+            mark()
+            rs.stream_fwd(gran, o_s, l_s, workspace=ws_stream)
+            mark()
+            C.cpattn_bwd_delta(desc, o_s, g, delta)
+            mark()
+            C.cpattn_bwd_dq(desc, qblk, bsegs, l_s, delta, g, dq, ws_dq)
+            mark()
+            C.cpattn_bwd_dkdv(desc, qblk, bsegs, l_s, delta, g, dk, dv)
+            mark()
             if timed:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record()
-                marks.append(e)
+                for i, n in enumerate(names):
+                    ev[n].append((marks[i], marks[i + 1]))
 
-        mark()
-        C.cpattn_partition(part_mode, w.seq, w.cp, r, p_idx, p_doc, [gq, gk, gv], p_out, cu, cu_dev)
-        mark()
-        rs.tile_fwd(edges, parts, workspace=ws_tile)
-        mark()
-        rs.merge(edges, parts, o_t, l_t)
-        mark()
-        rs.stream_fwd(gran, o_s, l_s, workspace=ws_stream)
-        mark()
-        C.cpattn_bwd_delta(desc, o_s, g, delta)
-        mark()
-        C.cpattn_bwd_dq(desc, qblk, bsegs, l_s, delta, g, dq, ws_dq)
-        mark()
-        C.cpattn_bwd_dkdv(desc, qblk, bsegs, l_s, delta, g, dk, dv)
-        mark()
-        if timed:
-            for i, n in enumerate(names):
-                ev[n].append((marks[i], marks[i + 1]))
+        info = dict(rs=rs, edges=edges, split_t=ws_tile is not None, split_s=ws_stream is not None,
+                    split_q=ws_dq.numel() > 1)
+        return step, ev, info
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed_run(step):
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
+    step, ev, info = share_steps(r)
+    wall = timed_run(step)
+    rs, edges = info["rs"], info["edges"]
+    # the workload's other ranks (every rank of the 8K share) carry the same visible
+    # pairs; each is timed the same way after the headline rank
+    other_ranks = {}
+    if not w.packed and args.rank is None:
+        for rr in w.ranks:
+            if rr == r:
+                continue
+            st, ev_r, _ = share_steps(rr)
+            timed_run(st)
+            other_ranks[rr] = sum(float(np.mean([a.elapsed_time(b) for a, b in ev_r[n]])) for n in names)
+            del st, ev_r
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
     step_ms = sum(ms.values())
     bwd_ms = ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"]
@@ -202,9 +226,7 @@ def main():
     delta_bytes = n_local * w.hq * (2 * w.d * elt + 4)
     # call -> (kernel launches, bound, algorithmic work, unit); the forward calls add a
     # merge launch when their plan splits the KV tiles, the dQ call a sum launch
-    split_t = ws_tile is not None
-    split_s = ws_stream is not None
-    split_q = ws_dq.numel() > 1
+    split_t, split_s, split_q = info["split_t"], info["split_s"], info["split_q"]
     calls = {
         "partition": (1, "hbm", part_bytes),
         "tile_fwd": (1 + split_t, "mfma", f_fwd),
@@ -246,6 +268,9 @@ def main():
                    "seq_len": w.seq, "cp": w.cp, "rank": r, "hq": w.hq, "hkv": w.hkv, "d": w.d,
                    "visible_pairs_per_head": pairs},
         "pct_bf16_peak": round(100 * tflops(step_flops, step_ms) / PEAK_BF16_TFLOPS, 2),
+        "forward_target": {"kernel": "stream_fwd", "frac_of_bf16_peak": round(tflops(f_fwd, ms["stream_fwd"])
+                                                                             / PEAK_BF16_TFLOPS, 4),
+                           "target_frac": 0.5},
         "per_kernel": {n: {kk: round(vv, 2) for kk, vv in d_.items()} for n, d_ in per_kernel.items()},
         "bwd_tflops": round(tflops(f_bwd, bwd_ms), 2),
         "fwd_tflops": {"tile+merge": round(tflops(f_fwd, ms["tile_fwd"] + ms["merge"]), 2),
@@ -255,6 +280,12 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, args.workload),
                      "algorithmic": work},
     }
+    if other_ranks:
+        per_rank = {r: round(tflops(step_flops, step_ms), 3)}
+        per_rank.update({rr: round(tflops(step_flops, t), 3) for rr, t in other_ranks.items()})
+        vals = [per_rank[x] for x in sorted(per_rank)]
+        out["per_rank_tflops"] = {"ranks": {str(x): per_rank[x] for x in sorted(per_rank)},
+                                  "min": min(vals), "mean": round(sum(vals) / len(vals), 3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, w, r, cu)
     print(json.dumps(out), flush=True)

@@ -174,11 +174,18 @@ def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out,
     _check(st, "cpattn_partition")
 
 
-def _workspace(nbytes, like):
-    """A device buffer of ``nbytes`` (None for 0), allocated through torch."""
+def _workspace(nbytes, like, stream=None):
+    """A device buffer of ``nbytes`` (None for 0), allocated through torch on the stream
+    the kernels will run on: when the caller drops it, torch's caching allocator only
+    hands the block to later work of that same stream, which runs after the kernels."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=like.device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
 
 
 def _ws_args(ws):
@@ -204,7 +211,8 @@ def cpattn_tile_fwd(desc: cpattn_attn_desc, q_blocks, segs, o_parts, lse_parts, 
     if not (len(segs) == len(o_parts) == len(lse_parts) == n):
         raise ValueError("one q block, segment, O and LSE buffer per edge")
     if isinstance(workspace, str):
-        workspace = _workspace(cpattn_tile_fwd_workspace_bytes(desc, q_blocks, segs), o_parts[0]) if n else None
+        workspace = (_workspace(cpattn_tile_fwd_workspace_bytes(desc, q_blocks, segs), o_parts[0], stream)
+                     if n else None)
     qa = (cpattn_q_block * max(1, n))(*q_blocks)
     sa = (cpattn_kv_seg * max(1, n))(*segs)
     wp, wb = _ws_args(workspace)
@@ -235,7 +243,8 @@ def cpattn_stream_fwd(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o_out, ls
 
     ``workspace`` as for cpattn_tile_fwd (cpattn_stream_fwd_workspace_bytes)."""
     if isinstance(workspace, str):
-        workspace = _workspace(cpattn_stream_fwd_workspace_bytes(desc, q, segs), o_out) if o_out is not None else None
+        workspace = (_workspace(cpattn_stream_fwd_workspace_bytes(desc, q, segs), o_out, stream)
+                     if o_out is not None else None)
     sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
     wp, wb = _ws_args(workspace)
     st = lib.cpattn_stream_fwd(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o_out),

@@ -316,9 +316,11 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
     }
   }
 
-  // finalize: combine the two lane halves' partial sums, normalise, store
+  // finalize: combine the two lane halves' partial sums, normalise, store.  A row that
+  // saw a key has l >= 2^-8 (its largest score contributes at least that), so l == 0
+  // means no visible key; a NaN input makes l NaN, which must reach O and the LSE.
   const float lt = half_sum(l);
-  const bool live = lt > 0.0f;
+  const bool live = !(lt == 0.0f);
   const float inv = live ? 1.0f / lt : 0.0f;
   const float lse = live ? (m + fast_log2(lt)) * kLn2 : neg_inf();
   if (row_ok) {
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdArgs a) {
     }
   }
   if (!row_ok) return;
-  const bool live = l > 0.0f;
+  const bool live = !(l == 0.0f);  // NaN inputs stay NaN
   const float inv = live ? 1.0f / l : 0.0f;
   const int64_t off = ((int64_t)row * a.hq + head) * D;
   float* out = reinterpret_cast<float*>(job.o) + off;  // fp32 in both modes

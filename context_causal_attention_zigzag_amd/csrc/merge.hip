@@ -3,7 +3,8 @@
 // "Context Parallelism (CP)", section 2.2: for one query row,
 //   L = log sum_j exp(L_j),   O = sum_j exp(L_j - L) O_j,
 // valid in any order and grouping.  Parts with L_j = -inf (no visible key) carry no
-// weight; a row whose parts are all -inf becomes (0, -inf).
+// weight; a row whose parts are all -inf becomes (0, -inf); a part whose L_j is NaN
+// (a NaN among its inputs) makes the row NaN.
 //
 // Bandwidth-bound: each (row, head) pair is handled by d/4 threads that each own a
 // 16-byte slice of the head vector, so the n partial outputs stream through in
@@ -39,6 +40,7 @@ struct MergeArgs {
 template <bool SUM, int kU, bool LAZY, class L, class O>
 __device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse_out) {
   float m = neg_inf(), s = 0.0f;
+  bool nan_part = false;  // a NaN LSE: the merged state is NaN (fmaxf would drop it)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < n; p0 += kU) {
     float lv[kU];
@@ -63,6 +65,8 @@ __device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse
     float bm = lv[0];
 #pragma unroll
     for (int u = 1; u < kU; ++u) bm = fmaxf(bm, lv[u]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) nan_part |= __builtin_isnan(lv[u]);
     const float m_new = fmaxf(m, bm);
     if (m_new == neg_inf()) continue;
     const float c = fast_exp2((m - m_new) * kLog2e);  // 0 while m is -inf
@@ -80,6 +84,10 @@ __device__ __forceinline__ f32x4 merge_slice(int n, L lse_of, O o_of, float& lse
   if (SUM) {
     lse_out = 0.0f;
     return acc;
+  }
+  if (nan_part) {
+    lse_out = __builtin_nanf("");
+    return f32x4{lse_out, lse_out, lse_out, lse_out};
   }
   if (!(s > 0.0f)) {
     lse_out = neg_inf();

@@ -207,13 +207,17 @@ def stream_fwd(q, segments, q_pos=None, q_doc=None, mask=MASK_CAUSAL, scale=None
 
 
 def attention_bwd(q, k, v, g, q_pos=None, k_pos=None, q_doc=None, k_doc=None,
-                  mask=MASK_CAUSAL, scale=None):
+                  mask=MASK_CAUSAL, scale=None, o_saved=None):
     """Gradients of sum(G ∘ O) with O = attention_fwd(q, k, v).  Returns (dQ, dK, dV).
 
     The forward (O, LSE) is recomputed here in float64; then per visible pair
     P_ij = exp(S_ij − LSE_i), D_i = Σ_d G_i·O_i, dP_ij = G_i·v_j, dS_ij = P_ij(dP_ij − D_i),
     dQ_i = scale Σ_j dS_ij k_j, dK_j = scale Σ_i dS_ij q_i, dV_j = Σ_i P_ij G_i.
-    dK/dV of a kv head sum over its query heads.  Rows with no visible key give zero."""
+    dK/dV of a kv head sum over its query heads.  Rows with no visible key give zero.
+
+    ``o_saved``: the forward output the backward is handed (the teaching page's replay
+    uses the saved full-row output, section 01); D_i is then formed from it, e.g. from
+    an output stored in bf16, instead of from the recomputed O."""
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
@@ -227,6 +231,8 @@ def attention_bwd(q, k, v, g, q_pos=None, k_pos=None, q_doc=None, k_doc=None,
     q_pos, k_pos = _i64(q_pos), _i64(k_pos)
     q_doc, k_doc = _i64(q_doc), _i64(k_doc)
     o, lse = attention_fwd(q, k, v, q_pos, k_pos, q_doc, k_doc, mask, scale)
+    if o_saved is not None:
+        o = _f64(o_saved)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -263,7 +269,8 @@ def attention_bwd_keys(q, k, v, g, key_rows, q_pos=None, k_pos=None, q_doc=None,
     dK_j = scale Σ_i P_ij (G_i·v_j − D_i) q_i and dV_j = Σ_i P_ij G_i, summed over the
     query heads of each kv head (the per-owner sums of the teaching page, section 01,
     for a subset of the owner's keys).  ``o`` / ``lse`` are the full-row forward
-    results of these queries over all of k / v (computed here when not given)."""
+    results of these queries over all of k / v (computed here when not given); a
+    given ``o`` is the saved output D is formed from, as for ``attention_bwd``."""
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
     tq, hq, d = q.shape
     tk, hkv, _ = k.shape
@@ -277,7 +284,9 @@ def attention_bwd_keys(q, k, v, g, key_rows, q_pos=None, k_pos=None, q_doc=None,
     q_pos, k_pos = _i64(q_pos), _i64(k_pos)
     q_doc, k_doc = _i64(q_doc), _i64(k_doc)
     if o is None or lse is None:
-        o, lse = attention_fwd(q, k, v, q_pos, k_pos, q_doc, k_doc, mask, scale)
+        o_f, lse_f = attention_fwd(q, k, v, q_pos, k_pos, q_doc, k_doc, mask, scale)
+        o = o_f if o is None else o
+        lse = lse_f if lse is None else lse
     o, lse = _f64(o), _f64(lse)
     sel = _i64(key_rows)
     kj, vj = k[sel], v[sel]

@@ -397,3 +397,22 @@ def test_bwd_keys_with_given_forward_matches_full_backward_rows():
     _, dk_f, dv_f = A.attention_bwd(q, k, v, g)
     assert np.array_equal(dk1, dk2) and np.array_equal(dv1, dv2)
     assert np.max(np.abs(dk1 - dk_f[keys])) < 1e-13 and np.max(np.abs(dv1 - dv_f[keys])) < 1e-13
+
+
+def test_bwd_saved_output_only_enters_through_d():
+    # D_i = G_i . O_i is the only place the saved output enters: with the exact output
+    # nothing changes; with another output dQ and dK move, dV (= P^T G) does not
+    seq, hq, hkv, d = 30, 2, 1, 4
+    q, k, v, g = rnd((seq, hq, d), 81), rnd((seq, hkv, d), 82), rnd((seq, hkv, d), 83), rnd((seq, hq, d), 84)
+    o, _ = A.attention_fwd(q, k, v)
+    base = A.attention_bwd(q, k, v, g)
+    same = A.attention_bwd(q, k, v, g, o_saved=o)
+    assert all(np.array_equal(a, b) for a, b in zip(base, same))
+    o2 = o + 1e-3 * rnd(o.shape, 85)
+    dq2, dk2, dv2 = A.attention_bwd(q, k, v, g, o_saved=o2)
+    assert np.array_equal(dv2, base[2])
+    assert np.max(np.abs(dq2 - base[0])) > 1e-6 and np.max(np.abs(dk2 - base[1])) > 1e-6
+    # and it matches the chosen-keys form given the same saved output
+    keys = np.arange(0, seq, 4)
+    dk3, dv3 = A.attention_bwd_keys(q, k, v, g, keys, o=o2)
+    assert np.max(np.abs(dk3 - dk2[keys])) < 1e-13 and np.max(np.abs(dv3 - dv2[keys])) < 1e-13
