@@ -88,10 +88,15 @@ lib.cpattn_bwd_dkdv.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32
                                 _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp]
 lib.cpattn_bwd_dkdv.restype = _c_i32
 
+lib.cpattn_bwd_noalloc.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
+                                   _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp]
+lib.cpattn_bwd_noalloc.restype = _c_i32
+
 EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
             "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
             "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
-            "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv")
+            "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
+            "cpattn_bwd_noalloc")
 
 
 class CpattnError(RuntimeError):
@@ -300,3 +305,12 @@ def cpattn_bwd_dkdv(desc: cpattn_attn_desc, q: cpattn_q_block, segs, lse, delta,
                              _ptr(dout), _vp_array([_ptr(x) for x in dk]), _vp_array([_ptr(x) for x in dv]),
                              _stream(stream))
     _check(st, "cpattn_bwd_dkdv")
+
+
+def cpattn_bwd_noalloc(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o, lse, dout, dq, dk, dv, stream=None):
+    """cpattn_bwd with the library's per-device scratch array as its workspace."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    st = lib.cpattn_bwd_noalloc(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o), _ptr(lse),
+                                _ptr(dout), _ptr(dq), _vp_array([_ptr(x) for x in dk]),
+                                _vp_array([_ptr(x) for x in dv]), _stream(stream))
+    _check(st, "cpattn_bwd_noalloc")

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/cpattn.h"
 
@@ -469,3 +470,51 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// The backward for callers that cannot allocate (graph capture, serving loops): its
+// workspace is a file-scope device array.  In host code `scratch` names a host-side
+// stand-in, not device memory; the device address comes from hipGetSymbolAddress,
+// once per device (each device holds its own copy), and only that address is ever
+// handed to kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[CPATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on first use).
+int current_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CPATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CPATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CPATTN_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return CPATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int cpattn_bwd_noalloc(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                                  const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout,
+                                  float* dq, float* const* dk, float* const* dv, void* stream) {
+  const int st = check_bwd_problem(desc, q, n_segs, segs);
+  if (st != CPATTN_OK) return st;
+  if (bwd_delta_bytes(desc, q->len) > (size_t)CPATTN_NOALLOC_SCRATCH_BYTES) return CPATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (q->len > 0) {
+    const int sst = current_scratch(&ws);
+    if (sst != CPATTN_OK) return sst;
+  }
+  // the per-row values are rewritten by every call before they are read, and every
+  // split of the dQ pass writes its partial and its flag, so nothing needs clearing
+  return cpattn_bwd(desc, q, n_segs, segs, o, lse, dout, dq, dk, dv, ws,
+                    q->len > 0 ? (size_t)CPATTN_NOALLOC_SCRATCH_BYTES : 0, stream);
+}

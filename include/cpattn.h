@@ -21,9 +21,10 @@
  *    entries; a violated precondition gives wrong masks but never an out-of-bounds
  *    access.
  *  - Grouped queries: q head h reads kv head h / (Hq / Hkv).
- *  - The library keeps no global state and allocates no device memory.  All
- *    device buffers belong to the caller; host arrays are read only during the
- *    call.  Work is enqueued asynchronously on `stream`; every argument the host
+ *  - The library allocates no device memory and keeps no state between calls,
+ *    except the fixed per-device scratch array behind cpattn_bwd_noalloc (held from
+ *    library load on).  All other device buffers belong to the caller; host arrays
+ *    are read only during the call.  Work is enqueued asynchronously on `stream`; every argument the host
  *    can see is validated first, and on any error nothing is enqueued.
  *  - Outputs are overwritten, never accumulated across calls.
  *  - A row that sees no key at all gets O = 0 and LSE = -inf (never NaN).
@@ -303,6 +304,26 @@ size_t cpattn_bwd_dq_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_
 int cpattn_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                     const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
                     float* const* dk, float* const* dv, void* stream);
+
+/*
+ * cpattn_bwd_noalloc — cpattn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, rules, outputs and errors as cpattn_bwd, without the
+ * workspace: the call uses a device array inside the library of
+ * CPATTN_NOALLOC_SCRATCH_BYTES bytes, one per device, held from library load until
+ * the process ends, and allocates nothing itself.
+ *  - The array of the current device is used; `stream` must belong to that device.
+ *  - Inputs whose per-row values (q.len * hq * 4 bytes, rounded up to 256) exceed
+ *    the array return CPATTN_ERR_WORKSPACE; when the dQ pass's split plan does not
+ *    fit beside them, the pass runs unsplit (results agree to rounding).
+ *  - Every call on a device shares that device's array, which keeps the last call's
+ *    contents: calls that overlap in time on one device (other streams, other host
+ *    threads) race and must be serialised by the caller.
+ */
+#define CPATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int cpattn_bwd_noalloc(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                       const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout,
+                       float* dq, float* const* dk, float* const* dv, void* stream);
 
 #ifdef __cplusplus
 }

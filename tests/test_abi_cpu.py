@@ -211,3 +211,19 @@ def test_bwd_pass_calls_validation():
                                None) == C.ERR_ALIGN
     assert lib.cpattn_bwd_dkdv(ctypes.byref(f32), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, p, p,
                                None) == C.ERR_UNSUPPORTED
+
+
+def test_bwd_noalloc_validation():
+    # rejected on the host before any device work: dtype, sizes, and per-row values
+    # larger than the library's scratch array (CPATTN_NOALLOC_SCRATCH_BYTES, 64 MiB)
+    d, f32 = desc(), desc(dtype=C.F32)
+    s = (C.cpattn_kv_seg * 1)(sg())
+    p = (ctypes.c_void_p * 1)(FAKE)
+    rest = (FAKE, FAKE, FAKE, FAKE, p, p, None)
+    assert C.lib.cpattn_bwd_noalloc(ctypes.byref(f32), ctypes.byref(qb(64)), 1, s, *rest) == C.ERR_UNSUPPORTED
+    assert C.lib.cpattn_bwd_noalloc(ctypes.byref(d), ctypes.byref(qb(-1)), 1, s, *rest) == C.ERR_ARG
+    wide = desc(hq=64, hkv=8)
+    rows = (64 << 20) // (64 * 4) + 1
+    assert C.lib.cpattn_bwd_noalloc(ctypes.byref(wide), ctypes.byref(qb(rows)), 1, s, *rest) == C.ERR_WORKSPACE
+    text = open(HEADER).read()
+    assert "#define CPATTN_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
