@@ -122,9 +122,10 @@ def main():
     n_local = w.seq // w.cp
     names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
 
-    def share_steps(rank):
+    def share_steps(rank, striped=False):
         """Buffers of one rank's share and the function running one step of it."""
-        rs = build_rank_share(gq, gk, gv, w.cp, rank, cu)
+        rs = build_rank_share(gq, gk, gv, w.cp, rank, cu, striped=striped)
+        mode = C.PART_STRIPED if striped else part_mode
         g = workloads.randn((n_local, w.hq, w.d), 5, "bf16", 3).to(dev)
         edges, parts = rs.alloc_tile_buffers(gran)
         o_t = torch.empty_like(rs.q)
@@ -156,7 +157,7 @@ def main():
                     marks.append(e)
 
             mark()
-            C.cpattn_partition(part_mode, w.seq, w.cp, rank, p_idx, p_doc, [gq, gk, gv], p_out, cu, cu_dev)
+            C.cpattn_partition(mode, w.seq, w.cp, rank, p_idx, p_doc, [gq, gk, gv], p_out, cu, cu_dev)
             mark()
             rs.tile_fwd(edges, parts, workspace=ws_tile)
             mark()
@@ -175,8 +176,11 @@ def main():
                     ev[n].append((marks[i], marks[i + 1]))
 
         info = dict(rs=rs, edges=edges, split_t=ws_tile is not None, split_s=ws_stream is not None,
-                    split_q=ws_dq.numel() > 1)
+                    split_q=ws_dq.numel() > 1, p_idx=p_idx, p_doc=p_doc, p_out=p_out)
         return step, ev, info
+
+    def mean_ms(pairs_of_events):
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs_of_events]))
 
     def timed_run(step):
         for _ in range(args.warmup):
@@ -200,9 +204,37 @@ def main():
                 continue
             st, ev_r, _ = share_steps(rr)
             timed_run(st)
-            other_ranks[rr] = sum(float(np.mean([a.elapsed_time(b) for a, b in ev_r[n]])) for n in names)
+            other_ranks[rr] = sum(mean_ms(ev_r[n]) for n in names)
             del st, ev_r
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+
+    # Rotary embedding fused into the gather (Q and K rotated at the rows' positions, V
+    # copied), timed like the plain partition, after the step loop
+    rope = C.rope_desc((0, 1), torch.bfloat16, w.d)
+    rope_ev = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        C.cpattn_partition(part_mode, w.seq, w.cp, r, info["p_idx"], info["p_doc"], [gq, gk, gv], info["p_out"], cu,
+                           cu_dev, rope=rope)
+        e1.record()
+        if i >= args.warmup:
+            rope_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    rope_ms = mean_ms(rope_ev)
+
+    # the striped split against the zigzag split on every rank of the 8K share: visible
+    # pairs per rank and the time of the same step
+    striped_cmp = None
+    if not w.packed and args.rank is None and len(w.ranks) == w.cp:
+        st_ms, st_pairs = {}, {}
+        for rr in w.ranks:
+            st, ev_r, inf = share_steps(rr, striped=True)
+            timed_run(st)
+            st_ms[rr] = sum(mean_ms(ev_r[n]) for n in names)
+            st_pairs[rr] = int((inf["rs"].q_idx.cpu().numpy().astype(np.int64) + 1).sum())
+            del st, ev_r, inf
+        striped_cmp = (st_ms, st_pairs)
+    ms = {n: mean_ms(ev[n]) for n in names}
     step_ms = sum(ms.values())
     bwd_ms = ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"]
     if w.packed:
@@ -242,6 +274,8 @@ def main():
         per_kernel[n] = {"us": ms[n] * 1e3, ("GB/s" if bound == "hbm" else "TFLOP/s"): rate,
                          "launches": launches}
     per_kernel["bwd"] = {"us": bwd_ms * 1e3, "TFLOP/s": tflops(f_bwd, bwd_ms)}
+    per_kernel["partition_rope"] = {"us": rope_ms * 1e3, "GB/s": gbs(part_bytes, rope_ms), "launches": 2,
+                                    "note": "outside the step: Q and K rotated, V copied"}
     # roofline of the dominant kernel: the longest call that is one launch
     dom = max((n for n in calls if calls[n][0] == 1), key=lambda n: ms[n])
     _, bound, work = calls[dom]
@@ -271,7 +305,8 @@ def main():
         "forward_target": {"kernel": "stream_fwd", "frac_of_bf16_peak": round(tflops(f_fwd, ms["stream_fwd"])
                                                                              / PEAK_BF16_TFLOPS, 4),
                            "target_frac": 0.5},
-        "per_kernel": {n: {kk: round(vv, 2) for kk, vv in d_.items()} for n, d_ in per_kernel.items()},
+        "per_kernel": {n: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in d_.items()}
+                       for n, d_ in per_kernel.items()},
         "bwd_tflops": round(tflops(f_bwd, bwd_ms), 2),
         "fwd_tflops": {"tile+merge": round(tflops(f_fwd, ms["tile_fwd"] + ms["merge"]), 2),
                        "stream": round(tflops(f_fwd, ms["stream_fwd"]), 2)},
@@ -280,6 +315,18 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, args.workload),
                      "algorithmic": work},
     }
+    if striped_cmp is not None:
+        st_ms, st_pairs = striped_cmp
+        zz_ms = {r: step_ms}
+        zz_ms.update(other_ranks)
+        zz_pairs = pairs
+        sp = [st_pairs[x] for x in sorted(st_pairs)]
+        out["striped_vs_zigzag"] = {
+            "visible_pairs_per_head": {"zigzag": [zz_pairs] * w.cp, "striped": sp},
+            "pairs_max_over_min": {"zigzag": 1.0, "striped": round(max(sp) / min(sp), 6)},
+            "step_us": {"zigzag": [round(zz_ms[x] * 1e3, 2) for x in sorted(zz_ms)],
+                        "striped": [round(st_ms[x] * 1e3, 2) for x in sorted(st_ms)]},
+            "note": "same step (partition, tile + merge, stream, backward) per rank; FLOPs differ by the pairs"}
     if other_ranks:
         per_rank = {r: round(tflops(step_flops, step_ms), 3)}
         per_rank.update({rr: round(tflops(step_flops, t), 3) for rr, t in other_ranks.items()})

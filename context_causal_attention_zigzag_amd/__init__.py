@@ -28,7 +28,7 @@ lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_ARG, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
 BF16, F32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_CAUSAL_DOC = 0, 1, 2
-PART_ZIGZAG, PART_THD = 0, 1
+PART_ZIGZAG, PART_THD, PART_STRIPED = 0, 1, 2
 
 _c_i32, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                           ctypes.c_void_p, ctypes.c_size_t)
@@ -37,6 +37,11 @@ _c_i32, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c
 class cpattn_attn_desc(ctypes.Structure):
     _fields_ = [("dtype", _c_i32), ("hq", _c_i32), ("hkv", _c_i32), ("d", _c_i32),
                 ("scale", _c_f32), ("mask", _c_i32)]
+
+
+class cpattn_rope_desc(ctypes.Structure):
+    _fields_ = [("rotate_mask", ctypes.c_uint32), ("dtype", _c_i32), ("d", _c_i32),
+                ("interleaved", _c_i32), ("base", _c_f32)]
 
 
 class cpattn_q_block(ctypes.Structure):
@@ -55,6 +60,10 @@ lib.cpattn_version.restype = _c_i32
 lib.cpattn_partition.argtypes = [_c_i32, _c_i64, _c_i32, _c_i32, _P(_c_i32), _c_vp, _c_i32, _c_vp,
                                  _c_vp, _c_i32, _P(_c_vp), _P(_c_vp), _P(_c_i64), _c_vp]
 lib.cpattn_partition.restype = _c_i32
+lib.cpattn_partition_rope.argtypes = [_c_i32, _c_i64, _c_i32, _c_i32, _P(_c_i32), _c_vp, _c_i32, _c_vp,
+                                      _c_vp, _c_i32, _P(_c_vp), _P(_c_vp), _P(_c_i64), _P(cpattn_rope_desc),
+                                      _c_vp]
+lib.cpattn_partition_rope.restype = _c_i32
 lib.cpattn_tile_fwd.argtypes = [_P(cpattn_attn_desc), _c_i32, _P(cpattn_q_block), _P(cpattn_kv_seg),
                                 _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
 lib.cpattn_tile_fwd.restype = _c_i32
@@ -92,7 +101,7 @@ lib.cpattn_bwd_noalloc.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_
                                    _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp]
 lib.cpattn_bwd_noalloc.restype = _c_i32
 
-EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_tile_fwd",
+EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_partition_rope", "cpattn_tile_fwd",
             "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
             "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
             "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
@@ -159,10 +168,21 @@ def _vp_array(ptrs):
 
 
 # ---- the five calls ---------------------------------------------------------------------
+def rope_desc(rotate=(0, 1), dtype=torch.bfloat16, d: int = 128, interleaved: bool = False,
+              base: float = 10000.0) -> cpattn_rope_desc:
+    """Rotary options of cpattn_partition_rope: ``rotate`` lists the gathered tensors to rotate."""
+    mask = 0
+    for g in rotate:
+        mask |= 1 << g
+    return cpattn_rope_desc(mask, _DT[dtype] if not isinstance(dtype, int) else dtype, d, int(interleaved),
+                            float(base))
+
+
 def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out, doc_out=None,
-                     src=(), dst=(), cu_seqlens_host=None, cu_seqlens_dev=None, stream=None):
-    """Rows of rank ``cp_rank`` (zigzag or per-document) into ``idx_out`` (+ ``doc_out``),
-    and ``dst[g][i] = src[g][idx_out[i]]`` for every tensor pair."""
+                     src=(), dst=(), cu_seqlens_host=None, cu_seqlens_dev=None, stream=None, rope=None):
+    """Rows of rank ``cp_rank`` (zigzag, per-document or striped) into ``idx_out`` (+ ``doc_out``),
+    and ``dst[g][i] = src[g][idx_out[i]]`` for every tensor pair; with ``rope`` (a
+    cpattn_rope_desc) the selected tensors are rotated on the way (cpattn_partition_rope)."""
     if len(src) != len(dst):
         raise ValueError("src and dst must pair up")
     row_bytes = [math.prod(s.shape[1:]) * s.element_size() for s in src]
@@ -172,11 +192,13 @@ def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out,
         vals = [int(x) for x in cu_seqlens_host]
         n_docs = len(vals) - 1
         cu_host = (_c_i32 * len(vals))(*vals)
-    st = lib.cpattn_partition(mode, total, cp_size, cp_rank, cu_host, _ptr(cu_seqlens_dev), n_docs,
-                              _ptr(idx_out), _ptr(doc_out), len(src),
-                              _vp_array([_ptr(s) for s in src]), _vp_array([_ptr(d) for d in dst]),
-                              (_c_i64 * max(1, len(src)))(*row_bytes), _stream(stream))
-    _check(st, "cpattn_partition")
+    args = (mode, total, cp_size, cp_rank, cu_host, _ptr(cu_seqlens_dev), n_docs, _ptr(idx_out), _ptr(doc_out),
+            len(src), _vp_array([_ptr(s) for s in src]), _vp_array([_ptr(d) for d in dst]),
+            (_c_i64 * max(1, len(src)))(*row_bytes))
+    if rope is None:
+        _check(lib.cpattn_partition(*args, _stream(stream)), "cpattn_partition")
+    else:
+        _check(lib.cpattn_partition_rope(*args, ctypes.byref(rope), _stream(stream)), "cpattn_partition_rope")
 
 
 def _workspace(nbytes, like, stream=None):

@@ -165,15 +165,21 @@ const char* cpattn_strerror(int status) {
 
 int cpattn_version(void) { return 100; }
 
-int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
-                     const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, int32_t n_docs,
-                     int32_t* idx_out, int32_t* doc_out, int32_t n_gather, const void* const* src,
-                     void* const* dst, const int64_t* row_bytes, void* stream) {
-  if (mode != CPATTN_PART_ZIGZAG && mode != CPATTN_PART_THD) return CPATTN_ERR_ARG;
+}  // extern "C"
+
+namespace {
+
+// Host checks of a partition call (before any rotation options).
+int check_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                    const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, int32_t n_docs,
+                    int32_t* idx_out, int32_t n_gather, const void* const* src, void* const* dst,
+                    const int64_t* row_bytes) {
+  if (mode != CPATTN_PART_ZIGZAG && mode != CPATTN_PART_THD && mode != CPATTN_PART_STRIPED) return CPATTN_ERR_ARG;
   if (total < 0 || total > INT32_MAX || cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size)
     return CPATTN_ERR_ARG;
   if (n_gather < 0 || n_gather > 8) return CPATTN_ERR_ARG;
-  if (total % (2 * (int64_t)cp_size) != 0) return CPATTN_ERR_ALIGN;
+  const int64_t unit = mode == CPATTN_PART_STRIPED ? (int64_t)cp_size : 2 * (int64_t)cp_size;
+  if (total % unit != 0) return CPATTN_ERR_ALIGN;
   if (mode == CPATTN_PART_THD) {
     if (cu_seqlens_host == nullptr || cu_seqlens_dev == nullptr || n_docs < 1) return CPATTN_ERR_ARG;
     if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_docs] != total) return CPATTN_ERR_ALIGN;
@@ -190,9 +196,54 @@ int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_ra
     if (total > 0 && (src[g] == nullptr || dst[g] == nullptr)) return CPATTN_ERR_ARG;
     if (!aligned16(src[g]) || !aligned16(dst[g])) return CPATTN_ERR_ALIGN;
   }
-  if (total == 0) return CPATTN_OK;
+  return CPATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                     const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, int32_t n_docs,
+                     int32_t* idx_out, int32_t* doc_out, int32_t n_gather, const void* const* src,
+                     void* const* dst, const int64_t* row_bytes, void* stream) {
+  const int st = check_partition(mode, total, cp_size, cp_rank, cu_seqlens_host, cu_seqlens_dev, n_docs, idx_out,
+                                 n_gather, src, dst, row_bytes);
+  if (st != CPATTN_OK || total == 0) return st;
   return hip_status(launch_partition(mode, total, cp_size, cp_rank, cu_seqlens_dev, n_docs, idx_out,
-                                     doc_out, n_gather, src, dst, row_bytes,
+                                     doc_out, n_gather, src, dst, row_bytes, nullptr,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cpattn_partition_rope(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                          const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev, int32_t n_docs,
+                          int32_t* idx_out, int32_t* doc_out, int32_t n_gather, const void* const* src,
+                          void* const* dst, const int64_t* row_bytes, const cpattn_rope_desc* rope,
+                          void* stream) {
+  int st = check_partition(mode, total, cp_size, cp_rank, cu_seqlens_host, cu_seqlens_dev, n_docs, idx_out,
+                           n_gather, src, dst, row_bytes);
+  if (st != CPATTN_OK) return st;
+  if (rope == nullptr) return CPATTN_ERR_ARG;
+  if (n_gather < 32 && (rope->rotate_mask >> n_gather) != 0) return CPATTN_ERR_ARG;
+  if (rope->dtype != CPATTN_BF16 && rope->dtype != CPATTN_F32) return CPATTN_ERR_UNSUPPORTED;
+  if (rope->d < 16 || rope->d > 256 || rope->d % 16 != 0) return CPATTN_ERR_UNSUPPORTED;
+  if (rope->interleaved != 0 && rope->interleaved != 1) return CPATTN_ERR_ARG;
+  if (!std::isfinite(rope->base) || rope->base < 0.0f) return CPATTN_ERR_ARG;
+  const int64_t head_bytes = (int64_t)rope->d * (rope->dtype == CPATTN_F32 ? 4 : 2);
+  for (int g = 0; g < n_gather; ++g) {
+    if (!((rope->rotate_mask >> g) & 1u)) continue;
+    if (row_bytes[g] % head_bytes != 0) return CPATTN_ERR_ALIGN;
+    if (rope_table_entries(rope->d, rope->interleaved, row_bytes[g]) < 0) return CPATTN_ERR_UNSUPPORTED;
+  }
+  if (total == 0) return CPATTN_OK;
+  RopeSpec spec{};
+  spec.mask = rope->rotate_mask;
+  spec.f32 = rope->dtype == CPATTN_F32;
+  spec.d = rope->d;
+  spec.interleaved = rope->interleaved;
+  spec.log2_base = std::log2(rope->base > 0.0f ? (double)rope->base : 10000.0);
+  return hip_status(launch_partition(mode, total, cp_size, cp_rank, cu_seqlens_dev, n_docs, idx_out,
+                                     doc_out, n_gather, src, dst, row_bytes, &spec,
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 

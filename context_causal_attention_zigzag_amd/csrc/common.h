@@ -279,11 +279,24 @@ struct BwdArgs {
   int32_t padded_wgs;
 };
 
+// Rotary embedding applied by the partition gather (validated by the caller).
+struct RopeSpec {
+  uint32_t mask;     // bit g: gathered tensor g is rotated
+  int f32;           // rotated tensors hold fp32 (else bf16)
+  int d;             // head dim: multiple of 16, at most 256
+  int interleaved;   // pairs (2i, 2i+1) instead of (i, i + d/2)
+  double log2_base;  // log2 of the frequency base
+};
+
 // Host-side launchers (defined in the .hip files).
+// mode: 0 zigzag, 1 packed documents (cu_dev), 2 striped.
 hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int32_t* cu_dev,
                             int n_docs, int32_t* idx, int32_t* doc, int n_gather,
                             const void* const* src, void* const* dst, const int64_t* row_bytes,
-                            hipStream_t stream);
+                            const RopeSpec* rope, hipStream_t stream);
+// Entries of the rotation table a block of the rotated gather needs for rows of
+// row_bytes bytes, or -1 when they exceed its LDS table.
+int rope_table_entries(int d, int interleaved, int64_t row_bytes);
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool partial_out, hipStream_t stream);
 // Split plan for forward jobs: fills n_split / tiles_per_split / n_tiles of each job and
 // the segments' tile offsets; returns the workspace bytes the plan needs.

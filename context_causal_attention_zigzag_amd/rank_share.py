@@ -13,7 +13,11 @@ arithmetic runs in libcpattn through the C-ABI calls of this package.
 * Edge set of the Q-KV task graph ("Context Parallelism (CP)", section 2.1): an edge
   (query chunk, KV segment) exists when some key position is <= some query position;
   for zigzag shards the position ranges are known from (S, cp), so empty edges are
-  dropped before launch.  Packed documents keep every edge (the kernels classify).
+  dropped before launch.  Packed documents and striped shards keep every edge (the
+  kernels classify; under the striped split every edge holds visible pairs).
+* Layouts: "zigzag" (chunk pair), "thd" (packed documents, zigzag inside each) and
+  "striped" (rank r holds tokens r, r + cp, ...: the interleaved split of the
+  ring-attention page, section 5).
 """
 from __future__ import annotations
 
@@ -21,7 +25,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (PART_THD, PART_ZIGZAG, MASK_CAUSAL, MASK_CAUSAL_DOC, attn_desc, cpattn_bwd,
+from . import (PART_STRIPED, PART_THD, PART_ZIGZAG, MASK_CAUSAL, MASK_CAUSAL_DOC, attn_desc, cpattn_bwd,
                cpattn_bwd_workspace_bytes, cpattn_merge, cpattn_partition, cpattn_stream_fwd,
                cpattn_stream_fwd_workspace_bytes, cpattn_tile_fwd, cpattn_tile_fwd_workspace_bytes,
                kv_seg, q_block)
@@ -54,6 +58,7 @@ class RankShare:
     q_idx: torch.Tensor                  # their global positions
     q_doc: torch.Tensor | None
     owners: dict = field(default_factory=dict)   # owner -> Shard with [k, v]
+    striped: bool = False
 
     @property
     def mask(self):
@@ -101,7 +106,7 @@ class RankShare:
         out = []
         for (a, b) in self.q_chunks():
             for si, (seg, (o, pi), _) in enumerate(segs):
-                if not self.packed:
+                if not self.packed and not self.striped:
                     _, qhi = self._pos_range_q(a, b)
                     if self._pos_min_seg(o, pi, granularity) > qhi:
                         continue
@@ -186,17 +191,22 @@ def partition_shard(mode, total, cp, owner, tensors, cu_host=None, cu_dev=None, 
     return Shard(owner, idx, doc, outs)
 
 
-def build_rank_share(q_full, k_full, v_full, cp: int, rank: int, cu_seqlens=None) -> RankShare:
-    """Partition the rank's queries and every owner's K/V on the device."""
+def build_rank_share(q_full, k_full, v_full, cp: int, rank: int, cu_seqlens=None,
+                     striped: bool = False) -> RankShare:
+    """Partition the rank's queries and every owner's K/V on the device (zigzag, packed
+    documents when ``cu_seqlens`` is given, or the striped split)."""
     seq, hq, d = q_full.shape
     hkv = k_full.shape[1]
     packed = cu_seqlens is not None
-    mode = PART_THD if packed else PART_ZIGZAG
+    if packed and striped:
+        raise ValueError("the striped split is for one sequence")
+    mode = PART_THD if packed else (PART_STRIPED if striped else PART_ZIGZAG)
     cu_dev = None
     if packed:
         cu_dev = torch.as_tensor(list(cu_seqlens), dtype=torch.int32).to(q_full.device)
     qs = partition_shard(mode, seq, cp, rank, [q_full], cu_seqlens, cu_dev, packed)
-    rs = RankShare(seq, cp, rank, hq, hkv, d, q_full.dtype, packed, qs.tensors[0], qs.idx, qs.doc)
+    rs = RankShare(seq, cp, rank, hq, hkv, d, q_full.dtype, packed, qs.tensors[0], qs.idx, qs.doc,
+                   striped=striped)
     for o in range(cp):
         rs.owners[o] = partition_shard(mode, seq, cp, o, [k_full, v_full], cu_seqlens, cu_dev, packed)
     return rs

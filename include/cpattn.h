@@ -64,6 +64,7 @@ extern "C" {
 
 #define CPATTN_PART_ZIGZAG 0      /* one causal sequence cut into 2*cp chunks */
 #define CPATTN_PART_THD 1         /* packed documents, zigzag inside every document */
+#define CPATTN_PART_STRIPED 2     /* one causal sequence, rank r keeps tokens r, r+cp, r+2cp, ... */
 
 /* Attention problem description shared by the attention calls. */
 typedef struct {
@@ -106,10 +107,14 @@ int cpattn_version(void);
  * and section 1.2 with section 5 (packed THD: the same split inside every
  * document: for a document of length L at offset c, seg = L/(2cp), rows
  * c+[r*seg, (r+1)*seg) then c+[L-(r+1)*seg, L-r*seg); documents in order).
+ * "推理系统基础设施（二）：Sequence Parallelism + Ring Attention", section 5, with
+ * "Context Parallelism (CP)", sections 2.4 and 4 (striped: the interleaved
+ * assignment [0, cp, 2cp, ...], [1, cp+1, ...], per token).
  *
- *  mode             CPATTN_PART_ZIGZAG (cu_seqlens ignored, one document [0,total))
- *                   or CPATTN_PART_THD.
- *  total            tokens of the full (packed) sequence; total % (2*cp) == 0.
+ *  mode             CPATTN_PART_ZIGZAG (cu_seqlens ignored, one document [0,total)),
+ *                   CPATTN_PART_THD or CPATTN_PART_STRIPED (cu_seqlens ignored).
+ *  total            tokens of the full (packed) sequence; total % (2*cp) == 0
+ *                   (striped: total % cp == 0).
  *  cp_size, cp_rank 1 <= cp_size, 0 <= cp_rank < cp_size.
  *  cu_seqlens_host  THD: host int32 [n_docs+1], 0 = cu[0] <= cu[1] <= ... = total,
  *                   every difference divisible by 2*cp (validated on the host).
@@ -131,6 +136,47 @@ int cpattn_partition(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_ra
                      int32_t n_docs, int32_t* idx_out, int32_t* doc_out, int32_t n_gather,
                      const void* const* src, void* const* dst, const int64_t* row_bytes,
                      void* stream);
+
+/* Rotary embedding applied during a partition gather. */
+typedef struct {
+  uint32_t rotate_mask; /* bit g set: gathered tensor g is rotated; the others are copied */
+  int32_t dtype;        /* element type of the rotated tensors: CPATTN_BF16 or CPATTN_F32 */
+  int32_t d;            /* head dim: a multiple of 16, 16..256; a rotated row is
+                           row_bytes / (element size * d) heads, each rotated alike */
+  int32_t interleaved;  /* 0: pairs (x_i, x_{i+d/2}) ("rotate half"); 1: pairs (x_2i, x_2i+1) */
+  float base;           /* theta_i = base^(-2i/d), i = 0 .. d/2-1; 0 means 10000 */
+} cpattn_rope_desc;
+
+/*
+ * cpattn_partition_rope — cpattn_partition whose gather also applies the rotary
+ * position embedding to the tensors rope->rotate_mask selects (typically Q and K).
+ *
+ * Source: "04 · Megatron-LM 实现", section 5: rotary embedding depends on absolute
+ * positions, so the positions must be split exactly like the tokens (the zigzag
+ * chunk pair; per packed document the front and mirrored slices of the frequency
+ * table), and section 9's checklist: a token split and a rotary split that disagree
+ * give a silently wrong loss.  "Context Parallelism (CP)", section 5: positions
+ * restart at 0 in every packed document.
+ *
+ * Each head of a selected row at position p leaves with every pair (a, b) of its
+ * elements replaced by (a cos t - b sin t, b cos t + a sin t), t = p * theta_i, where
+ * p is the row's global index (zigzag, striped) or its index inside its document
+ * (CPATTN_PART_THD).  The angle, its sine and cosine are computed in fp64, the
+ * rotation in fp32, and the result is rounded once to the tensor's dtype (bf16:
+ * round to nearest even).  Unselected tensors are copied bit for bit, as are the
+ * index and document outputs.
+ *
+ *  rope             host pointer; every selected tensor's row_bytes must be a whole
+ *                   number of heads.
+ * Errors: those of cpattn_partition; ARG (rope NULL, rotate_mask naming a tensor
+ * beyond n_gather, interleaved not 0/1, base negative or not finite); UNSUPPORTED
+ * (dtype, d); ALIGN (a selected row not a whole number of heads).
+ */
+int cpattn_partition_rope(int32_t mode, int64_t total, int32_t cp_size, int32_t cp_rank,
+                          const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                          int32_t n_docs, int32_t* idx_out, int32_t* doc_out, int32_t n_gather,
+                          const void* const* src, void* const* dst, const int64_t* row_bytes,
+                          const cpattn_rope_desc* rope, void* stream);
 
 /*
  * cpattn_tile_fwd — TileAttention over a batch of independent (Q block, KV segment)

@@ -6,6 +6,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import context_causal_attention_zigzag_amd as C
 
@@ -227,3 +228,35 @@ def test_bwd_noalloc_validation():
     assert C.lib.cpattn_bwd_noalloc(ctypes.byref(wide), ctypes.byref(qb(rows)), 1, s, *rest) == C.ERR_WORKSPACE
     text = open(HEADER).read()
     assert "#define CPATTN_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+
+
+def test_striped_and_rope_partition_validation():
+    # striped: the length must divide by cp (not 2cp); checked before any launch
+    assert part(C.PART_STRIPED, 10, 4, 0) == C.ERR_ALIGN
+    assert part(3, 64, 2, 0) == C.ERR_ARG
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+
+    def rope_call(rope, row_bytes=(256, 256), n_gather=2):
+        rb = (ctypes.c_int64 * 2)(*row_bytes)
+        return C.lib.cpattn_partition_rope(C.PART_ZIGZAG, 64, 2, 0, None, None, 0, FAKE, None, n_gather, ptrs, ptrs,
+                                           rb, None if rope is None else ctypes.byref(rope), None)
+
+    ok = dict(rotate=(0, 1), dtype=torch.bfloat16, d=128)
+    assert rope_call(None) == C.ERR_ARG
+    assert rope_call(C.rope_desc(rotate=(0, 2))) == C.ERR_ARG            # tensor 2 is not gathered
+    r = C.rope_desc(**ok)
+    r.dtype = 7
+    assert rope_call(r) == C.ERR_UNSUPPORTED
+    assert rope_call(C.rope_desc(rotate=(0,), d=8)) == C.ERR_UNSUPPORTED
+    assert rope_call(C.rope_desc(rotate=(0,), d=72)) == C.ERR_UNSUPPORTED
+    assert rope_call(C.rope_desc(rotate=(0,), d=272)) == C.ERR_UNSUPPORTED
+    r = C.rope_desc(**ok)
+    r.interleaved = 2
+    assert rope_call(r) == C.ERR_ARG
+    assert rope_call(C.rope_desc(base=-1.0, **ok)) == C.ERR_ARG
+    assert rope_call(C.rope_desc(base=float("inf"), **ok)) == C.ERR_ARG
+    assert rope_call(C.rope_desc(**ok), row_bytes=(256, 48)) == C.ERR_ALIGN  # 48 B: not a whole head
+    # the plain partition's own checks come first
+    rb = (ctypes.c_int64 * 1)(256)
+    assert C.lib.cpattn_partition_rope(C.PART_ZIGZAG, 100, 4, 0, None, None, 0, FAKE, None, 1, ptrs, ptrs, rb,
+                                       ctypes.byref(C.rope_desc(**ok)), None) == C.ERR_ALIGN

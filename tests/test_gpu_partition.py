@@ -79,3 +79,19 @@ def test_indices_only(mode):
         assert np.array_equal(idx.cpu().numpy(), want)
         if cu is not None:
             assert np.array_equal(doc.cpu().numpy(), oracle.thd_doc_ids(cu, want))
+
+
+@pytest.mark.parametrize("seq,cp", [(512, 2), (8192, 4), (800, 4), (131072, 8), (48, 3), (64, 1), (12, 4)])
+def test_striped_indices_and_gather(seq, cp):
+    src = torch.arange(seq * 24, dtype=torch.int32).reshape(seq, 3, 8)
+    src2 = torch.randn(seq, 4, dtype=torch.float32)
+    g_src, g_src2 = src.to(DEV), src2.to(DEV)
+    for r in range(cp):
+        say(f"partition striped seq={seq} cp={cp} rank={r}")
+        sh = partition_shard(C.PART_STRIPED, seq, cp, r, [g_src, g_src2], with_doc=True)
+        torch.cuda.synchronize()
+        want = oracle.striped_indices(seq, cp, r)
+        assert np.array_equal(sh.idx.cpu().numpy(), want)
+        assert np.all(sh.doc.cpu().numpy() == 0)
+        assert torch.equal(sh.tensors[0].cpu(), src[torch.as_tensor(want)])
+        assert torch.equal(sh.tensors[1].cpu(), src2[torch.as_tensor(want)])
