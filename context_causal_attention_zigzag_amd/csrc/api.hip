@@ -17,6 +17,22 @@ using namespace cpattn;
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
+// Segments per call; a launch takes kMaxSegs of them, longer lists run as groups (at
+// most 64: the parts of one merge launch).
+constexpr int kMaxSegsTotal = 64 * kMaxSegs;
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int seg_groups(int n_segs) { return (n_segs + kMaxSegs - 1) / kMaxSegs; }
+
+// Workspace of a streaming forward over more than kMaxSegs segments: one fp32 partial
+// state (O and LSE) per group of segments, merged at the end.
+size_t grouped_stream_bytes(const cpattn_attn_desc* desc, int64_t q_len, int n_segs) {
+  if (n_segs <= kMaxSegs) return 0;
+  const size_t o = round256((size_t)q_len * desc->hq * desc->d * sizeof(float));
+  const size_t l = round256((size_t)q_len * desc->hq * sizeof(float));
+  return (size_t)seg_groups(n_segs) * (o + l);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -310,9 +326,10 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
 size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
                                          int32_t n_segs, const cpattn_kv_seg* segs) {
   if (check_desc(desc) != CPATTN_OK || check_qblock(desc, q) != CPATTN_OK) return 0;
-  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr || q->len == 0) return 0;
+  if (n_segs < 1 || n_segs > kMaxSegsTotal || segs == nullptr || q->len == 0) return 0;
   for (int s = 0; s < n_segs; ++s)
     if (check_seg(desc, &segs[s]) != CPATTN_OK) return 0;
+  if (n_segs > kMaxSegs) return grouped_stream_bytes(desc, q->len, n_segs);
   FwdArgs a{};
   fill_common(a, desc);
   fill_stream_job(a, q, n_segs, segs, nullptr, nullptr);
@@ -325,13 +342,41 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   int st = check_desc(desc);
   if (st != CPATTN_OK) return st;
   if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
-  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return CPATTN_ERR_ARG;
+  if (n_segs < 1 || n_segs > kMaxSegsTotal || segs == nullptr) return CPATTN_ERR_ARG;
   for (int s = 0; s < n_segs; ++s)
     if ((st = check_seg(desc, &segs[s])) != CPATTN_OK) return st;
   if (q->len == 0) return CPATTN_OK;
   if (o_out == nullptr || lse_out == nullptr) return CPATTN_ERR_ARG;
   if (!aligned16(o_out)) return CPATTN_ERR_ALIGN;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (n_segs > kMaxSegs) {
+    // groups of kMaxSegs segments, each streamed into its own fp32 partial state, then
+    // the log-sum-exp merge of the groups (the same result up to rounding order)
+    const size_t need = grouped_stream_bytes(desc, q->len, n_segs);
+    if (workspace == nullptr || workspace_bytes < need) return CPATTN_ERR_WORKSPACE;
+    const int ng = seg_groups(n_segs);
+    const size_t ob = round256((size_t)q->len * desc->hq * desc->d * sizeof(float));
+    const size_t lb = round256((size_t)q->len * desc->hq * sizeof(float));
+    const float* o_parts[64];
+    const float* l_parts[64];
+    for (int g = 0; g < ng; ++g) {
+      char* base = reinterpret_cast<char*>(workspace) + (size_t)g * (ob + lb);
+      float* op = reinterpret_cast<float*>(base);
+      float* lp = reinterpret_cast<float*>(base + ob);
+      o_parts[g] = op;
+      l_parts[g] = lp;
+      const int s0 = g * kMaxSegs, cnt = min(kMaxSegs, n_segs - s0);
+      FwdArgs a{};
+      fill_common(a, desc);
+      fill_stream_job(a, q, cnt, segs + s0, op, lp);
+      plan_fwd(a, desc->d, desc->dtype, device_cus(), false, 0);
+      const hipError_t e = launch_fwd(a, desc->d, desc->dtype, true, hs);
+      if (e != hipSuccess) return CPATTN_ERR_HIP;
+    }
+    return hip_status(launch_merge(ng, o_parts, l_parts, q->len, desc->hq, desc->d, desc->dtype, o_out, lse_out,
+                                   hs));
+  }
   FwdArgs a{};
   fill_common(a, desc);
   fill_stream_job(a, q, n_segs, segs, o_out, lse_out);
@@ -339,7 +384,7 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   size_t need = plan_fwd(a, desc->d, desc->dtype, cus, workspace != nullptr, 0);
   if (need > workspace_bytes) need = plan_fwd(a, desc->d, desc->dtype, cus, false, 0);  // too small: no split
   if (need > 0) assign_fwd_workspace(a, desc->d, workspace);
-  return hip_status(launch_fwd(a, desc->d, desc->dtype, false, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_fwd(a, desc->d, desc->dtype, false, hs));
 }
 
 }  // extern "C"
@@ -353,7 +398,7 @@ int check_bwd_problem(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   if (st != CPATTN_OK) return st;
   if (desc->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
   if ((st = check_qblock(desc, q)) != CPATTN_OK) return st;
-  if (n_segs < 1 || n_segs > kMaxSegs || segs == nullptr) return CPATTN_ERR_ARG;
+  if (n_segs < 1 || n_segs > kMaxSegsTotal || segs == nullptr) return CPATTN_ERR_ARG;
   for (int s = 0; s < n_segs; ++s)
     if ((st = check_seg(desc, &segs[s])) != CPATTN_OK) return st;
   return CPATTN_OK;
@@ -382,7 +427,6 @@ int check_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_
                    float* const* dk, float* const* dv) {
   int st = check_bwd_problem(desc, q, n_segs, segs);
   if (st != CPATTN_OK) return st;
-  if (q->len > bwd_max_rows()) return CPATTN_ERR_UNSUPPORTED;
   if ((st = check_bwd_rows(q, lse, delta, dout)) != CPATTN_OK) return st;
   if (dk == nullptr || dv == nullptr) return CPATTN_ERR_ARG;
   for (int s = 0; s < n_segs; ++s) {
@@ -394,11 +438,23 @@ int check_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_
 }
 
 // The dQ pass as one query-major job over the segments; split over KV tiles into the
-// workspace when it holds the plan's partial buffers.
+// workspace when it holds the plan's partial buffers.  More than kMaxSegs segments run
+// as unsplit launches of kMaxSegs segments, each adding its part to dQ.
 hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                       const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
                       float* dq, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (q->len == 0) return hipSuccess;
+  if (n_segs > kMaxSegs) {
+    for (int s0 = 0; s0 < n_segs; s0 += kMaxSegs) {
+      FwdArgs f{};
+      fill_common(f, desc);
+      fill_stream_job(f, q, min(kMaxSegs, n_segs - s0), segs + s0, dq, const_cast<float*>(lse));
+      plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), false, 0);
+      const hipError_t e = launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, s0 > 0, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   FwdArgs f{};
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, dq, const_cast<float*>(lse));
@@ -407,12 +463,20 @@ hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   if (need > 0 && (workspace == nullptr || need > workspace_bytes))
     need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false, 0);  // too small: no split
   if (need > 0) assign_fwd_workspace(f, desc->d, workspace);
-  return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, stream);
+  return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, false, stream);
 }
 
 hipError_t run_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                         const cpattn_kv_seg* segs, const float* lse, const float* delta,
                         const void* dout, float* const* dk, float* const* dv, hipStream_t stream) {
+  if (n_segs > kMaxSegs) {  // segments are independent here: one launch per group
+    for (int s0 = 0; s0 < n_segs; s0 += kMaxSegs) {
+      const hipError_t e = run_bwd_dkdv(desc, q, min(kMaxSegs, n_segs - s0), segs + s0, lse, delta, dout, dk + s0,
+                                        dv + s0, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   BwdArgs a{};
   for (int s = 0; s < n_segs; ++s) {
     a.segs[s] = to_seg(segs[s]);
@@ -438,7 +502,7 @@ hipError_t run_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, i
 
 size_t bwd_dq_split_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                           const cpattn_kv_seg* segs) {
-  if (q->len == 0) return 0;
+  if (q->len == 0 || n_segs > kMaxSegs) return 0;
   FwdArgs f{};
   fill_common(f, desc);
   fill_stream_job(f, q, n_segs, segs, nullptr, nullptr);

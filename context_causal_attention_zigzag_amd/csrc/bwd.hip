@@ -36,7 +36,6 @@ constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per dK/dV work-group (32 per wave)
 constexpr int kBQ = 32;    // query rows per dK/dV step
 constexpr int kPosPad = 0x7fffffff;
-constexpr int kMaxQTiles = 2048;  // query tiles of the LDS range table (65536 local rows)
 
 // ---------------------------------------------------------------------------
 template <int D>
@@ -71,6 +70,7 @@ struct DqExtra {
   const void* dout;
   const float* delta;  // [q_len, hq]
   float scale;         // softmax scale (factor of dS)
+  int32_t accumulate;  // add to the output instead of overwriting it (unsplit jobs)
 };
 
 // One 64-key tile for one wave of the dQ pass, in four phases over the tile's key
@@ -284,13 +284,15 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
     const int h = lane >> 5;
     const int64_t rowoff = ((int64_t)myrow * a.hq + head) * D;
     float* out = nsplit > 1 ? job.ws_o + (int64_t)split * job.len * a.hq * D : reinterpret_cast<float*>(job.o);
+    const bool acc = x.accumulate != 0 && nsplit == 1;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = db * 32 + g * 8 + h * 4;
-        *reinterpret_cast<f32x4*>(out + rowoff + d0) =
-            f32x4{dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]};
+        f32x4 val = {dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]};
+        if (acc) val += *reinterpret_cast<const f32x4*>(out + rowoff + d0);
+        *reinterpret_cast<f32x4*>(out + rowoff + d0) = val;
       }
     }
     if (nsplit > 1 && h == 0) flag_dst[(int64_t)myrow * a.hq + head] = 0.0f;
@@ -328,13 +330,11 @@ struct DkdvSmem {
   alignas(16) bf16 dos[kQBufs][kImage];
 };
 
-// Per-row values of the query tiles and the tile range table: a separate LDS object
-// from the tile images, so that reading them never waits on outstanding image fills.
+// Per-row values of the query tiles: a separate LDS object from the tile images, so
+// that reading them never waits on outstanding image fills.
 struct RowSmem {
   alignas(16) float ld[kQBufs][2][kBQ];    // log-sum-exp, then delta, of the tile's rows
   alignas(16) int32_t pd[kQBufs][2][kBQ];  // positions, then document ids
-  // first/last position and document of every query tile
-  int32_t qtab[4][kMaxQTiles];
 };
 
 // Per-lane source slots of the Q / dO fill instructions: fill instruction jj of a tile
@@ -366,8 +366,18 @@ struct QRange {
   int pmin, pmax, dmin, dmax;
 };
 
-__device__ __forceinline__ QRange qrange(const RowSmem& sm, int t) {
-  return {sm.qtab[0][t], sm.qtab[1][t], sm.qtab[2][t], sm.qtab[3][t]};
+// First / last position (and document) of query tile t, from the query block.
+template <bool DOC>
+__device__ __forceinline__ QRange qrange_global(const BwdArgs& a, int t) {
+  const int q0 = t * kBQ, q1 = min(a.q_len, q0 + kBQ) - 1;
+  return {a.qpos[q0], a.qpos[q1], DOC ? a.qdoc[q0] : 0, DOC ? a.qdoc[q1] : 0};
+}
+
+// The same for the tile whose row values sit in buffer `buf` (its first `nv` rows are
+// real; the rows after them were marked invisible once the fill landed).
+template <bool DOC>
+__device__ __forceinline__ QRange qrange_lds(const RowSmem& sm, int buf, int nv) {
+  return {sm.pd[buf][0][0], sm.pd[buf][0][nv - 1], DOC ? sm.pd[buf][1][0] : 0, DOC ? sm.pd[buf][1][nv - 1] : 0};
 }
 
 // The work-group's items are (head within the group, query tile) for every head and
@@ -662,18 +672,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // per-query-tile position ranges in LDS (n_qt <= kMaxQTiles is checked on the host);
-  // they depend on the query block only, so the second pass keeps the first one's
   const int n_qt = (a.q_len + kBQ - 1) / kBQ;
-  for (int t = tid; pass == 0 && t < n_qt; t += kThreads) {
-    const int q0 = t * kBQ, q1 = min(a.q_len, q0 + kBQ) - 1;
-    rs.qtab[0][t] = a.qpos[q0];
-    rs.qtab[1][t] = a.qpos[q1];
-    rs.qtab[2][t] = docmask ? a.qdoc[q0] : 0;
-    rs.qtab[3][t] = docmask ? a.qdoc[q1] : 0;
-  }
-  // the K/V loads go out after the range loads above: completions count in issue
-  // order, so the visible-range test below then waits for its own loads only
+  // the first query tiles' ranges go out before the K/V loads: completions count in
+  // issue order, so the visible-range test below then waits for its own loads only
+  QRange q_first = {0, -1, 0, 0};
+  if (tid < n_qt) q_first = qrange_global<DOC>(a, tid);
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 kf[D / 16], vf[D / 16];
   {
@@ -693,11 +696,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   QFillPlan<D> fp;
   fp.init(wave, lane);
   lds_barrier();
-  // range of query tiles the work-group's keys can see
+  // range of query tiles the work-group's keys can see (read from the query block:
+  // any number of local rows)
   {
     int lo = INT32_MAX, hi = -1;
     for (int t = tid; t < n_qt; t += kThreads) {
-      const QRange q = qrange(rs, t);
+      const QRange q = t == tid ? q_first : qrange_global<DOC>(a, t);
       if (classify(mask, q.pmin, q.pmax, q.dmin, q.dmax, kmin, kmax, kdmin, kdmax) != kTileEmpty) {
         lo = min(lo, t);
         hi = max(hi, t);
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       load_rows<DOC>(rs, b0, h, rv);
       RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
       TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
-      const QRange q = qrange(rs, cur.qt);
+      const QRange q = qrange_lds<DOC>(rs, b0, min(kBQ, a.q_len - cur.qt * kBQ));
       __builtin_amdgcn_sched_barrier(0);
       // fill of tile i+3 (its buffers held tile i-2, released at the last barrier)
       const bool issued = nf.hh >= 0;
@@ -884,7 +888,7 @@ void launch_dq(bool ranked, dim3 grid, dim3 block, hipStream_t stream, const Fwd
 }
 
 hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* delta, float scale, int d,
-                         hipStream_t stream) {
+                         bool accumulate, hipStream_t stream) {
   FwdArgs f = args;
   // work-groups as in the forward kernel (wave count chosen by the plan)
   const int nw = f.wg_waves == 8 ? 8 : 4;
@@ -897,7 +901,7 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   if (total == 0) return hipSuccess;
   f.total_wgs = total;
   f.padded_wgs = (total + 7) & ~7;
-  const DqExtra x{dout, delta, scale};
+  const DqExtra x{dout, delta, scale, accumulate ? 1 : 0};
   const dim3 grid(f.padded_wgs), block(nw * kWave);
   const bool ranked = kv::ranked_plan(f, qt_rows);
   if (d == 64) {
@@ -942,6 +946,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& args, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int bwd_max_rows() { return kMaxQTiles * kBQ; }
+
 
 }  // namespace cpattn

@@ -211,7 +211,8 @@ __device__ __forceinline__ int xcd_remap(int b, int padded_n) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel-argument tables (passed by value).
+// Kernel-argument tables (passed by value): at most kMaxSegs segments per launch; the
+// host runs longer segment lists as several launches.
 constexpr int kMaxSegs = 32;
 constexpr int kMaxJobs = 20;
 
@@ -313,9 +314,8 @@ hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* c
 hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t pairs, int d,
                             hipStream_t stream);
 hipError_t launch_bwd_dq(const FwdArgs& dq, const void* dout, const float* delta, float scale, int d,
-                         hipStream_t stream);
+                         bool accumulate, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t stream);
-int bwd_max_rows();  // local query rows the backward kernel supports
 // One launch merging the KV splits of every split job of a forward launch.
 hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream,
                                    bool sum = false);

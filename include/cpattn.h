@@ -187,7 +187,7 @@ int cpattn_partition_rope(int32_t mode, int64_t total, int32_t cp_size, int32_t 
  * the per-row log-sum-exp of the masked, scaled scores Q_i K_j^T and O_ij is the
  * output normalised inside segment j only.
  *
- *  n_edges          number of edges (0 is a no-op).
+ *  n_edges          number of edges (0 is a no-op); launched 20 edges at a time.
  *  q_blocks, segs   host arrays [n_edges]: the edge's queries and its KV segment.
  *  o_parts          host array [n_edges] of device fp32 [q.len, hq, d] outputs O_ij.
  *  lse_parts        host array [n_edges] of device fp32 [q.len, hq] outputs L_ij.
@@ -244,7 +244,11 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
  * (Q stays, KV blocks arrive one by one, the running max/sum/output are updated).
  *
  *  q                the local query block.
- *  n_segs, segs     host array of KV segments in arrival order (1..32).
+ *  n_segs, segs     host array of KV segments in arrival order (1..2048).  A launch
+ *                   streams up to 32 segments; a longer list runs as groups of 32, each
+ *                   streamed into an fp32 partial state in the workspace, merged by
+ *                   log-sum-exp at the end (needs cpattn_stream_fwd_workspace_bytes()
+ *                   bytes, else CPATTN_ERR_WORKSPACE; no KV split then).
  *  o_out            device [q.len, hq, d] in desc.dtype (final output O).
  *  lse_out          device fp32 [q.len, hq] (lambda, natural log).
  *  workspace        as for cpattn_tile_fwd (cpattn_stream_fwd_workspace_bytes()): when
@@ -258,7 +262,8 @@ int cpattn_stream_fwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
                       const cpattn_kv_seg* segs, void* o_out, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for the KV-split plan of cpattn_stream_fwd (0: no split planned). */
+/* Workspace bytes for the KV-split plan of cpattn_stream_fwd (0: no split planned), or
+ * for the per-group partial states of a list of more than 32 segments. */
 size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
                                          int32_t n_segs, const cpattn_kv_seg* segs);
 
@@ -271,8 +276,10 @@ size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpa
  * dK_j = sum_i dS_ij Q_i / sqrt(d), dV_j = sum_i P_ij G_i, and the K/V gradient
  * contributions of all local queries are summed per owner (per segment here).
  *
- *  q, segs          as for cpattn_stream_fwd (bf16 only in this version; at most
- *                   65536 local query rows, else CPATTN_ERR_UNSUPPORTED).
+ *  q, segs          as for cpattn_stream_fwd (bf16 only in this version; 1..2048
+ *                   segments; beyond 32 segments the dQ pass runs unsplit, one launch
+ *                   per group of 32 adding its part, and the dK/dV pass one launch per
+ *                   group).
  *  o                device [q.len, hq, d] forward output (desc.dtype).
  *  lse              device fp32 [q.len, hq] forward log-sum-exp.
  *  dout             device [q.len, hq, d] upstream gradient G (desc.dtype).
@@ -343,7 +350,7 @@ size_t cpattn_bwd_dq_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_
  * sum_i dS_is^T Q_i over all local query rows i (and all query heads of each kv
  * head's group): the contribution this rank returns to the owner of segment s.
  * One launch, key-major.
- *  q, n_segs, segs  as for cpattn_bwd (at most 65536 local rows).
+ *  q, n_segs, segs  as for cpattn_bwd.
  *  lse, delta, dout as for cpattn_bwd_dq.
  *  dk, dv           as for cpattn_bwd.
  * Errors: ARG, ALIGN, UNSUPPORTED, HIP. */

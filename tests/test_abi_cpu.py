@@ -97,7 +97,8 @@ def test_attention_validation():
     assert stream_call(desc(hkv=0)) == C.ERR_ARG
     assert stream_call(desc(scale=float("nan"))) == C.ERR_ARG
     assert stream_call(desc(), segs=[]) == C.ERR_ARG
-    assert stream_call(desc(), segs=[sg()] * 33) == C.ERR_ARG
+    assert stream_call(desc(), segs=[sg()] * 33) == C.ERR_WORKSPACE   # two groups of segments need a workspace
+    assert stream_call(desc(), segs=[sg()] * 2049) == C.ERR_ARG
     assert stream_call(desc(), q=qb(q=FAKE + 8)) == C.ERR_ALIGN
     assert stream_call(desc(), q=C.cpattn_q_block(FAKE, None, None, 64)) == C.ERR_ARG
     assert stream_call(desc(mask=C.MASK_CAUSAL_DOC)) == C.ERR_ARG     # doc ids required
@@ -161,8 +162,8 @@ def test_bwd_validation_and_workspace():
                             FAKE, 1 << 20, None) == C.ERR_UNSUPPORTED
     assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
                             FAKE, 100, None) == C.ERR_WORKSPACE
-    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(qb(65537)), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
-                            FAKE, 1 << 30, None) == C.ERR_UNSUPPORTED
+    assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(qb((1 << 30) + 1)), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
+                            FAKE, 1 << 30, None) == C.ERR_ARG
     assert C.lib.cpattn_bwd(ctypes.byref(d), ctypes.byref(q), 1, s, FAKE, FAKE, FAKE, FAKE, p, p,
                             None, 1 << 20, None) == C.ERR_WORKSPACE
     nul = (ctypes.c_void_p * 1)(None)
@@ -202,8 +203,8 @@ def test_bwd_pass_calls_validation():
     p = (ctypes.c_void_p * 4)(*[FAKE] * 4)
     nul = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
     odd = (ctypes.c_void_p * 4)(FAKE, FAKE + 4, FAKE, FAKE)
-    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(qb(65537)), 4, s4, FAKE, FAKE, FAKE, p, p,
-                               None) == C.ERR_UNSUPPORTED
+    assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(qb((1 << 30) + 1)), 4, s4, FAKE, FAKE, FAKE, p, p,
+                               None) == C.ERR_ARG
     assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, None, p,
                                None) == C.ERR_ARG
     assert lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, p, nul,
@@ -260,3 +261,25 @@ def test_striped_and_rope_partition_validation():
     rb = (ctypes.c_int64 * 1)(256)
     assert C.lib.cpattn_partition_rope(C.PART_ZIGZAG, 100, 4, 0, None, None, 0, FAKE, None, 1, ptrs, ptrs, rb,
                                        ctypes.byref(C.rope_desc(**ok)), None) == C.ERR_ALIGN
+
+
+def test_segment_and_row_limits():
+    # up to 2048 segments per call (groups of 32 per launch); more is refused
+    d = desc()
+    q = qb(1024)
+    segs = (C.cpattn_kv_seg * 2049)(*[sg(64)] * 2049)
+    p = (ctypes.c_void_p * 2049)(*[FAKE] * 2049)
+    assert C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), 2049, segs, FAKE, FAKE, None, 0,
+                                   None) == C.ERR_ARG
+    assert C.lib.cpattn_bwd_dkdv(ctypes.byref(d), ctypes.byref(q), 2049, segs, FAKE, FAKE, FAKE, p, p,
+                                 None) == C.ERR_ARG
+    # more than 32 segments: the streaming form needs one fp32 partial state per group of 32
+    want = 2 * (((1024 * 8 * 128 * 4 + 255) // 256) * 256 + ((1024 * 8 * 4 + 255) // 256) * 256)
+    assert C.lib.cpattn_stream_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 40, segs) == want
+    assert C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), 40, segs, FAKE, FAKE, None, 0,
+                                   None) == C.ERR_WORKSPACE
+    assert C.lib.cpattn_stream_fwd(ctypes.byref(d), ctypes.byref(q), 40, segs, FAKE, FAKE, FAKE, want - 256,
+                                   None) == C.ERR_WORKSPACE
+    # and the dQ pass of a grouped list runs unsplit: no split workspace is planned
+    assert C.lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 40, segs) == 0
+    assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 40, segs) == 1024 * 8 * 4
