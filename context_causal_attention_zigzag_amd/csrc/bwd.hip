@@ -165,18 +165,28 @@ template <int D, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(FwdArgs a, DqExtra x) {
   using namespace kv;
   __shared__ DqSmem<D> sm;
-  static_assert(sizeof(sm) >= (kMaxRankedTiles + 1) * sizeof(int), "ranking scratch");
+  static_assert(sizeof(sm) >= (kMaxRankedTiles + 8) * sizeof(int), "ranking scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
   TileTab tt{0, 0};
   WorkItem wi;
+  int ns_mine = 1;      // splits that exist for this work item's query tile (compact launches)
+  bool tt_all = false;  // the tile table covers every segment of the launch
   if constexpr (RANKED) {
     int s1 = 0;
     for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
     tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
     wi = ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
   } else {
-    wi = indexed_work_item(a, qt_rows);
+    if (a.compact) {
+      int s1 = 0;
+      for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
+      tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
+      tt_all = true;
+      wi = compact_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
+    } else {
+      wi = indexed_work_item(a, qt_rows);
+    }
     if (wi.job < 0) return;
   }
   const JobDesc& job = a.jobs[wi.job];
@@ -241,8 +251,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   // tiles of the walk, and per wave the skipped and the fully visible ones, from one
   // binary search per segment (kv_stream.h); the loop reads no segment table
   TileIter it;
-  if (!RANKED && a.mask != kMaskNone) tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
+  if (!RANKED && !tt_all && a.mask != kMaskNone)
+    tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
   iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax, sm, tt);
+  // compact launches run no work-group for the splits past a query tile's visible
+  // tiles: the first split marks their partials empty for the sum
+  if (nsplit > 1 && split == 0 && row_ok && (lane >> 5) == 0)
+    for (int s = ns_mine; s < nsplit; ++s) job.ws_lse[((int64_t)s * job.len + myrow) * a.hq + head] = neg_inf();
   if (nsplit == 1) {
     iter_walk_all(it, job);
   } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
@@ -904,6 +919,7 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   const DqExtra x{dout, delta, scale, accumulate ? 1 : 0};
   const dim3 grid(f.padded_wgs), block(nw * kWave);
   const bool ranked = kv::ranked_plan(f, qt_rows);
+  f.compact = !ranked && kv::compact_plan(f, qt_rows) ? 1 : 0;
   if (d == 64) {
     if (nw == 8)
       launch_dq<64, 8>(ranked, grid, block, stream, f, x);

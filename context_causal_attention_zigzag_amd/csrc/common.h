@@ -255,6 +255,7 @@ struct FwdArgs {
   int32_t total_wgs;     // logical work-groups
   int32_t padded_wgs;    // grid size (multiple of 8)
   int32_t wg_waves;      // waves per work-group of the launch (32 query rows each)
+  int32_t compact;       // KV splits numbered densely (no work-group for an empty split)
 };
 
 struct BwdArgs {

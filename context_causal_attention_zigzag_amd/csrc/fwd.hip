@@ -207,18 +207,28 @@ template <int D, bool PARTIAL_OUT, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(FwdArgs a) {
   using Sm = FwdSmem<D>;
   __shared__ Sm sm;
-  static_assert(sizeof(Sm) >= (kMaxRankedTiles + 1) * sizeof(int), "ranking scratch");
+  static_assert(sizeof(Sm) >= (kMaxRankedTiles + 8) * sizeof(int), "ranking scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
   TileTab tt{0, 0};
   WorkItem wi;
+  int ns_mine = 1;      // splits that exist for this work item's query tile (compact launches)
+  bool tt_all = false;  // the tile table covers every segment of the launch
   if constexpr (RANKED) {
     int s1 = 0;
     for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
     tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
     wi = ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
   } else {
-    wi = indexed_work_item(a, qt_rows);
+    if (a.compact) {
+      int s1 = 0;
+      for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
+      tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
+      tt_all = true;
+      wi = compact_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
+    } else {
+      wi = indexed_work_item(a, qt_rows);
+    }
     if (wi.job < 0) return;
   }
   const JobDesc& job = a.jobs[wi.job];
@@ -278,8 +288,13 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
   float* lse_dst = nsplit > 1 ? job.ws_lse + (int64_t)split * job.len * a.hq : job.lse;
 
   TileIter it;
-  if (!RANKED && a.mask != kMaskNone) tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
+  if (!RANKED && !tt_all && a.mask != kMaskNone)
+    tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
   iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax, sm, tt);
+  // compact launches run no work-group for the splits past a query tile's visible
+  // tiles: the first split marks their partial states empty for the merge
+  if (nsplit > 1 && split == 0 && row_ok && h == 0)
+    for (int s = ns_mine; s < nsplit; ++s) job.ws_lse[((int64_t)s * job.len + myrow) * a.hq + head] = neg_inf();
   if (nsplit == 1) {
     iter_walk_all(it, job);
   } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
@@ -465,6 +480,7 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
     if (total == 0) return hipSuccess;
     const dim3 grid(a.padded_wgs), block(nw * kWave);
     const bool ranked = ranked_plan(a, qt_rows);
+    a.compact = !ranked && compact_plan(a, qt_rows) ? 1 : 0;
     if (nw == 8) {
       if (partial_out)
         launch_fwd_bf16<D, true, 8>(ranked, grid, block, stream, a);

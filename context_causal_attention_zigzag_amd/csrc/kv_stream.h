@@ -534,5 +534,171 @@ __device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_ro
   return w;
 }
 
+// Visible KV tiles of query rows [.., qmax] (documents [qdmin, qdmax]) in one segment of
+// nt tiles, the count the tile iterators walk: from the first tile that reaches the
+// rows' first document (documents only) to the first tile past their last position or
+// document.
+template <class FP, class FD, class LD>
+__device__ __forceinline__ int visible_tiles(int nt, bool docm, int qmax, int qdmin, int qdmax, FP fp, FD fd, LD ld) {
+  if (docm) return walk_tiles(nt, qmax, qdmin, qdmax, fp, fd, ld);
+  int l0 = 0, h0 = nt;
+  while (l0 < h0) {
+    const int m0 = (l0 + h0) >> 1;
+    if (fp(m0) > qmax) h0 = m0; else l0 = m0 + 1;
+  }
+  return l0;
+}
+
+// Work items of a launch whose jobs are split over KV tiles, numbered densely over the
+// splits that exist.  A query tile that sees V of its job's KV tiles needs
+// ns = ceil(V / tiles_per_split) splits (at least one, which finds nothing when V = 0);
+// the grid holds the plan's upper bound n_split per query tile.  Numbering only the
+// splits that exist puts the surplus work-groups, which leave at once, after all the
+// real ones in dispatch order: interleaved among them, they made the dispatcher place
+// later real work-groups on compute units that were already full, while others held a
+// single work-group (measured: the last ones started up to 50 us late at 8K).
+// Order: as indexed_work_item (head-group blocks per XCD when the head groups divide
+// by 8, else contiguous ranges), query tiles latest first, splits inner.
+// Every thread calls this; scratch holds kMaxRankedTiles + 8 ints of LDS that nothing
+// uses yet; tt is the tile table of every segment of the launch.  job = -1: surplus.
+template <int NT, class Sm>
+__device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, int qt_rows, int* scratch, Sm& sm,
+                                                      TileTab tt, int& ns_out) {
+  const int tid = threadIdx.x;
+  const bool docm = a.mask == kMaskCausalDoc;
+  int n_all = 0, n_pairs = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    n_all += n_qt;
+    n_pairs += n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
+  }
+  for (int t = tid; t < n_all; t += NT) scratch[t] = 0;
+  __syncthreads();
+  // visible tiles of every (job, query tile): one (job, query tile, segment) search per thread
+  for (int k = tid; k < n_pairs; k += NT) {
+    int j = 0, kk = k, base = 0;
+    while (true) {
+      const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+      const int n = n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
+      if (kk < n) break;
+      kk -= n;
+      base += n_qt;
+      ++j;
+    }
+    const JobDesc& job = a.jobs[j];
+    const int n_seg = job.seg_end - job.seg_begin;
+    const int q = kk / n_seg, sidx = kk - q * n_seg;
+    const int r0 = q * qt_rows, r1 = min(job.len, r0 + qt_rows);
+    const SegDesc& sg = a.segs[job.seg_begin + sidx];
+    const int nt = (sg.len + kBK - 1) / kBK;
+    const int qmax = job.pos[r1 - 1];
+    const int qdmin = docm ? job.doc[r0] : 0, qdmax = docm ? job.doc[r1 - 1] : 0;
+    int c;
+    if (tt.stride > 0) {
+      using T = TabLds<Sm>;
+      const int b = (job.seg_begin + sidx - tt.s0) * tt.stride;
+      const int32_t* f = T::fpos(sm) + b;
+      const int32_t* fdc = T::fdoc(sm) + b;
+      const int32_t* ldc = T::ldoc(sm) + b;
+      c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return f[m]; }, [&](int m) { return fdc[m]; },
+                        [&](int m) { return ldc[m]; });
+    } else {
+      c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return sg.pos[m * kBK]; },
+                        [&](int m) { return sg.doc[m * kBK]; },
+                        [&](int m) { return sg.doc[min(sg.len, m * kBK + kBK) - 1]; });
+    }
+    if (c) atomicAdd(&scratch[base + q], c);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // splits per (job, query tile), then the item of this work-group
+    int t0 = 0;
+    int total = 0;  // splits over every job, per head group
+    for (int j = 0; j < a.n_jobs; ++j) {
+      const JobDesc& job = a.jobs[j];
+      const int n_qt = (job.len + qt_rows - 1) / qt_rows;
+      for (int q = 0; q < n_qt; ++q) {
+        const int v = scratch[t0 + q];
+        scratch[t0 + q] = job.n_split > 1 ? max(1, (v + job.tiles_per_split - 1) / job.tiles_per_split) : 1;
+        total += scratch[t0 + q];
+      }
+      t0 += n_qt;
+    }
+    const int n_hg = a.hq / a.heads_per_wg;
+    const int b = blockIdx.x;
+    int rj = -1, rq = 0, rs = 0, rhg = 0, rns = 1;
+    int j = 0, i = 0, hg_base = 0, hg_span = 1;
+    bool live = false;
+    if ((n_hg & 7) == 0) {
+      // XCD b % 8 takes head groups [x * hpx, (x + 1) * hpx) of every job
+      const int hpx = n_hg >> 3;
+      i = b >> 3;
+      hg_base = (b & 7) * hpx;
+      hg_span = hpx;
+      live = true;
+    } else {
+      const int T = total * n_hg;
+      const int per = (T + 7) >> 3;
+      i = (b & 7) * per + (b >> 3);
+      live = (b >> 3) < per && i < T;
+      hg_span = n_hg;
+    }
+    if (live) {
+      t0 = 0;
+      for (j = 0; j < a.n_jobs; ++j) {
+        const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+        int m = 0;
+        for (int q = 0; q < n_qt; ++q) m += scratch[t0 + q];
+        if (i < m * hg_span) {
+          const int hl = i / m;
+          int k = i - hl * m;
+          for (int q = n_qt - 1; q >= 0; --q) {  // latest query tile first
+            const int ns = scratch[t0 + q];
+            if (k < ns) {
+              rj = j;
+              rq = q;
+              rs = k;
+              rns = ns;
+              rhg = hg_base + hl;
+              break;
+            }
+            k -= ns;
+          }
+          break;
+        }
+        i -= m * hg_span;
+        t0 += n_qt;
+      }
+    }
+    scratch[n_all] = rj;
+    scratch[n_all + 1] = rq;
+    scratch[n_all + 2] = rs;
+    scratch[n_all + 3] = rhg;
+    scratch[n_all + 4] = rns;
+  }
+  __syncthreads();
+  WorkItem w;
+  w.job = scratch[n_all];
+  w.qt = scratch[n_all + 1];
+  w.split = scratch[n_all + 2];
+  w.hg = scratch[n_all + 3];
+  ns_out = scratch[n_all + 4];
+  __syncthreads();  // scratch free again
+  return w;
+}
+
+// A compact launch (no empty split) needs a document or causal mask, KV splits, and at
+// most kMaxRankedTiles query tiles over all jobs.
+inline bool compact_plan(const FwdArgs& a, int qt_rows) {
+  if (a.mask == kMaskNone) return false;
+  bool split = false;
+  int n_all = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    split |= a.jobs[j].n_split > 1;
+    n_all += (a.jobs[j].len + qt_rows - 1) / qt_rows;
+  }
+  return split && n_all <= kMaxRankedTiles;
+}
+
 }  // namespace kv
 }  // namespace cpattn
