@@ -62,8 +62,10 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restr
 // ---------------------------------------------------------------------------
 // dQ pass
 template <int D>
-// K is read both as rows and transposed (row stride D + 24: conflict-free for both on
-// gfx950), V only as rows (D + 8).
+// K is read both as rows and transposed, at row stride D + 24: its 16-byte row reads are
+// conflict-free there, its transposing reads are not (44% of their LDS cycles in
+// conflicts in a microbenchmark; only D + 32 serves them without conflicts, at 3.7x the
+// cost of the row reads); V only as rows (D + 8).
 using DqSmem = kv::KvSmem<D, D + 24, D + 8>;
 
 struct DqExtra {
@@ -329,9 +331,11 @@ constexpr int kQBufs = 5;
 
 template <int D>
 struct DkdvSmem {
-  // Row stride (elements) measured on gfx950 to serve both access patterns of these
-  // tiles without bank conflicts: 16-byte row reads and transposing reads (D + 24:
-  // 304 bytes for D = 128; D + 32 conflicts on row reads, D + 8 on transposing reads).
+  // Row stride (elements) of these tiles, read both as 16-byte rows and transposed:
+  // D + 24 (304 bytes at D = 128) keeps the row reads conflict-free and leaves the
+  // transposing reads with 44% of their LDS cycles in conflicts (microbenchmark with the
+  // kernel's lane addressing); D + 32 would serve the transposing reads but make the row
+  // reads 3.7x slower, so the cheaper side keeps the conflicts.
   static constexpr int kRS = D + 24;
   static constexpr int kSlots = kRS / 8;                                // 16-byte slots per row
   static constexpr int kTileInst = (kBQ * kSlots + kWave - 1) / kWave;  // fill instructions per tile

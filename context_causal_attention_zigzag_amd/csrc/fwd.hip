@@ -44,9 +44,10 @@ namespace {
 
 using namespace kv;
 
-// K rows at stride D + 8 (row reads), V rows at D + 24 (transposing reads; also
-// conflict-free for row reads): 73 KiB with both double-buffered, two work-groups
-// per CU.
+// K rows at stride D + 8 (row reads, conflict-free), V rows at D + 24 (transposing
+// reads, 44% of their LDS cycles in conflicts; D + 32 would remove them but measured
+// no faster and needs one more fill instruction per tile): 73 KiB with both
+// double-buffered, two work-groups per CU.
 template <int D>
 using FwdSmem = KvSmem<D, D + 8, D + 24>;
 

@@ -20,9 +20,10 @@ struct TileRef {
   int tile;
 };
 
-// Double-buffered LDS image of one KV tile (kBK keys).  Row strides measured
-// conflict-free on gfx950's 64-bank LDS: 16-byte row reads need a stride of 4
-// (mod 16) dwords (D + 8 elements), transposing reads 16 (mod 64) dwords (D + 32).
+// Double-buffered LDS image of one KV tile (kBK keys).  Bank conflicts measured on
+// gfx950's 64-bank LDS: 16-byte row reads are conflict-free at a stride of 4 (mod 16)
+// dwords (D + 8 or D + 24 elements), transposing reads only at 16 (mod 64) dwords
+// (D + 32); the kernels choose the stride per image (see their Smem types).
 template <int D, int KS, int VS>
 struct KvSmem {
   static constexpr int kKS = KS;
