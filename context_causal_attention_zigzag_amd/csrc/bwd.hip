@@ -170,22 +170,17 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   static_assert(sizeof(sm) >= (kMaxRankedTiles + 8) * sizeof(int), "ranking scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
+  const LaneDescs ld = load_lane_descs(a);
   TileTab tt{0, 0};
   WorkItem wi;
   int ns_mine = 1;      // splits that exist for this work item's query tile (compact launches)
   bool tt_all = false;  // the tile table covers every segment of the launch
   if constexpr (RANKED) {
-    int s1 = 0;
-    for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
-    tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
-    wi = ranked_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
+    wi = ranked_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
   } else {
     if (a.compact) {
-      int s1 = 0;
-      for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
-      tt = load_tile_table<NW * kWave>(sm, a, 0, s1);
+      wi = compact_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
       tt_all = true;
-      wi = compact_work_item<NW * kWave>(a, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
     } else {
       wi = indexed_work_item(a, qt_rows);
     }
@@ -254,8 +249,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   // binary search per segment (kv_stream.h); the loop reads no segment table
   TileIter it;
   if (!RANKED && !tt_all && a.mask != kMaskNone)
-    tt = load_tile_table<NW * kWave>(sm, a, job.seg_begin, job.seg_end);
-  iter_init_lanes(it, a, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax, sm, tt);
+    tt = load_tile_table<NW * kWave>(sm, a, ld, job.seg_begin, job.seg_end);
+  iter_init_lanes(it, a, ld, job, lane, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax, sm, tt);
   // compact launches run no work-group for the splits past a query tile's visible
   // tiles: the first split marks their partials empty for the sum
   if (nsplit > 1 && split == 0 && row_ok && (lane >> 5) == 0)

@@ -92,24 +92,105 @@ struct TabLds {
   __device__ static int32_t* ldoc(Sm& sm) { return reinterpret_cast<int32_t*>(sm.v[1]) + kCap; }
 };
 
-// Every thread of the work-group calls this with the same arguments.
+// The launch's segment and job descriptors, one per lane: lane l of every wave holds
+// segment l's and job l's fields, fetched by one round of independent loads at kernel
+// start.  A thread that needs another entry's field reads it across lanes (ds_bpermute,
+// no memory access).  Indexing the argument block with a per-thread index instead
+// makes every field a dependent vector load: the prologue's searches and scans then
+// waited on chains of three to five memory round trips.
+struct LaneDescs {
+  uint32_t sk_lo, sk_hi, sv_lo, sv_hi, sp_lo, sp_hi, sd_lo, sd_hi;  // segment: K, V, positions, documents
+  int slen;
+  uint32_t jp_lo, jp_hi, jd_lo, jd_hi;  // job: positions, documents
+  int jlen, jsb, jns, jtps;             // job: rows, first segment, n_split, tiles_per_split
+};
+
+__device__ __forceinline__ LaneDescs load_lane_descs(const FwdArgs& a) {
+  static_assert(kMaxSegs <= kWave && kMaxJobs <= kWave, "one descriptor per lane");
+  const int l = threadIdx.x & (kWave - 1);
+  LaneDescs d{};
+  if (l < kMaxSegs) {  // entries past the launch's segments are zero
+    const SegDesc& sg = a.segs[l];
+    const uint64_t k = reinterpret_cast<uint64_t>(sg.k), v = reinterpret_cast<uint64_t>(sg.v);
+    const uint64_t p = reinterpret_cast<uint64_t>(sg.pos), dc = reinterpret_cast<uint64_t>(sg.doc);
+    d.sk_lo = (uint32_t)k;
+    d.sk_hi = (uint32_t)(k >> 32);
+    d.sv_lo = (uint32_t)v;
+    d.sv_hi = (uint32_t)(v >> 32);
+    d.sp_lo = (uint32_t)p;
+    d.sp_hi = (uint32_t)(p >> 32);
+    d.sd_lo = (uint32_t)dc;
+    d.sd_hi = (uint32_t)(dc >> 32);
+    d.slen = sg.len;
+  }
+  if (l < kMaxJobs) {
+    const JobDesc& jb = a.jobs[l];
+    const uint64_t p = reinterpret_cast<uint64_t>(jb.pos), dc = reinterpret_cast<uint64_t>(jb.doc);
+    d.jp_lo = (uint32_t)p;
+    d.jp_hi = (uint32_t)(p >> 32);
+    d.jd_lo = (uint32_t)dc;
+    d.jd_hi = (uint32_t)(dc >> 32);
+    d.jlen = jb.len;
+    d.jsb = jb.seg_begin;
+    d.jns = jb.n_split;
+    d.jtps = jb.tiles_per_split;
+  }
+  return d;
+}
+
+// Lane src's value.  Every lane of the wave must execute it, outside any condition:
+// a read from a lane that is not active does not return that lane's value.
+__device__ __forceinline__ int lane_val(int v, int src) { return __shfl(v, src); }
+
+__device__ __forceinline__ const int32_t* lane_ptr(uint32_t lo, uint32_t hi, int src) {
+  return reinterpret_cast<const int32_t*>((uint64_t)(uint32_t)__shfl((int)hi, src) << 32 |
+                                          (uint32_t)__shfl((int)lo, src));
+}
+
+// Every thread of the work-group calls this with the same arguments.  All table entries
+// of a thread are loaded before any is stored, so the table costs one round of loads.
 template <int NT, class Sm>
-__device__ __forceinline__ TileTab load_tile_table(Sm& sm, const FwdArgs& a, int s0, int s1) {
+__device__ __forceinline__ TileTab load_tile_table(Sm& sm, const FwdArgs& a, const LaneDescs& ld, int s0, int s1) {
   using T = TabLds<Sm>;
   int stride = 0;
   for (int s = s0; s < s1; ++s) stride = max(stride, (a.segs[s].len + kBK - 1) / kBK);
   if (stride == 0 || (s1 - s0) * stride > T::kCap) return {s0, 0};
   const bool docm = a.mask == kMaskCausalDoc;
-  for (int i = threadIdx.x; i < (s1 - s0) * stride; i += NT) {
-    const int sl = i / stride, m = i - sl * stride;
-    const SegDesc& sg = a.segs[s0 + sl];
-    if (m * kBK < sg.len) {
-      const int f = m * kBK, l = min(sg.len, f + kBK) - 1;
-      T::fpos(sm)[i] = sg.pos[f];
-      T::lpos(sm)[i] = sg.pos[l];
-      if (docm) {
-        T::fdoc(sm)[i] = sg.doc[f];
-        T::ldoc(sm)[i] = sg.doc[l];
+  const int n = (s1 - s0) * stride;
+  constexpr int kIt = (T::kCap + NT - 1) / NT;
+  int fpv[kIt], lpv[kIt], fdv[kIt], ldv[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (it * NT < n) {  // uniform: every lane takes part in the cross-lane reads
+      const int i = threadIdx.x + it * NT;
+      const int sl = min(i / stride, s1 - s0 - 1), m = i - sl * stride;
+      const int len = lane_val(ld.slen, s0 + sl);
+      const int32_t* pos = lane_ptr(ld.sp_lo, ld.sp_hi, s0 + sl);
+      const int32_t* dc = lane_ptr(ld.sd_lo, ld.sd_hi, s0 + sl);
+      if (i < n && m * kBK < len) {
+        const int f = m * kBK, l = min(len, f + kBK) - 1;
+        fpv[it] = pos[f];
+        lpv[it] = pos[l];
+        if (docm) {
+          fdv[it] = dc[f];
+          ldv[it] = dc[l];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (it * NT < n) {
+      const int i = threadIdx.x + it * NT;
+      const int sl = min(i / stride, s1 - s0 - 1), m = i - sl * stride;
+      const int len = lane_val(ld.slen, s0 + sl);
+      if (i < n && m * kBK < len) {
+        T::fpos(sm)[i] = fpv[it];
+        T::lpos(sm)[i] = lpv[it];
+        if (docm) {
+          T::fdoc(sm)[i] = fdv[it];
+          T::ldoc(sm)[i] = ldv[it];
+        }
       }
     }
   }
@@ -150,19 +231,22 @@ __device__ __forceinline__ VisRanges vis_search(int nt, int nf, bool docm, int q
 }
 
 template <class Sm>
-__device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, const JobDesc& job, int lane,
-                                                int qmax, int qdmin, int qdmax, bool wave_rows, int wqmin,
-                                                int wqmax, int wqdmin, int wqdmax, Sm& sm, TileTab tt) {
-  int len = 0;
-  uint64_t kp = 0, vp = 0, pp = 0, dp = 0;
+__device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, const LaneDescs& ld,
+                                                const JobDesc& job, int lane, int qmax, int qdmin, int qdmax,
+                                                bool wave_rows, int wqmin, int wqmax, int wqdmin, int wqdmax, Sm& sm,
+                                                TileTab tt) {
+  // lane s takes segment seg_begin + s of the job from the lane that holds it (every
+  // lane reads: a cross-lane read does not see the value of a lane that is not active)
+  const int src = min(job.seg_begin + lane, kMaxSegs - 1);
+  const bool mine = lane < job.seg_end - job.seg_begin;
+  const int slen = lane_val(ld.slen, src);
+  const int len = mine ? slen : 0;
+  const uint64_t kp = reinterpret_cast<uint64_t>(lane_ptr(ld.sk_lo, ld.sk_hi, src));
+  const uint64_t vp = reinterpret_cast<uint64_t>(lane_ptr(ld.sv_lo, ld.sv_hi, src));
+  const uint64_t pp = reinterpret_cast<uint64_t>(lane_ptr(ld.sp_lo, ld.sp_hi, src));
+  const uint64_t dp = reinterpret_cast<uint64_t>(lane_ptr(ld.sd_lo, ld.sd_hi, src));
   VisRanges r = {0, 0, 0, 0, 0, 0};
-  if (lane < job.seg_end - job.seg_begin) {
-    const SegDesc& sg = a.segs[job.seg_begin + lane];
-    len = sg.len;
-    kp = reinterpret_cast<uint64_t>(sg.k);
-    vp = reinterpret_cast<uint64_t>(sg.v);
-    pp = reinterpret_cast<uint64_t>(sg.pos);
-    dp = reinterpret_cast<uint64_t>(sg.doc);
+  if (mine) {
     const int nt = (len + kBK - 1) / kBK, nf = len / kBK;
     const bool docm = a.mask == kMaskCausalDoc;
     const int wnt = wave_rows ? nt : 0;
@@ -180,8 +264,8 @@ __device__ __forceinline__ void iter_init_lanes(TileIter& it, const FwdArgs& a, 
                        [&](int m) { return f[m]; }, [&](int m) { return l[m]; },
                        [&](int m) { return fdc[m]; }, [&](int m) { return ldc[m]; });
       } else {
-        const int32_t* pos = sg.pos;
-        const int32_t* dc = sg.doc;
+        const int32_t* pos = reinterpret_cast<const int32_t*>(pp);
+        const int32_t* dc = reinterpret_cast<const int32_t*>(dp);
         r = vis_search(nt, nf, docm, qmax, qdmin, qdmax, wave_rows, wqmin, wqmax, wqdmin, wqdmax,
                        [&](int m) { return pos[m * kBK]; }, [&](int m) { return pos[min(len, m * kBK + kBK) - 1]; },
                        [&](int m) { return dc[m * kBK]; }, [&](int m) { return dc[min(len, m * kBK + kBK) - 1]; });
@@ -451,90 +535,6 @@ __device__ __forceinline__ int walk_tiles(int nt, int qmax, int qdmin, int qdmax
   return max(0, l0 - l1);
 }
 
-// Work-group b runs on XCD b % 8, which takes head groups [x*hpx, (x+1)*hpx) of every
-// job, hpx = head groups / 8.  Every work-group counts, for every query tile of every
-// job, the KV tiles that tile's work-group walks, ranks the (job, tile) pairs by that
-// count (most first; ties: the later pair first) and takes the pair of rank (b / 8) /
-// hpx, head group (b / 8) % hpx of its XCD's block: each XCD's list is then the
-// longest-processing-time-first schedule of its share, its head groups inner.  Every
-// thread of the work-group calls this; scratch holds kMaxRankedTiles + 1 ints of LDS
-// that nothing else uses yet.
-template <int NT, class Sm>
-__device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, int qt_rows, int* scratch, Sm& sm,
-                                                     TileTab tt) {
-  const int b = blockIdx.x;
-  const int hpx = (a.hq / a.heads_per_wg) >> 3;
-  const int i = b >> 3;
-  const int rank = i / hpx;
-  WorkItem w;
-  w.split = 0;
-  w.hg = (b & 7) * hpx + (i - rank * hpx);
-  const int tid = threadIdx.x;
-  int n_all = 0, n_pairs = 0;
-  for (int j = 0; j < a.n_jobs; ++j) {
-    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-    n_all += n_qt;
-    n_pairs += n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
-  }
-  for (int t = tid; t < n_all; t += NT) scratch[t] = 0;
-  __syncthreads();
-  // one (job, query tile, segment) search per thread, all jobs at once
-  for (int k = tid; k < n_pairs; k += NT) {
-    int j = 0, kk = k, base = 0;
-    while (true) {
-      const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-      const int n = n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
-      if (kk < n) break;
-      kk -= n;
-      base += n_qt;
-      ++j;
-    }
-    const JobDesc& job = a.jobs[j];
-    const int n_seg = job.seg_end - job.seg_begin;
-    const int q = kk / n_seg, s = kk - q * n_seg;
-    const int r0 = q * qt_rows, r1 = min(job.len, r0 + qt_rows);
-    const SegDesc& sg = a.segs[job.seg_begin + s];
-    const int nt = (sg.len + kBK - 1) / kBK;
-    const int qmax = job.pos[r1 - 1], qdmin = job.doc[r0], qdmax = job.doc[r1 - 1];
-    int c;
-    if (tt.stride > 0) {
-      using T = TabLds<Sm>;
-      const int b = (job.seg_begin + s - tt.s0) * tt.stride;
-      const int32_t* f = T::fpos(sm) + b;
-      const int32_t* fdc = T::fdoc(sm) + b;
-      const int32_t* ldc = T::ldoc(sm) + b;
-      c = walk_tiles(nt, qmax, qdmin, qdmax, [&](int m) { return f[m]; }, [&](int m) { return fdc[m]; },
-                     [&](int m) { return ldc[m]; });
-    } else {
-      c = walk_tiles(nt, qmax, qdmin, qdmax, [&](int m) { return sg.pos[m * kBK]; },
-                     [&](int m) { return sg.doc[m * kBK]; },
-                     [&](int m) { return sg.doc[min(sg.len, m * kBK + kBK) - 1]; });
-    }
-    if (c) atomicAdd(&scratch[base + q], c);
-  }
-  __syncthreads();
-  for (int t = tid; t < n_all; t += NT) {
-    const int c = scratch[t];
-    int r = 0;
-    for (int p = 0; p < n_all; ++p) {
-      const int cp = scratch[p];
-      r += (cp > c) | ((cp == c) & (p > t));
-    }
-    if (r == rank) scratch[n_all] = t;
-  }
-  __syncthreads();
-  int t = scratch[n_all];
-  __syncthreads();  // scratch free again
-  int j = 0;
-  while (t >= (a.jobs[j].len + qt_rows - 1) / qt_rows) {
-    t -= (a.jobs[j].len + qt_rows - 1) / qt_rows;
-    ++j;
-  }
-  w.job = j;
-  w.qt = t;
-  return w;
-}
-
 // Visible KV tiles of query rows [.., qmax] (documents [qdmin, qdmax]) in one segment of
 // nt tiles, the count the tile iterators walk: from the first tile that reaches the
 // rows' first document (documents only) to the first tile past their last position or
@@ -550,6 +550,146 @@ __device__ __forceinline__ int visible_tiles(int nt, bool docm, int qmax, int qd
   return l0;
 }
 
+// (job, query tile, segment) triple k of the launch, jobs in order, segments inner
+// (job -1: k is past the last triple).  A uniform loop over the jobs, so their
+// descriptors come from scalar loads.
+struct PairRef {
+  int job, base, q, sidx;  // base: index of the job's first query tile over all jobs
+};
+
+__device__ __forceinline__ PairRef pair_at(const FwdArgs& a, int qt_rows, int k) {
+  PairRef p{-1, 0, 0, 0};
+  int acc = 0, base = 0, nseg = 1, kk = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    const int ns = a.jobs[j].seg_end - a.jobs[j].seg_begin;
+    const int n = n_qt * ns;
+    if (p.job < 0 && k >= acc && k < acc + n) {
+      p.job = j;
+      p.base = base;
+      kk = k - acc;
+      nseg = ns;
+    }
+    acc += n;
+    base += n_qt;
+  }
+  p.q = kk / nseg;
+  p.sidx = kk - p.q * nseg;
+  return p;
+}
+
+// For every query tile t (over all jobs) the number of KV tiles its work-group walks,
+// summed over the job's segments, in scratch[t]; returns the number of query tiles.
+// Loads the tile table of every segment of the launch into tt.  Every thread calls
+// this; scratch holds kMaxRankedTiles + 8 ints of LDS outside the table.  The first
+// triple of each thread and its query tile's ends are loaded before the table, so the
+// two rounds of loads overlap.
+template <int NT, class Sm>
+__device__ __forceinline__ int count_visible(const FwdArgs& a, const LaneDescs& ld, int qt_rows, int* scratch,
+                                             Sm& sm, TileTab& tt) {
+  const int tid = threadIdx.x;
+  const bool docm = a.mask == kMaskCausalDoc;
+  int n_all = 0, n_pairs = 0, s1 = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    n_all += n_qt;
+    n_pairs += n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
+    s1 = max(s1, a.jobs[j].seg_end);
+  }
+  const int iters = (n_pairs + NT - 1) / NT;
+  // values of this thread's triple k = tid + it * NT: query tile ends, segment
+  int qmax = 0, qdmin = 0, qdmax = 0, seg = 0, slot = 0;
+  auto prepare = [&](int it) {  // every lane calls this (cross-lane reads)
+    const int k = tid + it * NT;
+    const PairRef p = pair_at(a, qt_rows, k);
+    const int jj = max(p.job, 0);
+    const int len = lane_val(ld.jlen, jj);
+    const int32_t* pos = lane_ptr(ld.jp_lo, ld.jp_hi, jj);
+    const int32_t* dc = lane_ptr(ld.jd_lo, ld.jd_hi, jj);
+    seg = min(lane_val(ld.jsb, jj) + p.sidx, kMaxSegs - 1);
+    slot = p.base + p.q;
+    if (p.job >= 0) {
+      const int r0 = p.q * qt_rows, r1 = min(len, r0 + qt_rows);
+      qmax = pos[r1 - 1];
+      if (docm) {
+        qdmin = dc[r0];
+        qdmax = dc[r1 - 1];
+      }
+    }
+  };
+  if (iters > 0) prepare(0);
+  for (int t = tid; t < n_all; t += NT) scratch[t] = 0;
+  tt = load_tile_table<NT>(sm, a, ld, 0, s1);  // ends with a barrier
+  for (int it = 0; it < iters; ++it) {
+    if (it > 0) prepare(it);
+    const int nt = (lane_val(ld.slen, seg) + kBK - 1) / kBK;
+    const int32_t* spos = lane_ptr(ld.sp_lo, ld.sp_hi, seg);
+    const int32_t* sdoc = lane_ptr(ld.sd_lo, ld.sd_hi, seg);
+    const int slen = lane_val(ld.slen, seg);
+    if (tid + it * NT < n_pairs) {
+      int c;
+      if (tt.stride > 0) {
+        using T = TabLds<Sm>;
+        const int b = (seg - tt.s0) * tt.stride;
+        const int32_t* f = T::fpos(sm) + b;
+        const int32_t* fdc = T::fdoc(sm) + b;
+        const int32_t* ldc = T::ldoc(sm) + b;
+        c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return f[m]; },
+                          [&](int m) { return fdc[m]; }, [&](int m) { return ldc[m]; });
+      } else {
+        c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return spos[m * kBK]; },
+                          [&](int m) { return sdoc[m * kBK]; },
+                          [&](int m) { return sdoc[min(slen, m * kBK + kBK) - 1]; });
+      }
+      if (c) atomicAdd(&scratch[slot], c);
+    }
+  }
+  __syncthreads();
+  return n_all;
+}
+
+// Work-group b runs on XCD b % 8, which takes head groups [x*hpx, (x+1)*hpx) of every
+// job, hpx = head groups / 8.  Every work-group counts, for every query tile of every
+// job, the KV tiles that tile's work-group walks, ranks the (job, tile) pairs by that
+// count (most first; ties: the later pair first) and takes the pair of rank (b / 8) /
+// hpx, head group (b / 8) % hpx of its XCD's block: each XCD's list is then the
+// longest-processing-time-first schedule of its share, its head groups inner.  Every
+// thread of the work-group calls this; scratch holds kMaxRankedTiles + 1 ints of LDS
+// that nothing else uses yet.
+template <int NT, class Sm>
+__device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, const LaneDescs& ld, int qt_rows,
+                                                     int* scratch, Sm& sm, TileTab& tt) {
+  const int b = blockIdx.x;
+  const int hpx = (a.hq / a.heads_per_wg) >> 3;
+  const int i = b >> 3;
+  const int rank = i / hpx;
+  WorkItem w;
+  w.split = 0;
+  w.hg = (b & 7) * hpx + (i - rank * hpx);
+  const int tid = threadIdx.x;
+  const int n_all = count_visible<NT, Sm>(a, ld, qt_rows, scratch, sm, tt);
+  for (int t = tid; t < n_all; t += NT) {
+    const int c = scratch[t];
+    int r = 0;
+    for (int p = 0; p < n_all; ++p) {
+      const int cp = scratch[p];
+      r += (cp > c) | ((cp == c) & (p > t));
+    }
+    if (r == rank) scratch[n_all] = t;
+  }
+  __syncthreads();
+  int t = __builtin_amdgcn_readfirstlane(scratch[n_all]);
+  __syncthreads();  // scratch free again
+  int j = 0;
+  while (t >= (a.jobs[j].len + qt_rows - 1) / qt_rows) {
+    t -= (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    ++j;
+  }
+  w.job = j;
+  w.qt = t;
+  return w;
+}
+
 // Work items of a launch whose jobs are split over KV tiles, numbered densely over the
 // splits that exist.  A query tile that sees V of its job's KV tiles needs
 // ns = ceil(V / tiles_per_split) splits (at least one, which finds nothing when V = 0);
@@ -560,58 +700,103 @@ __device__ __forceinline__ int visible_tiles(int nt, bool docm, int qmax, int qd
 // single work-group (measured: the last ones started up to 50 us late at 8K).
 // Order: as indexed_work_item (head-group blocks per XCD when the head groups divide
 // by 8, else contiguous ranges), query tiles latest first, splits inner.
-// Every thread calls this; scratch holds kMaxRankedTiles + 8 ints of LDS that nothing
-// uses yet; tt is the tile table of every segment of the launch.  job = -1: surplus.
+// Every thread calls this; it loads the tile table of every segment of the launch
+// (returned in tt) and uses scratch, kMaxRankedTiles + 8 ints of LDS outside the
+// table that nothing uses yet.  job = -1: surplus.
+
 template <int NT, class Sm>
-__device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, int qt_rows, int* scratch, Sm& sm,
-                                                      TileTab tt, int& ns_out) {
+__device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, const LaneDescs& ld, int qt_rows,
+                                                      int* scratch, Sm& sm, TileTab& tt, int& ns_out) {
   const int tid = threadIdx.x;
-  const bool docm = a.mask == kMaskCausalDoc;
-  int n_all = 0, n_pairs = 0;
-  for (int j = 0; j < a.n_jobs; ++j) {
-    const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-    n_all += n_qt;
-    n_pairs += n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
-  }
-  for (int t = tid; t < n_all; t += NT) scratch[t] = 0;
-  __syncthreads();
-  // visible tiles of every (job, query tile): one (job, query tile, segment) search per thread
-  for (int k = tid; k < n_pairs; k += NT) {
-    int j = 0, kk = k, base = 0;
-    while (true) {
-      const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-      const int n = n_qt * (a.jobs[j].seg_end - a.jobs[j].seg_begin);
-      if (kk < n) break;
-      kk -= n;
-      base += n_qt;
-      ++j;
+  const int n_all = count_visible<NT, Sm>(a, ld, qt_rows, scratch, sm, tt);
+  const int n_hg = a.hq / a.heads_per_wg;
+  const int b = blockIdx.x;
+  if (n_all <= kWave) {
+    // one wave: lane t holds query tile t (over all jobs); the splits of its job's later
+    // query tiles come from a segmented suffix scan across the lanes
+    if (tid < kWave) {
+      const int t = tid;
+      const bool have = t < n_all;
+      int jt = 0, tb = 0, acc = 0;
+      for (int j = 0; j < a.n_jobs; ++j) {
+        if (t >= acc) {
+          jt = j;
+          tb = acc;
+        }
+        acc += (a.jobs[j].len + qt_rows - 1) / qt_rows;
+      }
+      const int jlen = lane_val(ld.jlen, jt), jns = lane_val(ld.jns, jt), jtps = lane_val(ld.jtps, jt);
+      const int te = have ? tb + (jlen + qt_rows - 1) / qt_rows - 1 : t;  // the job's last query tile
+      int ns = 0;
+      if (have) {
+        const int v = scratch[t];
+        ns = jns > 1 ? max(1, (v + jtps - 1) / jtps) : 1;
+      }
+      int suf = ns;  // splits of query tiles t .. te
+#pragma unroll
+      for (int dl = 1; dl < kWave; dl <<= 1) {
+        const int o = __shfl_down(suf, dl);
+        if (t + dl <= te) suf += o;
+      }
+      const int before = suf - ns;  // splits of the job's query tiles after t (numbered first)
+      // the work-group's item: job totals from the lanes of the jobs' first query tiles
+      int total = 0;
+      {
+        int tb_j = 0;
+        for (int j = 0; j < a.n_jobs; ++j) {
+          const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+          if (n_qt > 0) total += __builtin_amdgcn_readlane(suf, tb_j);
+          tb_j += n_qt;
+        }
+      }
+      int i = 0, hg_base = 0, hg_span = 1;
+      bool live;
+      if ((n_hg & 7) == 0) {
+        const int hpx = n_hg >> 3;
+        i = b >> 3;
+        hg_base = (b & 7) * hpx;
+        hg_span = hpx;
+        live = true;
+      } else {
+        const int T = total * n_hg;
+        const int per = (T + 7) >> 3;
+        i = (b & 7) * per + (b >> 3);
+        live = (b >> 3) < per && i < T;
+        hg_span = n_hg;
+      }
+      int rj = -1, rq = 0, rs = 0, rhg = 0, rns = 1;
+      if (live) {
+        int tb_j = 0;
+        for (int j = 0; j < a.n_jobs; ++j) {
+          const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+          const int m = n_qt > 0 ? __builtin_amdgcn_readlane(suf, tb_j) : 0;
+          if (i < m * hg_span) {
+            const int hl = i / m;
+            const int k = i - hl * m;
+            const uint64_t hit = __ballot(have && jt == j && before <= k && k < before + ns);
+            if (hit) {
+              const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+              rj = j;
+              rq = L - tb_j;
+              rs = k - __builtin_amdgcn_readlane(before, L);
+              rns = __builtin_amdgcn_readlane(ns, L);
+              rhg = hg_base + hl;
+            }
+            break;
+          }
+          i -= m * hg_span;
+          tb_j += n_qt;
+        }
+      }
+      if (t == 0) {
+        scratch[n_all] = rj;
+        scratch[n_all + 1] = rq;
+        scratch[n_all + 2] = rs;
+        scratch[n_all + 3] = rhg;
+        scratch[n_all + 4] = rns;
+      }
     }
-    const JobDesc& job = a.jobs[j];
-    const int n_seg = job.seg_end - job.seg_begin;
-    const int q = kk / n_seg, sidx = kk - q * n_seg;
-    const int r0 = q * qt_rows, r1 = min(job.len, r0 + qt_rows);
-    const SegDesc& sg = a.segs[job.seg_begin + sidx];
-    const int nt = (sg.len + kBK - 1) / kBK;
-    const int qmax = job.pos[r1 - 1];
-    const int qdmin = docm ? job.doc[r0] : 0, qdmax = docm ? job.doc[r1 - 1] : 0;
-    int c;
-    if (tt.stride > 0) {
-      using T = TabLds<Sm>;
-      const int b = (job.seg_begin + sidx - tt.s0) * tt.stride;
-      const int32_t* f = T::fpos(sm) + b;
-      const int32_t* fdc = T::fdoc(sm) + b;
-      const int32_t* ldc = T::ldoc(sm) + b;
-      c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return f[m]; }, [&](int m) { return fdc[m]; },
-                        [&](int m) { return ldc[m]; });
-    } else {
-      c = visible_tiles(nt, docm, qmax, qdmin, qdmax, [&](int m) { return sg.pos[m * kBK]; },
-                        [&](int m) { return sg.doc[m * kBK]; },
-                        [&](int m) { return sg.doc[min(sg.len, m * kBK + kBK) - 1]; });
-    }
-    if (c) atomicAdd(&scratch[base + q], c);
-  }
-  __syncthreads();
-  if (tid == 0) {
+  } else if (tid == 0) {
     // splits per (job, query tile), then the item of this work-group
     int t0 = 0;
     int total = 0;  // splits over every job, per head group
@@ -625,10 +810,8 @@ __device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, int qt_r
       }
       t0 += n_qt;
     }
-    const int n_hg = a.hq / a.heads_per_wg;
-    const int b = blockIdx.x;
     int rj = -1, rq = 0, rs = 0, rhg = 0, rns = 1;
-    int j = 0, i = 0, hg_base = 0, hg_span = 1;
+    int i = 0, hg_base = 0, hg_span = 1;
     bool live = false;
     if ((n_hg & 7) == 0) {
       // XCD b % 8 takes head groups [x * hpx, (x + 1) * hpx) of every job
@@ -646,7 +829,7 @@ __device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, int qt_r
     }
     if (live) {
       t0 = 0;
-      for (j = 0; j < a.n_jobs; ++j) {
+      for (int j = 0; j < a.n_jobs; ++j) {
         const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
         int m = 0;
         for (int q = 0; q < n_qt; ++q) m += scratch[t0 + q];
@@ -679,11 +862,11 @@ __device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, int qt_r
   }
   __syncthreads();
   WorkItem w;
-  w.job = scratch[n_all];
-  w.qt = scratch[n_all + 1];
-  w.split = scratch[n_all + 2];
-  w.hg = scratch[n_all + 3];
-  ns_out = scratch[n_all + 4];
+  w.job = __builtin_amdgcn_readfirstlane(scratch[n_all]);
+  w.qt = __builtin_amdgcn_readfirstlane(scratch[n_all + 1]);
+  w.split = __builtin_amdgcn_readfirstlane(scratch[n_all + 2]);
+  w.hg = __builtin_amdgcn_readfirstlane(scratch[n_all + 3]);
+  ns_out = __builtin_amdgcn_readfirstlane(scratch[n_all + 4]);
   __syncthreads();  // scratch free again
   return w;
 }
