@@ -64,6 +64,8 @@ lib.cpattn_partition_rope.argtypes = [_c_i32, _c_i64, _c_i32, _c_i32, _P(_c_i32)
                                       _c_vp, _c_i32, _P(_c_vp), _P(_c_vp), _P(_c_i64), _P(cpattn_rope_desc),
                                       _c_vp]
 lib.cpattn_partition_rope.restype = _c_i32
+lib.cpattn_zigzag_edge_visible.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _P(_c_i32)]
+lib.cpattn_zigzag_edge_visible.restype = _c_i32
 lib.cpattn_tile_fwd.argtypes = [_P(cpattn_attn_desc), _c_i32, _P(cpattn_q_block), _P(cpattn_kv_seg),
                                 _P(_c_vp), _P(_c_vp), _c_vp, _c_sz, _c_vp]
 lib.cpattn_tile_fwd.restype = _c_i32
@@ -101,7 +103,8 @@ lib.cpattn_bwd_noalloc.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_
                                    _c_vp, _c_vp, _c_vp, _c_vp, _P(_c_vp), _P(_c_vp), _c_vp]
 lib.cpattn_bwd_noalloc.restype = _c_i32
 
-EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_partition_rope", "cpattn_tile_fwd",
+EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_partition_rope",
+            "cpattn_zigzag_edge_visible", "cpattn_tile_fwd",
             "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
             "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
             "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
@@ -199,6 +202,16 @@ def cpattn_partition(mode: int, total: int, cp_size: int, cp_rank: int, idx_out,
         _check(lib.cpattn_partition(*args, _stream(stream)), "cpattn_partition")
     else:
         _check(lib.cpattn_partition_rope(*args, ctypes.byref(rope), _stream(stream)), "cpattn_partition_rope")
+
+
+def cpattn_zigzag_edge_visible(seq_len: int, cp_size: int, q_rank: int, q_part: int, kv_owner: int,
+                               kv_part: int) -> bool:
+    """Whether the (query block, KV segment) edge of a zigzag share has visible pairs
+    (part: 0 front chunk, 1 back chunk, -1 both)."""
+    out = _c_i32(0)
+    _check(lib.cpattn_zigzag_edge_visible(seq_len, cp_size, q_rank, q_part, kv_owner, kv_part, ctypes.byref(out)),
+           "cpattn_zigzag_edge_visible")
+    return bool(out.value)
 
 
 def _workspace(nbytes, like, stream=None):

@@ -181,6 +181,23 @@ const char* cpattn_strerror(int status) {
 
 int cpattn_version(void) { return 100; }
 
+int cpattn_zigzag_edge_visible(int64_t seq_len, int32_t cp_size, int32_t q_rank, int32_t q_part,
+                               int32_t kv_owner, int32_t kv_part, int32_t* visible) {
+  if (visible == nullptr || cp_size < 1 || seq_len < 1) return CPATTN_ERR_ARG;
+  if (q_rank < 0 || q_rank >= cp_size || kv_owner < 0 || kv_owner >= cp_size) return CPATTN_ERR_ARG;
+  if (q_part < -1 || q_part > 1 || kv_part < -1 || kv_part > 1) return CPATTN_ERR_ARG;
+  if (seq_len % (2 * (int64_t)cp_size) != 0) return CPATTN_ERR_ALIGN;
+  const int64_t chunk = seq_len / (2 * (int64_t)cp_size);
+  // the block's chunks end at (c + 1) * chunk - 1, the segment's start at c * chunk
+  const int64_t q_front = q_rank, q_back = 2 * (int64_t)cp_size - 1 - q_rank;
+  const int64_t k_front = kv_owner, k_back = 2 * (int64_t)cp_size - 1 - kv_owner;
+  const int64_t q_chunk = q_part == 0 ? q_front : q_back;  // the later chunk when both
+  const int64_t k_chunk = kv_part == 1 ? k_back : k_front;  // the earlier chunk when both
+  const int64_t q_max = (q_chunk + 1) * chunk - 1, k_min = k_chunk * chunk;
+  *visible = k_min <= q_max ? 1 : 0;
+  return CPATTN_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -12,9 +12,10 @@ arithmetic runs in libcpattn through the C-ABI calls of this package.
   order.  Inside an owner, its chunks keep their storage order (front, then back).
 * Edge set of the Q-KV task graph ("Context Parallelism (CP)", section 2.1): an edge
   (query chunk, KV segment) exists when some key position is <= some query position;
-  for zigzag shards the position ranges are known from (S, cp), so empty edges are
-  dropped before launch.  Packed documents and striped shards keep every edge (the
-  kernels classify; under the striped split every edge holds visible pairs).
+  for zigzag shards the library decides this from (S, cp) alone
+  (cpattn_zigzag_edge_visible), so empty edges are never launched.  Packed documents
+  and striped shards keep every edge (the kernels classify; under the striped split
+  every edge holds visible pairs).
 * Layouts: "zigzag" (chunk pair), "thd" (packed documents, zigzag inside each) and
   "striped" (rank r holds tokens r, r + cp, ...: the interleaved split of the
   ring-attention page, section 5).
@@ -28,7 +29,7 @@ import torch
 from . import (PART_STRIPED, PART_THD, PART_ZIGZAG, MASK_CAUSAL, MASK_CAUSAL_DOC, attn_desc, cpattn_bwd,
                cpattn_bwd_workspace_bytes, cpattn_merge, cpattn_partition, cpattn_stream_fwd,
                cpattn_stream_fwd_workspace_bytes, cpattn_tile_fwd, cpattn_tile_fwd_workspace_bytes,
-               kv_seg, q_block)
+               cpattn_zigzag_edge_visible, kv_seg, q_block)
 
 
 def ring_order(cp: int, rank: int):
@@ -64,10 +65,6 @@ class RankShare:
     def mask(self):
         return MASK_CAUSAL_DOC if self.packed else MASK_CAUSAL
 
-    @property
-    def chunk(self):
-        return self.seq // (2 * self.cp)
-
     def desc(self, scale: float = 0.0):
         return attn_desc(self.hq, self.hkv, self.d, self.dtype, self.mask, scale)
 
@@ -90,25 +87,15 @@ class RankShare:
         n = self.seq // self.cp
         return [(0, n // 2), (n // 2, n)]
 
-    def _pos_range_q(self, a, b):
-        # zigzag: front chunk = rank, back chunk = 2cp-1-rank
-        c = self.rank if a == 0 else 2 * self.cp - 1 - self.rank
-        return c * self.chunk, (c + 1) * self.chunk - 1
-
-    def _pos_min_seg(self, owner, part, granularity):
-        if granularity == "owner" or part == 0:
-            return owner * self.chunk
-        return (2 * self.cp - 1 - owner) * self.chunk
-
     def edges(self, granularity: str = "owner"):
         """Non-empty (query chunk, segment) edges: list of (q rows (a,b), seg, seg index)."""
         segs = self.segments(granularity)
         out = []
-        for (a, b) in self.q_chunks():
+        for qi, (a, b) in enumerate(self.q_chunks()):
             for si, (seg, (o, pi), _) in enumerate(segs):
                 if not self.packed and not self.striped:
-                    _, qhi = self._pos_range_q(a, b)
-                    if self._pos_min_seg(o, pi, granularity) > qhi:
+                    kv_part = -1 if granularity == "owner" else pi
+                    if not cpattn_zigzag_edge_visible(self.seq, self.cp, self.rank, qi, o, kv_part):
                         continue
                 out.append(((a, b), seg, si))
         return out

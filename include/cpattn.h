@@ -179,6 +179,31 @@ int cpattn_partition_rope(int32_t mode, int64_t total, int32_t cp_size, int32_t 
                           const cpattn_rope_desc* rope, void* stream);
 
 /*
+ * cpattn_zigzag_edge_visible — whether an edge of a zigzag share's Q-KV task graph
+ * holds any (query, key) pair that the causal mask keeps, so that edges without work
+ * are never launched.
+ *
+ * Source: "Context Parallelism (CP)", section 2.1 (the task graph has an edge (i, j)
+ * where KV block j holds keys visible to Q block i under the mask) and section 4
+ * (zigzag: 2*cp equal chunks, rank r holds chunk r and chunk 2cp-1-r).  Positions are
+ * the tokens' global indices, so within a chunk they are contiguous, and an edge has
+ * work exactly when the segment's smallest key position is <= the block's largest
+ * query position.
+ *
+ *  seq_len          tokens of the sequence: positive and a multiple of 2*cp_size.
+ *  cp_size          ranks (>= 1).
+ *  q_rank, kv_owner ranks holding the query block and the KV segment (0..cp_size-1).
+ *  q_part, kv_part  which of that rank's chunks the block / segment holds:
+ *                   0 = its front chunk (chunk rank), 1 = its back chunk
+ *                   (chunk 2cp-1-rank), -1 = both (the rank's whole shard).
+ *  visible          host output: 1 if the edge has work, else 0.
+ * Host only (no GPU call).  Errors: ARG (sizes, ranks or parts out of range, NULL
+ * output); ALIGN (seq_len not a multiple of 2*cp_size).
+ */
+int cpattn_zigzag_edge_visible(int64_t seq_len, int32_t cp_size, int32_t q_rank, int32_t q_part,
+                               int32_t kv_owner, int32_t kv_part, int32_t* visible);
+
+/*
  * cpattn_tile_fwd — TileAttention over a batch of independent (Q block, KV segment)
  * edges of the Q-KV task graph.
  *

@@ -34,6 +34,17 @@ int main() {
   void* dst[8] = {F, F, F, F, F, F, F, F};
   int64_t rb[8] = {256, 256, 512, 16, 32, 48, 64, 1 << 20};
 
+  // zigzag edge check (host arithmetic only)
+  int32_t vis = -1;
+  EXPECT(cpattn_zigzag_edge_visible(8192, 4, 0, 0, 1, -1, &vis), CPATTN_OK);
+  EXPECT(vis, 0);
+  EXPECT(cpattn_zigzag_edge_visible(8192, 4, 0, 1, 3, 1, &vis), CPATTN_OK);
+  EXPECT(vis, 1);
+  EXPECT(cpattn_zigzag_edge_visible(INT64_MAX - 7, 4, 3, -1, 3, -1, &vis), CPATTN_OK);
+  EXPECT(cpattn_zigzag_edge_visible(8192, 4, 4, 0, 0, 0, &vis), CPATTN_ERR_ARG);
+  EXPECT(cpattn_zigzag_edge_visible(8190, 4, 0, 0, 0, 0, &vis), CPATTN_ERR_ALIGN);
+  EXPECT(cpattn_zigzag_edge_visible(8192, 4, 0, 0, 0, 0, nullptr), CPATTN_ERR_ARG);
+
   // partition and its rotary form
   EXPECT(cpattn_partition(9, 64, 2, 0, nullptr, nullptr, 0, Fo, nullptr, 0, src, dst, rb, nullptr), CPATTN_ERR_ARG);
   EXPECT(cpattn_partition(CPATTN_PART_ZIGZAG, 100, 4, 0, nullptr, nullptr, 0, Fo, nullptr, 0, src, dst, rb, nullptr),

@@ -283,3 +283,38 @@ def test_segment_and_row_limits():
     # and the dQ pass of a grouped list runs unsplit: no split workspace is planned
     assert C.lib.cpattn_bwd_dq_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 40, segs) == 0
     assert C.lib.cpattn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(q), 40, segs) == 1024 * 8 * 4
+
+
+def test_zigzag_edge_visible_matches_the_causal_mask():
+    # brute force over the oracle's zigzag rows: an edge has work iff some key position
+    # of the segment is <= some query position of the block
+    import numpy as np
+    import oracle
+
+    out = ctypes.c_int32(-1)
+    checked = 0
+    for seq, cp in [(16, 1), (32, 2), (64, 4), (96, 3), (128, 8), (8192, 4)]:
+        chunk = seq // (2 * cp)
+        for r in range(cp):
+            rows_q = oracle.zigzag_indices(seq, cp, r)
+            for o in range(cp):
+                rows_k = oracle.zigzag_indices(seq, cp, o)
+                for qp in (-1, 0, 1):
+                    q = rows_q if qp < 0 else rows_q[qp * chunk:(qp + 1) * chunk]
+                    for kp in (-1, 0, 1):
+                        k = rows_k if kp < 0 else rows_k[kp * chunk:(kp + 1) * chunk]
+                        want = bool(np.any(k[:, None] <= q[None, :]))
+                        assert C.lib.cpattn_zigzag_edge_visible(seq, cp, r, qp, o, kp, ctypes.byref(out)) == C.OK
+                        assert bool(out.value) == want, (seq, cp, r, qp, o, kp)
+                        assert C.cpattn_zigzag_edge_visible(seq, cp, r, qp, o, kp) == want
+                        checked += 1
+    assert checked == 990
+    # the diagonal edge always has work; rank 0's front chunk sees no later owner
+    assert C.cpattn_zigzag_edge_visible(8192, 4, 2, 0, 2, 0)
+    assert not C.cpattn_zigzag_edge_visible(8192, 4, 0, 0, 1, -1)
+    bad = [(0, 2, 0, 0, 0, 0), (64, 0, 0, 0, 0, 0), (64, 2, 2, 0, 0, 0), (64, 2, 0, 2, 0, 0),
+           (64, 2, 0, 0, -1, 0), (64, 2, 0, 0, 0, -2)]
+    for args in bad:
+        assert C.lib.cpattn_zigzag_edge_visible(*args, ctypes.byref(out)) == C.ERR_ARG, args
+    assert C.lib.cpattn_zigzag_edge_visible(66, 2, 0, 0, 0, 0, ctypes.byref(out)) == C.ERR_ALIGN
+    assert C.lib.cpattn_zigzag_edge_visible(64, 2, 0, 0, 0, 0, None) == C.ERR_ARG
