@@ -351,23 +351,33 @@ struct RowSmem {
   alignas(16) int32_t pd[kQBufs][2][kBQ];  // positions, then document ids
 };
 
-// Per-lane source slots of the Q / dO fill instructions: fill instruction jj of a tile
+// Per-lane sources of the Q / dO fill instructions: fill instruction jj of a tile
 // writes the 64 16-byte slots 64*jj .. 64*jj+63 of the tile image, lane l slot
-// 64*jj + l (row-major, kSlots per row, the last ones padding).
+// 64*jj + l (row-major, kSlots per row, the last ones padding).  The byte offsets of a
+// whole tile's sources are fixed for the kernel and computed once; only a ragged last
+// tile recomputes them with its rows clamped.  The LDS images' base offsets are taken
+// once too, so a fill costs the loop three instructions (m0, the wait state it needs,
+// the load) instead of re-deriving pointers every step.
 template <int D>
 struct QFillPlan {
   using Sm = DkdvSmem<D>;
-  uint32_t slot[Sm::kBigPer];  // row << 16 | element column
+  uint32_t off[Sm::kBigPer];  // (row * rs + column) * 2 of a whole tile
+  uint32_t lds_q, lds_o;      // LDS byte offsets of qs[0] and dos[0]
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  __device__ __forceinline__ static uint32_t source(int wave, int lane, int j, uint32_t last, uint32_t rs) {
+    const int jj = (wave + 4 * j) % Sm::kTileInst;
+    const int s = kWave * jj + lane;
+    const int c = s % Sm::kSlots;
+    // slots past the last row (slack) and padding slots load a valid dummy chunk
+    const uint32_t row = min((uint32_t)min(s / Sm::kSlots, kBQ - 1), last);
+    return (row * rs + (uint32_t)(c < D / 8 ? c * 8 : 0)) * 2;
+  }
+
+  __device__ __forceinline__ void init(const Sm& sm, int wave, int lane, uint32_t rs) {
 #pragma unroll
-    for (int j = 0; j < Sm::kBigPer; ++j) {
-      const int jj = (wave + 4 * j) % Sm::kTileInst;
-      const int s = kWave * jj + lane;
-      const int c = s % Sm::kSlots;
-      // slots past the last row (slack) and padding slots load a valid dummy chunk
-      slot[j] = (uint32_t)min(s / Sm::kSlots, kBQ - 1) << 16 | (uint32_t)(c < D / 8 ? c * 8 : 0);
-    }
+    for (int j = 0; j < Sm::kBigPer; ++j) off[j] = source(wave, lane, j, kBQ - 1, rs);
+    lds_q = lds_offset(sm.qs[0]);
+    lds_o = lds_offset(sm.dos[0]);
   }
 };
 
@@ -418,19 +428,28 @@ __device__ __forceinline__ void fill_qtile(DkdvSmem<D>& sm, RowSmem& rsm, int bu
   const int64_t base = ((int64_t)r0 * a.hq + head) * D;
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + base;
   const bf16* ob = reinterpret_cast<const bf16*>(a.dout) + base;
-  // byte offsets of every fill first, each in its own register, then the burst
-  uint32_t offs[Sm::kBigPer];
+  const uint32_t ib = (uint32_t)buf * (Sm::kImage * 2);
+  auto burst = [&](const uint32_t(&offs)[Sm::kBigPer]) {
 #pragma unroll
-  for (int j = 0; j < Sm::kBigPer; ++j) offs[j] = (min(fp.slot[j] >> 16, last) * rs + (fp.slot[j] & 0xffffu)) * 2;
+    for (int j = 0; j < Sm::kBigPer; ++j) {
+      const int jj = wave + 4 * j;
+      const bool isq = jj < Sm::kTileInst;
+      const uint32_t dst = (isq ? fp.lds_q : fp.lds_o) + ib + (uint32_t)(isq ? jj : jj - Sm::kTileInst) * (kWave * 16);
+      fill16_off(isq ? qb : ob, offs[j], dst);
+    }
+  };
+  if (last == kBQ - 1) {
+    burst(fp.off);
+  } else {
+    // ragged last tile: rows past the end read the last row (their positions mark them
+    // invisible); each offset in its own register before the burst
+    uint32_t offs[Sm::kBigPer];
 #pragma unroll
-  for (int j = 0; j < Sm::kBigPer; ++j) {
-    const int jj = wave + 4 * j;
-    const bool isq = jj < Sm::kTileInst;
-    const uint32_t dst = lds_offset(isq ? sm.qs[buf] : sm.dos[buf]) + (isq ? jj : jj - Sm::kTileInst) * kWave * 16;
-    fill16_off(isq ? qb : ob, offs[j], dst);
+    for (int j = 0; j < Sm::kBigPer; ++j) offs[j] = QFillPlan<D>::source(wave, lane, j, last, rs);
+    burst(offs);
+#pragma unroll
+    for (int j = 0; j < Sm::kBigPer; ++j) asm volatile("" ::"v"(offs[j]));
   }
-#pragma unroll
-  for (int j = 0; j < Sm::kBigPer; ++j) asm volatile("" ::"v"(offs[j]));
   // per-row values: wave 1 positions (lanes 0..31) and document ids (32..63), the
   // others log-sum-exp (0..31) and delta (32..63) (identical data)
   const int q = r0 + (int)min((uint32_t)(lane & 31), last);
@@ -708,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     vis_hi = -1;
   }
   QFillPlan<D> fp;
-  fp.init(wave, lane);
+  fp.init(sm, wave, lane, (uint32_t)a.hq * D);
   lds_barrier();
   // range of query tiles the work-group's keys can see (read from the query block:
   // any number of local rows)
