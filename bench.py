@@ -338,12 +338,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(q, k, v, w, r, cu=None, min_seconds=12.0, max_reps=8):
+def cpu_baseline(q, k, v, w, r, cu=None, min_seconds=10.0, max_reps=8):
     """The float64 oracle, as it stands, on a bounded sample of the same share: forward and
-    backward of the rank's query rows against all keys, repeated until about
-    ``min_seconds`` of CPU work (the 8K share is small); for larger shares an evenly
-    spaced subset of the rows, sized for one repetition of about that length.  A packed
-    share passes every row's and key's document id with the document mask."""
+    backward of the rank's query rows against all keys (for shares longer than 8K an
+    evenly spaced subset of 64 rows), repeated until about ``min_seconds`` of CPU work.
+    A packed share passes every row's and key's document id with the document mask."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -367,7 +366,7 @@ def cpu_baseline(q, k, v, w, r, cu=None, min_seconds=12.0, max_reps=8):
         OA.attention_bwd(qr, k, v, g, rows, keys, **docs)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= max_reps or w.seq > 8192:
+        if dt >= min_seconds or reps >= max_reps:
             break
     if w.packed:
         pairs = int(np.sum(rows - np.asarray(cu, dtype=np.int64)[docs["q_doc"]] + 1))
