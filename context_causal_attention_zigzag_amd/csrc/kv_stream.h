@@ -28,7 +28,7 @@ template <int D, int KS, int VS>
 struct KvSmem {
   static constexpr int kKS = KS;
   static constexpr int kVS = VS;
-  bf16 k[2][kBK * kKS];
+  alignas(16) bf16 k[2][kBK * kKS];
   bf16 v[2][kBK * kVS];
   int32_t kpos[2][kBK];
   int32_t kdoc[2][kBK];
@@ -654,7 +654,7 @@ __device__ __forceinline__ int count_visible(const FwdArgs& a, const LaneDescs& 
 // count (most first; ties: the later pair first) and takes the pair of rank (b / 8) /
 // hpx, head group (b / 8) % hpx of its XCD's block: each XCD's list is then the
 // longest-processing-time-first schedule of its share, its head groups inner.  Every
-// thread of the work-group calls this; scratch holds kMaxRankedTiles + 1 ints of LDS
+// thread of the work-group calls this; scratch holds kMaxRankedTiles + 8 ints of LDS
 // that nothing else uses yet.
 template <int NT, class Sm>
 __device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, const LaneDescs& ld, int qt_rows,
@@ -668,17 +668,29 @@ __device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, const Lan
   w.hg = (b & 7) * hpx + (i - rank * hpx);
   const int tid = threadIdx.x;
   const int n_all = count_visible<NT, Sm>(a, ld, qt_rows, scratch, sm, tt);
+  // rank of pair t = pairs with a larger count, plus pairs with the same count and a
+  // larger index; every thread reads the counts four at a time (16-byte LDS reads, four
+  // in flight), the list padded with -1 (no count is negative)
+  const int n4 = (n_all + 3) & ~3;
+  for (int t = n_all + tid; t < n4; t += NT) scratch[t] = -1;
+  __syncthreads();
+  const int4* s4 = reinterpret_cast<const int4*>(scratch);
   for (int t = tid; t < n_all; t += NT) {
     const int c = scratch[t];
     int r = 0;
-    for (int p = 0; p < n_all; ++p) {
-      const int cp = scratch[p];
-      r += (cp > c) | ((cp == c) & (p > t));
+#pragma unroll 4
+    for (int p4 = 0; p4 < n4 / 4; ++p4) {
+      const int4 v = s4[p4];
+      const int p = 4 * p4;
+      r += (v.x > c) | ((v.x == c) & (p > t));
+      r += (v.y > c) | ((v.y == c) & (p + 1 > t));
+      r += (v.z > c) | ((v.z == c) & (p + 2 > t));
+      r += (v.w > c) | ((v.w == c) & (p + 3 > t));
     }
-    if (r == rank) scratch[n_all] = t;
+    if (r == rank) scratch[n4] = t;
   }
   __syncthreads();
-  int t = __builtin_amdgcn_readfirstlane(scratch[n_all]);
+  int t = __builtin_amdgcn_readfirstlane(scratch[n4]);
   __syncthreads();  // scratch free again
   int j = 0;
   while (t >= (a.jobs[j].len + qt_rows - 1) / qt_rows) {
