@@ -176,7 +176,10 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   int ns_mine = 1;      // splits that exist for this work item's query tile (compact launches)
   bool tt_all = false;  // the tile table covers every segment of the launch
   if constexpr (RANKED) {
-    wi = ranked_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
+    if (a.plan != nullptr)
+      wi = planned_work_item<NW * kWave>(a, qt_rows, sm, tt);
+    else
+      wi = ranked_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
   } else {
     if (a.compact) {
       wi = compact_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
@@ -936,8 +939,17 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   f.padded_wgs = (total + 7) & ~7;
   const DqExtra x{dout, delta, scale, accumulate ? 1 : 0};
   const dim3 grid(f.padded_wgs), block(nw * kWave);
-  const bool ranked = kv::ranked_plan(f, qt_rows);
+  const bool ranked = kv::ranked_plan(f, qt_rows, f.plan != nullptr ? kv::kMaxPlanTiles : kv::kMaxRankedTiles);
+  if (!ranked) f.plan = nullptr;
   f.compact = !ranked && kv::compact_plan(f, qt_rows) ? 1 : 0;
+  if (f.plan != nullptr) {
+    if (d == 64)
+      hipLaunchKernelGGL((kv::plan_ranked_kernel<64>), dim3(1), dim3(kv::kPlanThreads), 0, stream, f, qt_rows);
+    else
+      hipLaunchKernelGGL((kv::plan_ranked_kernel<128>), dim3(1), dim3(kv::kPlanThreads), 0, stream, f, qt_rows);
+    const hipError_t pe = hipGetLastError();
+    if (pe != hipSuccess) return pe;
+  }
   if (d == 64) {
     if (nw == 8)
       launch_dq<64, 8>(ranked, grid, block, stream, f, x);

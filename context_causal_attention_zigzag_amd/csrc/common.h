@@ -256,6 +256,8 @@ struct FwdArgs {
   int32_t padded_wgs;    // grid size (multiple of 8)
   int32_t wg_waves;      // waves per work-group of the launch (32 query rows each)
   int32_t compact;       // KV splits numbered densely (no work-group for an empty split)
+  int32_t plan_tiles;    // a ranked launch planned once: its query tiles over all jobs (else 0)
+  int32_t* plan;         // that plan in the workspace (rank order, then the KV tile table)
 };
 
 struct BwdArgs {

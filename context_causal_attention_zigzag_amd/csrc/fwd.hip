@@ -217,7 +217,10 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
   int ns_mine = 1;      // splits that exist for this work item's query tile (compact launches)
   bool tt_all = false;  // the tile table covers every segment of the launch
   if constexpr (RANKED) {
-    wi = ranked_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
+    if (a.plan != nullptr)
+      wi = planned_work_item<NW * kWave>(a, qt_rows, sm, tt);
+    else
+      wi = ranked_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt);
   } else {
     if (a.compact) {
       wi = compact_work_item<NW * kWave>(a, ld, qt_rows, reinterpret_cast<int*>(&sm), sm, tt, ns_mine);
@@ -475,8 +478,14 @@ hipError_t launch_fwd_d(FwdArgs& a, int dtype, bool partial_out, hipStream_t str
     a.padded_wgs = (total + 7) & ~7;
     if (total == 0) return hipSuccess;
     const dim3 grid(a.padded_wgs), block(nw * kWave);
-    const bool ranked = ranked_plan(a, qt_rows);
+    const bool ranked = ranked_plan(a, qt_rows, a.plan != nullptr ? kMaxPlanTiles : kMaxRankedTiles);
+    if (!ranked) a.plan = nullptr;
     a.compact = !ranked && compact_plan(a, qt_rows) ? 1 : 0;
+    if (a.plan != nullptr) {
+      hipLaunchKernelGGL((plan_ranked_kernel<D>), dim3(1), dim3(kPlanThreads), 0, stream, a, qt_rows);
+      const hipError_t pe = hipGetLastError();
+      if (pe != hipSuccess) return pe;
+    }
     if (nw == 8) {
       if (partial_out)
         launch_fwd_bf16<D, true, 8>(ranked, grid, block, stream, a);
@@ -550,11 +559,26 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
   };
   if (waves == 0) waves = query_wgs(8) >= num_cu ? 8 : 4;
   a.wg_waves = waves;
+  a.plan_tiles = 0;
+  a.plan = nullptr;
   if (dtype != 0 || !allow_split) return 0;
   const int64_t base = query_wgs(waves);
   const int64_t slots = (int64_t)wg_per_cu(waves) * num_cu;
-  if (base == 0 || base >= slots) return 0;
   const int qt_rows = waves * kRowsPerWave / hpw;
+  if (base == 0 || base >= slots) {
+    // no KV split: a ranked launch is planned once when it runs more than two rounds of
+    // work-groups (the per-work-group ranking then costs more than one plan) or holds
+    // more query tiles than a work-group can rank
+    if (base > 0 && kv::ranked_plan(a, qt_rows, kv::kMaxPlanTiles)) {
+      int n_all = 0, n_tab = 0;
+      kv::plan_layout(a, d, qt_rows, n_all, n_tab);
+      if (base > 2 * slots || n_all > kv::kMaxRankedTiles) {
+        a.plan_tiles = n_all;
+        return align256(kv::plan_bytes(n_all, n_tab));
+      }
+    }
+    return 0;
+  }
   int64_t visible = 0;  // expected visible (query tile, KV tile) pairs over all work-groups
   for (int j = 0; j < a.n_jobs; ++j)
     visible += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw) * a.jobs[j].n_tiles / 2;
@@ -590,6 +614,7 @@ void assign_fwd_workspace(FwdArgs& a, int d, void* ws) {
     jb.ws_lse = reinterpret_cast<float*>(p);
     p += align256((size_t)jb.n_split * jb.len * a.hq * sizeof(float));
   }
+  if (a.plan_tiles > 0) a.plan = reinterpret_cast<int32_t*>(p);
 }
 
 hipError_t launch_fwd(const FwdArgs& args, int d, int dtype, bool partial_out, hipStream_t stream) {

@@ -501,18 +501,48 @@ __device__ __forceinline__ WorkItem indexed_work_item(const FwdArgs& a, int qt_r
 // Ranked order, for packed documents: a query tile's work follows the lengths of the
 // documents it falls in, not its index.
 constexpr int kMaxRankedTiles = 1024;
+// A ranked launch with more query tiles, or with many rounds of work-groups, is planned
+// once by a single work-group (plan_ranked_kernel) when the workspace has room.
+constexpr int kMaxPlanTiles = 4096;
 
 // The launch ranks when the head groups split evenly over the 8 XCDs, no job has KV
 // splits and the jobs hold 1..kMaxRankedTiles query tiles in all; then every logical
 // work item is one (head group, job, query tile) and the grid needs no padding.
-inline bool ranked_plan(const FwdArgs& a, int qt_rows) {
+inline bool ranked_plan(const FwdArgs& a, int qt_rows, int cap = kMaxRankedTiles) {
   if (a.mask != kMaskCausalDoc || (a.hq / a.heads_per_wg) % 8 != 0) return false;
   int n_all = 0;
   for (int j = 0; j < a.n_jobs; ++j) {
     if (a.jobs[j].n_split != 1) return false;
     n_all += (a.jobs[j].len + qt_rows - 1) / qt_rows;
   }
-  return n_all > 0 && n_all <= kMaxRankedTiles;
+  return n_all > 0 && n_all <= cap;
+}
+
+// Entries per array of the KV tile table in LDS: the kernels' smaller K/V image has a
+// row stride of d + 8 elements (TabLds::kCap).
+inline int tile_tab_cap(int d) { return 16 * (d + 8); }
+
+// Layout of a ranked launch's plan: n_all ints of rank order (padded to 64), then the
+// tile table's four arrays of n_tab entries (first / last key position, first / last
+// key document of every KV tile of segments [0, s1)); n_tab = 0 when the table does
+// not fit in LDS (the kernels then search global memory).
+inline void plan_layout(const FwdArgs& a, int d, int qt_rows, int& n_all, int& n_tab) {
+  n_all = 0;
+  int s1 = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    n_all += (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    s1 = s1 > a.jobs[j].seg_end ? s1 : a.jobs[j].seg_end;
+  }
+  int stride = 0;
+  for (int s = 0; s < s1; ++s) {
+    const int nt = (a.segs[s].len + kBK - 1) / kBK;
+    stride = stride > nt ? stride : nt;
+  }
+  n_tab = (stride > 0 && s1 * stride <= tile_tab_cap(d)) ? s1 * stride : 0;
+}
+
+inline size_t plan_bytes(int n_all, int n_tab) {
+  return (size_t)(((n_all + 63) & ~63) + 4 * n_tab) * sizeof(int32_t);
 }
 
 // KV tiles the work-group of query rows [r0, r1) walks in one segment of nt tiles: from
@@ -700,6 +730,132 @@ __device__ __forceinline__ WorkItem ranked_work_item(const FwdArgs& a, const Lan
   w.job = j;
   w.qt = t;
   return w;
+}
+
+// The work item of a planned ranked launch: its pair from the plan's rank order (the
+// same order ranked_work_item computes), and the tile table copied from the plan into
+// LDS with coalesced loads, all of a thread's loads issued before any store.
+template <int NT, class Sm>
+__device__ __forceinline__ WorkItem planned_work_item(const FwdArgs& a, int qt_rows, Sm& sm, TileTab& tt) {
+  using T = TabLds<Sm>;
+  const int b = blockIdx.x;
+  const int hpx = (a.hq / a.heads_per_wg) >> 3;
+  const int i = b >> 3;
+  const int rank = i / hpx;
+  WorkItem w;
+  w.split = 0;
+  w.hg = (b & 7) * hpx + (i - rank * hpx);
+  int n_all = 0, s1 = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    n_all += (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    s1 = max(s1, a.jobs[j].seg_end);
+  }
+  int t = a.plan[rank];
+  int stride = 0;
+  for (int s = 0; s < s1; ++s) stride = max(stride, (a.segs[s].len + kBK - 1) / kBK);
+  const int n_tab = (stride > 0 && s1 * stride <= T::kCap) ? s1 * stride : 0;
+  tt = {0, n_tab > 0 ? stride : 0};
+  if (n_tab > 0) {
+    const bool docm = a.mask == kMaskCausalDoc;
+    const int32_t* tab = a.plan + ((n_all + 63) & ~63);
+    constexpr int kIt = (T::kCap + NT - 1) / NT;
+    int v[kIt][4];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = threadIdx.x + it * NT;
+      if (it * NT < n_tab && e < n_tab) {
+        v[it][0] = tab[e];
+        v[it][1] = tab[n_tab + e];
+        if (docm) {
+          v[it][2] = tab[2 * n_tab + e];
+          v[it][3] = tab[3 * n_tab + e];
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = threadIdx.x + it * NT;
+      if (it * NT < n_tab && e < n_tab) {
+        T::fpos(sm)[e] = v[it][0];
+        T::lpos(sm)[e] = v[it][1];
+        if (docm) {
+          T::fdoc(sm)[e] = v[it][2];
+          T::ldoc(sm)[e] = v[it][3];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  t = __builtin_amdgcn_readfirstlane(t);
+  int j = 0;
+  while (t >= (a.jobs[j].len + qt_rows - 1) / qt_rows) {
+    t -= (a.jobs[j].len + qt_rows - 1) / qt_rows;
+    ++j;
+  }
+  w.job = j;
+  w.qt = t;
+  return w;
+}
+
+// The plan of a ranked launch, built once: one work-group counts every (job, query
+// tile)'s visible KV tiles exactly as ranked_work_item does, sorts the pairs by
+// (count, index), largest first (bitonic sort in LDS), and writes the order and the tile
+// table to a.plan.  qt_rows as in the launch it plans.
+template <int D>
+struct PlanSmem {
+  KvSmem<D, D + 8, D + 8> kv;  // the tile table lives in its second K/V images
+  alignas(16) int32_t cnt[kMaxPlanTiles + 8];
+  alignas(16) uint64_t key[kMaxPlanTiles];
+};
+
+constexpr int kPlanThreads = 1024;
+
+template <int D>
+__global__ __launch_bounds__(kPlanThreads) void plan_ranked_kernel(FwdArgs a, int qt_rows) {
+  using Sm = KvSmem<D, D + 8, D + 8>;
+  using T = TabLds<Sm>;
+  __shared__ PlanSmem<D> ps;
+  const int tid = threadIdx.x;
+  const LaneDescs ld = load_lane_descs(a);
+  TileTab tt{0, 0};
+  const int n_all = count_visible<kPlanThreads, Sm>(a, ld, qt_rows, ps.cnt, ps.kv, tt);
+  // the tile table, as the launch's work-groups would load it
+  int s1 = 0;
+  for (int j = 0; j < a.n_jobs; ++j) s1 = max(s1, a.jobs[j].seg_end);
+  const int n_tab = tt.stride > 0 ? s1 * tt.stride : 0;
+  int32_t* tab = a.plan + ((n_all + 63) & ~63);
+  const bool docm = a.mask == kMaskCausalDoc;
+  for (int e = tid; e < n_tab; e += kPlanThreads) {
+    tab[e] = T::fpos(ps.kv)[e];
+    tab[n_tab + e] = T::lpos(ps.kv)[e];
+    if (docm) {
+      tab[2 * n_tab + e] = T::fdoc(ps.kv)[e];
+      tab[3 * n_tab + e] = T::ldoc(ps.kv)[e];
+    }
+  }
+  // keys (count + 1, index): descending order is the rank order; padding keys are 0
+  int n2 = 1;
+  while (n2 < n_all) n2 <<= 1;
+  for (int t = tid; t < n2; t += kPlanThreads)
+    ps.key[t] = t < n_all ? ((uint64_t)(uint32_t)(ps.cnt[t] + 1) << 32 | (uint32_t)t) : 0ull;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int t = tid; t < n2; t += kPlanThreads) {
+        const int u = t ^ jj;
+        if (u > t) {
+          const uint64_t x = ps.key[t], y = ps.key[u];
+          const bool desc = (t & k) == 0;
+          if (desc ? x < y : x > y) {
+            ps.key[t] = y;
+            ps.key[u] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = tid; r < n_all; r += kPlanThreads) a.plan[r] = (int32_t)(uint32_t)ps.key[r];
 }
 
 // Work items of a launch whose jobs are split over KV tiles, numbered densely over the

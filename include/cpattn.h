@@ -222,8 +222,14 @@ int cpattn_zigzag_edge_visible(int64_t seq_len, int32_t cp_size, int32_t q_rank,
  *                   KV tiles split over several work-groups whose partial states are
  *                   merged into O_ij (the same associative merge as cpattn_merge);
  *                   with less (or NULL) every query tile runs in one work-group.
- *                   Contents on entry are ignored; the results do not depend on it
- *                   beyond floating-point rounding.
+ *                   Packed-document launches (CPATTN_MASK_CAUSAL_DOC, head groups a
+ *                   multiple of 8) with many rounds of work-groups, or more than 1024
+ *                   query tiles, use it instead for a plan built once by one
+ *                   work-group: the order of their query tiles by work (up to 4096
+ *                   query tiles; without a workspace 1024) and the KV tile table.
+ *                   The planned launch runs the same work items and gives the same
+ *                   results bit for bit.  Contents on entry are ignored; the results
+ *                   do not depend on it beyond floating-point rounding.
  * Rows of a block that see nothing of the segment get (0, -inf).
  * Errors: ARG, UNSUPPORTED (d not 64/128, hq % hkv, dtype, mask), HIP.
  */
@@ -327,7 +333,8 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
 
 /* Bytes of device workspace for cpattn_bwd (0 on invalid arguments): the per-row
  * rowsum(dO * O) values, plus room for the dQ pass to split its KV tiles over more
- * work-groups when the local queries alone cannot fill the GPU.  A workspace that
+ * work-groups when the local queries alone cannot fill the GPU, or for its plan
+ * (see cpattn_bwd_dq).  A workspace that
  * only holds the first part (q.len * hq * 4 bytes, rounded up to 256) is accepted
  * and runs the dQ pass unsplit. */
 size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -360,8 +367,10 @@ int cpattn_bwd_delta(const cpattn_attn_desc* desc, int64_t rows, const void* o, 
  *  workspace        NULL, or a 256-byte aligned device buffer; with
  *                   cpattn_bwd_dq_workspace_bytes() bytes the KV tiles of each query
  *                   tile are split over more work-groups when the queries alone cannot
- *                   fill the GPU (fp32 partial sums, added in a second launch);
- *                   a smaller buffer runs unsplit.  Contents on entry are ignored.
+ *                   fill the GPU (fp32 partial sums, added in a second launch), or
+ *                   a packed-document launch is planned once as for cpattn_tile_fwd;
+ *                   a smaller buffer runs unsplit and unplanned.  Contents on entry
+ *                   are ignored.
  * Errors: ARG, ALIGN, UNSUPPORTED, HIP. */
 int cpattn_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                   const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
