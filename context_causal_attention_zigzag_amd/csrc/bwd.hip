@@ -167,7 +167,8 @@ template <int D, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(FwdArgs a, DqExtra x) {
   using namespace kv;
   __shared__ DqSmem<D> sm;
-  static_assert(sizeof(sm) >= (kMaxRankedTiles + 8) * sizeof(int), "ranking scratch");
+  // the work-list scratch sits in the first K image, below the tile table
+  static_assert(sizeof(DqSmem<D>::k) / 2 >= (2 * kMaxRankedTiles + 16) * sizeof(int), "work-list scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
   const LaneDescs ld = load_lane_descs(a);

@@ -208,7 +208,8 @@ template <int D, bool PARTIAL_OUT, int NW, bool RANKED>
 __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(FwdArgs a) {
   using Sm = FwdSmem<D>;
   __shared__ Sm sm;
-  static_assert(sizeof(Sm) >= (kMaxRankedTiles + 8) * sizeof(int), "ranking scratch");
+  // the work-list scratch sits in the first K image, below the tile table
+  static_assert(sizeof(Sm::k) / 2 >= (2 * kMaxRankedTiles + 16) * sizeof(int), "work-list scratch");
   const int hpw = a.heads_per_wg;
   const int qt_rows = NW * kRowsPerWave / hpw;
   const LaneDescs ld = load_lane_descs(a);

@@ -869,7 +869,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_ranked_kernel(FwdArgs a, in
 // Order: as indexed_work_item (head-group blocks per XCD when the head groups divide
 // by 8, else contiguous ranges), query tiles latest first, splits inner.
 // Every thread calls this; it loads the tile table of every segment of the launch
-// (returned in tt) and uses scratch, kMaxRankedTiles + 8 ints of LDS outside the
+// (returned in tt) and uses scratch, 2 * kMaxRankedTiles + 16 ints of LDS outside the
 // table that nothing uses yet.  job = -1: surplus.
 
 template <int NT, class Sm>
@@ -964,25 +964,59 @@ __device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, const La
         scratch[n_all + 4] = rns;
       }
     }
-  } else if (tid == 0) {
-    // splits per (job, query tile), then the item of this work-group
-    int t0 = 0;
-    int total = 0;  // splits over every job, per head group
-    for (int j = 0; j < a.n_jobs; ++j) {
-      const JobDesc& job = a.jobs[j];
-      const int n_qt = (job.len + qt_rows - 1) / qt_rows;
-      for (int q = 0; q < n_qt; ++q) {
-        const int v = scratch[t0 + q];
-        scratch[t0 + q] = job.n_split > 1 ? max(1, (v + job.tiles_per_split - 1) / job.tiles_per_split) : 1;
-        total += scratch[t0 + q];
+  } else if (tid < kWave) {
+    // more query tiles than lanes: the same scan over chunks of one wave, the last chunk
+    // first, each adding the suffix at the next chunk's first tile to the tiles whose
+    // job continues there.  Split counts replace the visible counts in scratch; the
+    // suffix sums go to sufs.
+    int* sufs = scratch + n_all + 8;
+    const int t_lane = tid;
+    int carry = 0;
+    for (int c = (n_all - 1) / kWave; c >= 0; --c) {
+      const int t = c * kWave + t_lane;
+      const bool have = t < n_all;
+      const int end = min(n_all, (c + 1) * kWave) - 1;
+      int jt = 0, tb = 0, acc = 0;
+      for (int j = 0; j < a.n_jobs; ++j) {
+        if (t >= acc) {
+          jt = j;
+          tb = acc;
+        }
+        acc += (a.jobs[j].len + qt_rows - 1) / qt_rows;
       }
-      t0 += n_qt;
+      const int jlen = lane_val(ld.jlen, jt), jns = lane_val(ld.jns, jt), jtps = lane_val(ld.jtps, jt);
+      const int te = have ? tb + (jlen + qt_rows - 1) / qt_rows - 1 : t;
+      int ns = 0;
+      if (have) {
+        const int v = scratch[t];
+        ns = jns > 1 ? max(1, (v + jtps - 1) / jtps) : 1;
+      }
+      const int tel = min(te, end);
+      int suf = ns;
+#pragma unroll
+      for (int dl = 1; dl < kWave; dl <<= 1) {
+        const int o = __shfl_down(suf, dl);
+        if (t + dl <= tel) suf += o;
+      }
+      if (have && te > end) suf += carry;
+      if (have) {
+        scratch[t] = ns;
+        sufs[t] = suf;
+      }
+      carry = __builtin_amdgcn_readlane(suf, 0);
     }
-    int rj = -1, rq = 0, rs = 0, rhg = 0, rns = 1;
+    int total = 0;
+    {
+      int tb_j = 0;
+      for (int j = 0; j < a.n_jobs; ++j) {
+        const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
+        if (n_qt > 0) total += sufs[tb_j];
+        tb_j += n_qt;
+      }
+    }
     int i = 0, hg_base = 0, hg_span = 1;
-    bool live = false;
+    bool live;
     if ((n_hg & 7) == 0) {
-      // XCD b % 8 takes head groups [x * hpx, (x + 1) * hpx) of every job
       const int hpx = n_hg >> 3;
       i = b >> 3;
       hg_base = (b & 7) * hpx;
@@ -995,38 +1029,44 @@ __device__ __forceinline__ WorkItem compact_work_item(const FwdArgs& a, const La
       live = (b >> 3) < per && i < T;
       hg_span = n_hg;
     }
+    int rj = -1, rq = 0, rs = 0, rhg = 0, rns = 1;
     if (live) {
-      t0 = 0;
+      int tb_j = 0;
       for (int j = 0; j < a.n_jobs; ++j) {
         const int n_qt = (a.jobs[j].len + qt_rows - 1) / qt_rows;
-        int m = 0;
-        for (int q = 0; q < n_qt; ++q) m += scratch[t0 + q];
+        const int m = n_qt > 0 ? sufs[tb_j] : 0;
         if (i < m * hg_span) {
           const int hl = i / m;
-          int k = i - hl * m;
-          for (int q = n_qt - 1; q >= 0; --q) {  // latest query tile first
-            const int ns = scratch[t0 + q];
-            if (k < ns) {
+          const int k = i - hl * m;
+          for (int c0 = tb_j; c0 < tb_j + n_qt; c0 += kWave) {
+            const int t = c0 + t_lane;
+            const bool in = t < tb_j + n_qt;
+            const int sv = in ? sufs[t] : 0, nv = in ? scratch[t] : 0;
+            const uint64_t hit = __ballot(in && sv - nv <= k && k < sv);
+            if (hit) {
+              const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+              const int sl = __builtin_amdgcn_readlane(sv, L), nl = __builtin_amdgcn_readlane(nv, L);
               rj = j;
-              rq = q;
-              rs = k;
-              rns = ns;
+              rq = c0 + L - tb_j;
+              rs = k - (sl - nl);
+              rns = nl;
               rhg = hg_base + hl;
               break;
             }
-            k -= ns;
           }
           break;
         }
         i -= m * hg_span;
-        t0 += n_qt;
+        tb_j += n_qt;
       }
     }
-    scratch[n_all] = rj;
-    scratch[n_all + 1] = rq;
-    scratch[n_all + 2] = rs;
-    scratch[n_all + 3] = rhg;
-    scratch[n_all + 4] = rns;
+    if (t_lane == 0) {
+      scratch[n_all] = rj;
+      scratch[n_all + 1] = rq;
+      scratch[n_all + 2] = rs;
+      scratch[n_all + 3] = rhg;
+      scratch[n_all + 4] = rns;
+    }
   }
   __syncthreads();
   WorkItem w;

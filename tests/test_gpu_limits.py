@@ -1,7 +1,8 @@
 """Shapes beyond one launch's tables: more than 32 KV segments (streamed in groups of
-32 whose partial states are merged; the backward's passes run per group), and a
-1M-token share of 131072 local rows (cp = 8), the per-rank size of the pages'
-1M-context runs on 8 devices ("推理系统基础设施（二）…", sections 4-5)."""
+32 whose partial states are merged; the backward's passes run per group), a 1M-token
+share of 131072 local rows (cp = 8), the per-rank size of the pages' 1M-context runs
+on 8 devices ("推理系统基础设施（二）…", sections 4-5), and a split launch with more
+query tiles than one wave scans at once."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +105,43 @@ def test_one_million_token_share_of_131072_rows():
     tol = 3 * 2.0 ** -9 * g.double().pow(2).sum(0).sqrt()
     say(f"1M share: sum dV vs sum G max err {float((dv_sum - g_sum).abs().max()):.3e}")
     assert float(((dv_sum - g_sum).abs() - tol).max()) <= 0.0
+
+
+def test_split_numbering_beyond_one_wave():
+    # S = 16384 on one rank (cp = 1), two heads: four-wave work-groups of 128 rows, 128
+    # query tiles whose 256 KV tiles are split (256 query work-groups for 512 slots), so
+    # the dense split numbering scans its counts in two chunks of one wave.  Forward and
+    # dQ on sampled rows against the oracle.
+    seq, cp, hq, d = 16384, 1, 2, 64
+    q = workloads.randn((seq, hq, d), 23, "bf16", 0)
+    k = workloads.randn((seq, hq, d), 23, "bf16", 1)
+    v = workloads.randn((seq, hq, d), 23, "bf16", 2)
+    rs = build_rank_share(q.to(DEV), k.to(DEV), v.to(DEV), cp, 0)
+    ws = rs.stream_workspace("owner")
+    assert ws is not None, "expected a split launch"
+    say("split numbering over 128 query tiles: stream")
+    o, lse = rs.stream_fwd("owner", workspace=ws)
+    g = workloads.randn((seq // cp, hq, d), 23, "bf16", 3).to(DEV)
+    desc = rs.desc()
+    qblk = C.q_block(rs.q, rs.q_idx, rs.q_doc)
+    segs = [s for s, _, _ in rs.segments("owner")]
+    delta = torch.empty((seq // cp, hq), dtype=torch.float32, device=DEV)
+    C.cpattn_bwd_delta(desc, o, g, delta)
+    n_ws = C.cpattn_bwd_dq_workspace_bytes(desc, qblk, segs)
+    assert n_ws > 0, "expected a split dQ pass"
+    dq = torch.empty((seq // cp, hq, d), dtype=torch.float32, device=DEV)
+    say("split numbering over 128 query tiles: dQ")
+    C.cpattn_bwd_dq(desc, qblk, segs, lse, delta, g, dq, torch.empty(n_ws, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    local = rs.q_idx.cpu().numpy().astype(np.int64)
+    pick = np.unique(np.linspace(0, len(local) - 1, 40).astype(np.int64))
+    rows = local[pick]
+    keys = np.arange(seq)
+    o_ref, l_ref = OA.attention_fwd(q[torch.as_tensor(rows)], k, v, rows, keys)
+    sel = torch.as_tensor(pick, device=DEV)
+    assert_close(o[sel], o_ref, TOL_BF16, "128-tile split O")
+    assert_close(lse[sel], l_ref, TOL_LSE_BF16, "128-tile split LSE")
+    # dQ of those rows, with D formed from the bf16 O the GPU saved
+    g_rows = g[sel].cpu()
+    dq_ref, _, _ = OA.attention_bwd(q[torch.as_tensor(rows)], k, v, g_rows, rows, keys, o_saved=o[sel].cpu())
+    assert_close(dq[sel], dq_ref, TOL_BF16, "128-tile split dQ")
