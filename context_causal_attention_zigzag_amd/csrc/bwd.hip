@@ -607,27 +607,6 @@ __device__ __forceinline__ void dkdv_acc_all(const DkdvSmem<D>& sm, int buf, con
   for (int j = 0; j < D / 16; ++j) dkdv_mma<D>(dkdv_ops<D>(sm, buf, j, lane), j, pf, dsf, dk, dv);
 }
 
-// Instruction order of one iteration (scheduling-group masks: 0x008 matrix, 0x100 LDS
-// read, 0x002 vector ALU, 0x400 transcendental): the per-row values and the first
-// operands are read up front; then every contraction carries one or two operand reads
-// (two pairs ahead) and a share of the P / dS arithmetic, which none of them depends
-// on.
-template <int D, bool DOC>
-__device__ __forceinline__ void dkdv_schedule() {
-  constexpr int kMfma = D / 4;                // S, dP, dV, dK contractions
-  constexpr int kReads = D / 8 + 4 * (D / 16);  // row and transposing operand reads
-  constexpr int kSmall = DOC ? 16 : 12;       // per-row value reads
-  constexpr int kLead = 6;
-  constexpr int kPer = (kReads - kLead + kMfma - 1) / kMfma;
-  __builtin_amdgcn_sched_group_barrier(0x100, kSmall + kLead, 0);
-#pragma unroll
-  for (int k = 0; k < kMfma; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
-  }
-}
-
 template <int D, bool DOC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using Sm = DkdvSmem<D>;
@@ -785,6 +764,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // buffer whose results are not used.
     int b0 = 0, bp = 0;
     bf16x8 ppf[2] = {}, pdsf[2] = {};
+    // operands of the first two dV / dK pairs of the coming iteration (its previous tile)
+    TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
     while (true) {
       const int b1 = b0 == kQBufs - 1 ? 0 : b0 + 1;
       const int b2 = b1 == kQBufs - 1 ? 0 : b1 + 1;
@@ -794,8 +775,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       RowVals<DOC> rv;
       load_rows<DOC>(rs, b0, h, rv);
       RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
-      TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
       const QRange q = qrange_lds<DOC>(rs, b0, min(kBQ, a.q_len - cur.qt * kBQ));
+      // dV / dK of tile i-1, pairs 0 and 1: their operands were read in the last
+      // iteration, so these contractions run while the wave waits for the reads above
+      // and issues the fills
+      dkdv_mma<D>(to[0], 0, ppf, pdsf, dk, dv);
+      to[0] = dkdv_ops<D>(sm, bp, 2, lane);
+      dkdv_mma<D>(to[1], 1, ppf, pdsf, dk, dv);
+      to[1] = dkdv_ops<D>(sm, bp, 3, lane);
       __builtin_amdgcn_sched_barrier(0);
       // fill of tile i+3 (its buffers held tile i-2, released at the last barrier)
       const bool issued = nf.hh >= 0;
@@ -822,12 +809,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // S / dP of tile i+1, contraction step k
         sv = mfma32x32x16(ro[k & 1].aq, kf[k], sv);
         dpv = mfma32x32x16(ro[k & 1].ao, vf[k], dpv);
-        // dV / dK of tile i-1, pair k
-        dkdv_mma<D>(to[k & 1], k, ppf, pdsf, dk, dv);
-        if (k + 2 < D / 16) {
-          ro[k & 1] = dkdv_rowops<D>(sm, b1, k + 2, lane);
-          to[k & 1] = dkdv_ops<D>(sm, bp, k + 2, lane);
+        // dV / dK of tile i-1, pair k (pairs 0 and 1 ran in the opening); the last two
+        // stages read the next iteration's first two pairs (tile i is its previous tile)
+        if (k >= 2) {
+          dkdv_mma<D>(to[k & 1], k, ppf, pdsf, dk, dv);
+          to[k & 1] = k + 2 < D / 16 ? dkdv_ops<D>(sm, bp, k + 2, lane) : dkdv_ops<D>(sm, b0, k + 2 - D / 16, lane);
         }
+        if (k + 2 < D / 16) ro[k & 1] = dkdv_rowops<D>(sm, b1, k + 2, lane);
         // P / dS of tile i, a quarter per (D / 64) stages
         if ((k + 1) * 4 % (D / 16) == 0)
           dkdv_pds<D, DOC>(rv, scur, dpcur, (k + 1) * 4 / (D / 16) - 1, kpos_eff, kdoc, a.scale_log2, pf, dsf);
