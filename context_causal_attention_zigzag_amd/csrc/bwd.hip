@@ -764,8 +764,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // buffer whose results are not used.
     int b0 = 0, bp = 0;
     bf16x8 ppf[2] = {}, pdsf[2] = {};
-    // operands of the first two dV / dK pairs of the coming iteration (its previous tile)
-    TrOps to[2] = {dkdv_ops<D>(sm, bp, 0, lane), dkdv_ops<D>(sm, bp, 1, lane)};
+    // operands of the first kNP dV / dK pairs of the coming iteration (its previous
+    // tile); three at d = 128 (two and four measured slower), two at d = 64
+    constexpr int kPairs = D / 16, kNP = kPairs >= 8 ? 3 : 2;
+    TrOps to[kNP];
+#pragma unroll
+    for (int j = 0; j < kNP; ++j) to[j] = dkdv_ops<D>(sm, bp, j, lane);
     while (true) {
       const int b1 = b0 == kQBufs - 1 ? 0 : b0 + 1;
       const int b2 = b1 == kQBufs - 1 ? 0 : b1 + 1;
@@ -776,13 +780,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       load_rows<DOC>(rs, b0, h, rv);
       RowOps ro[2] = {dkdv_rowops<D>(sm, b1, 0, lane), dkdv_rowops<D>(sm, b1, 1, lane)};
       const QRange q = qrange_lds<DOC>(rs, b0, min(kBQ, a.q_len - cur.qt * kBQ));
-      // dV / dK of tile i-1, pairs 0 and 1: their operands were read in the last
+      // dV / dK of tile i-1, pairs 0 .. kNP-1: their operands were read in the last
       // iteration, so these contractions run while the wave waits for the reads above
       // and issues the fills
-      dkdv_mma<D>(to[0], 0, ppf, pdsf, dk, dv);
-      to[0] = dkdv_ops<D>(sm, bp, 2, lane);
-      dkdv_mma<D>(to[1], 1, ppf, pdsf, dk, dv);
-      to[1] = dkdv_ops<D>(sm, bp, 3, lane);
+#pragma unroll
+      for (int j = 0; j < kNP; ++j) {
+        dkdv_mma<D>(to[j], j, ppf, pdsf, dk, dv);
+        to[j] = j + kNP < kPairs ? dkdv_ops<D>(sm, bp, j + kNP, lane) : dkdv_ops<D>(sm, b0, j, lane);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // fill of tile i+3 (its buffers held tile i-2, released at the last barrier)
       const bool issued = nf.hh >= 0;
@@ -809,11 +814,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // S / dP of tile i+1, contraction step k
         sv = mfma32x32x16(ro[k & 1].aq, kf[k], sv);
         dpv = mfma32x32x16(ro[k & 1].ao, vf[k], dpv);
-        // dV / dK of tile i-1, pair k (pairs 0 and 1 ran in the opening); the last two
-        // stages read the next iteration's first two pairs (tile i is its previous tile)
-        if (k >= 2) {
-          dkdv_mma<D>(to[k & 1], k, ppf, pdsf, dk, dv);
-          to[k & 1] = k + 2 < D / 16 ? dkdv_ops<D>(sm, bp, k + 2, lane) : dkdv_ops<D>(sm, b0, k + 2 - D / 16, lane);
+        // dV / dK of tile i-1, pair k (pairs 0 .. kNP-1 ran in the opening); the last
+        // stages read the next iteration's first pairs (tile i is its previous tile)
+        if (k >= kNP) {
+          dkdv_mma<D>(to[k % kNP], k, ppf, pdsf, dk, dv);
+          // slot k % kNP holds pair k + kNP of this tile, or, once those are done, the
+          // next iteration's pair k % kNP (slot j serves pair j in the opening)
+          to[k % kNP] = k + kNP < kPairs ? dkdv_ops<D>(sm, bp, k + kNP, lane)
+                                          : dkdv_ops<D>(sm, b0, k % kNP, lane);
         }
         if (k + 2 < D / 16) ro[k & 1] = dkdv_rowops<D>(sm, b1, k + 2, lane);
         // P / dS of tile i, a quarter per (D / 64) stages
