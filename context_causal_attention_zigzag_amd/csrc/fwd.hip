@@ -558,18 +558,7 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
     for (int j = 0; j < a.n_jobs; ++j) n += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw);
     return n;
   };
-  if (waves == 0) {
-    waves = query_wgs(8) >= num_cu ? 8 : 4;
-    // A launch that will split its KV tiles fills the CUs at either size, and with
-    // eight-wave work-groups every K/V tile fill serves twice the query rows.  Launches
-    // without splits keep four-wave work-groups, two to a CU.
-    if (waves == 4 && allow_split && dtype == 0)
-      for (int j = 0; j < a.n_jobs; ++j)
-        if (a.jobs[j].n_tiles > 2 * kMinTilesPerSplit && a.jobs[j].n_tiles <= kMaxSplitTiles) {
-          waves = 8;
-          break;
-        }
-  }
+  if (waves == 0) waves = query_wgs(8) >= num_cu ? 8 : 4;
   a.wg_waves = waves;
   a.plan_tiles = 0;
   a.plan = nullptr;
