@@ -259,8 +259,14 @@ def main():
     # the headline: whole steps, events only at the ends of the loop and around the
     # dominant kernel's call (the longest call that is one launch)
     split_t, split_s, split_q = info["split_t"], info["split_s"], info["split_q"]
-    n_chunks = len(info["rs"].q_chunks())
-    launches = {"partition": 1, "tile_fwd": 1 + split_t, "merge": n_chunks, "stream_fwd": 1 + split_s,
+    # the query chunks' merges run as one grouped call: one launch per 8 chunks or 64 parts
+    merge_launches, ng, np_ = 0, 0, 0
+    for (a_, b_) in info["rs"].q_chunks():
+        n = sum(1 for e in info["edges"] if e[0] == (a_, b_))
+        if ng == 0 or ng == 8 or np_ + n > 64:
+            merge_launches, ng, np_ = merge_launches + 1, 0, 0
+        ng, np_ = ng + 1, np_ + n
+    launches = {"partition": 1, "tile_fwd": 1 + split_t, "merge": merge_launches, "stream_fwd": 1 + split_s,
                 "bwd_delta": 1, "bwd_dq": 1 + split_q, "bwd_dkdv": 1}
     single = [n for n in names if launches[n] == 1]
     dom = max(single, key=lambda n: ms[n])
@@ -329,7 +335,7 @@ def main():
     delta_bytes = n_local * w.hq * (2 * w.d * elt + 4)
     # call -> (kernel launches, bound, algorithmic work); the forward calls add a merge
     # launch when their plan splits the KV tiles, the dQ call a sum launch, and the merge
-    # call is one launch per query chunk
+    # call is one grouped launch for the query chunks
     calls = {
         "partition": (launches["partition"], "hbm", part_bytes),
         "tile_fwd": (launches["tile_fwd"], "mfma", f_fwd),

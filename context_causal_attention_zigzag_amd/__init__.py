@@ -75,6 +75,9 @@ lib.cpattn_tile_fwd_workspace_bytes.restype = _c_sz
 lib.cpattn_merge.argtypes = [_c_i32, _P(_c_vp), _P(_c_vp), _c_i64, _c_i32, _c_i32, _c_i32, _c_vp,
                              _c_vp, _c_vp]
 lib.cpattn_merge.restype = _c_i32
+lib.cpattn_merge_groups.argtypes = [_c_i32, _P(_c_i32), _P(_c_vp), _P(_c_vp), _P(_c_i64), _c_i32, _c_i32, _c_i32,
+                                    _P(_c_vp), _P(_c_vp), _c_vp]
+lib.cpattn_merge_groups.restype = _c_i32
 lib.cpattn_stream_fwd.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
                                   _P(cpattn_kv_seg), _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
 lib.cpattn_stream_fwd.restype = _c_i32
@@ -105,7 +108,7 @@ lib.cpattn_bwd_noalloc.restype = _c_i32
 
 EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_partition_rope",
             "cpattn_zigzag_edge_visible", "cpattn_tile_fwd",
-            "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_stream_fwd",
+            "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_merge_groups", "cpattn_stream_fwd",
             "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
             "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
             "cpattn_bwd_noalloc")
@@ -270,6 +273,25 @@ def cpattn_merge(o_parts, lse_parts, o_out, lse_out, stream=None):
                           _vp_array([_ptr(x) for x in lse_parts]), rows, hq, d, out_dtype,
                           _ptr(o_out), _ptr(lse_out), _stream(stream))
     _check(st, "cpattn_merge")
+
+
+def cpattn_merge_groups(groups, stream=None):
+    """Several log-sum-exp merges in one launch: ``groups`` is a list of
+    (o_parts, lse_parts, o_out, lse_out), each as for cpattn_merge; all outputs share
+    one dtype, head count and head dim."""
+    n = len(groups)
+    if n == 0:
+        return
+    _, hq, d = groups[0][2].shape
+    out_dtype = _DT[groups[0][2].dtype]
+    n_parts = (_c_i32 * n)(*[len(g[0]) for g in groups])
+    rows = (_c_i64 * n)(*[g[2].shape[0] for g in groups])
+    o_parts = _vp_array([_ptr(o) for g in groups for o in g[0]])
+    lse_parts = _vp_array([_ptr(x) for g in groups for x in g[1]])
+    st = lib.cpattn_merge_groups(n, n_parts, o_parts, lse_parts, rows, hq, d, out_dtype,
+                                 _vp_array([_ptr(g[2]) for g in groups]), _vp_array([_ptr(g[3]) for g in groups]),
+                                 _stream(stream))
+    _check(st, "cpattn_merge_groups")
 
 
 def cpattn_stream_fwd_workspace_bytes(desc: cpattn_attn_desc, q: cpattn_q_block, segs) -> int:

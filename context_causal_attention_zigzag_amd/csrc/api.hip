@@ -340,6 +340,32 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
+int cpattn_merge_groups(int32_t n_groups, const int32_t* n_parts, const float* const* o_parts,
+                        const float* const* lse_parts, const int64_t* rows, int32_t hq, int32_t d,
+                        int32_t out_dtype, void* const* o_out, float* const* lse_out, void* stream) {
+  if (n_groups < 0 || hq < 1) return CPATTN_ERR_ARG;
+  if (d < 4 || d > 256 || d % 4 != 0) return CPATTN_ERR_UNSUPPORTED;
+  if (out_dtype != CPATTN_BF16 && out_dtype != CPATTN_F32) return CPATTN_ERR_UNSUPPORTED;
+  if (n_groups == 0) return CPATTN_OK;
+  if (n_parts == nullptr || rows == nullptr || o_out == nullptr || lse_out == nullptr) return CPATTN_ERR_ARG;
+  for (int g = 0; g < n_groups; ++g)
+    if (n_parts[g] < 1 || n_parts[g] > 64 || rows[g] < 0 || rows[g] > kMaxRows) return CPATTN_ERR_ARG;
+  if (o_parts == nullptr || lse_parts == nullptr) return CPATTN_ERR_ARG;
+  // the buffers of groups with rows are checked (a group of 0 rows reads none of them)
+  int64_t j0 = 0;
+  for (int g = 0; g < n_groups; j0 += n_parts[g], ++g) {
+    if (rows[g] == 0) continue;
+    for (int64_t j = j0; j < j0 + n_parts[g]; ++j) {
+      if (o_parts[j] == nullptr || lse_parts[j] == nullptr) return CPATTN_ERR_ARG;
+      if (!aligned16(o_parts[j])) return CPATTN_ERR_ALIGN;
+    }
+    if (o_out[g] == nullptr || lse_out[g] == nullptr) return CPATTN_ERR_ARG;
+    if (!aligned16(o_out[g])) return CPATTN_ERR_ALIGN;
+  }
+  return hip_status(launch_merge_groups(n_groups, n_parts, o_parts, lse_parts, rows, hq, d, out_dtype, o_out,
+                                        lse_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q,
                                          int32_t n_segs, const cpattn_kv_seg* segs) {
   if (check_desc(desc) != CPATTN_OK || check_qblock(desc, q) != CPATTN_OK) return 0;

@@ -312,6 +312,11 @@ void assign_fwd_workspace(FwdArgs& a, int d, void* ws);
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
                         hipStream_t stream);
+// Several independent merges (group g: n_parts[g] consecutive parts over rows[g] rows
+// into o_out[g], lse_out[g]) in as few launches as the argument block allows.
+hipError_t launch_merge_groups(int n_groups, const int32_t* n_parts, const float* const* o_parts,
+                               const float* const* lse_parts, const int64_t* rows, int hq, int d, int out_dtype,
+                               void* const* o_out, float* const* lse_out, hipStream_t stream);
 // Backward passes: delta = rowsum(dO * O) over `pairs` (row, head) pairs; dQ
 // (query-major, `dq` holds its job, split plan and partial buffers); dK/dV (key-major).
 hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t pairs, int d,

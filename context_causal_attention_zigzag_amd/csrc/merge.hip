@@ -16,15 +16,21 @@ namespace cpattn {
 namespace {
 
 constexpr int kMaxParts = 64;
+constexpr int kMaxGroups = 8;
 constexpr int kThreads = 256;
 
+// One launch merges up to kMaxGroups groups of rows, each from its own parts (a run of
+// the part arrays) into its own output; every block belongs to one group.
 struct MergeArgs {
   const float* o[kMaxParts];
   const float* lse[kMaxParts];
-  void* o_out;
-  float* lse_out;
-  int64_t pairs;  // rows * hq
-  int32_t n;
+  void* o_out[kMaxGroups];
+  float* lse_out[kMaxGroups];
+  int64_t pairs[kMaxGroups];            // rows * hq of each group
+  int32_t block_begin[kMaxGroups + 1];  // first block of each group; the last entry ends the grid
+  int32_t part_begin[kMaxGroups];
+  int32_t n[kMaxGroups];
+  int32_t n_groups;
   int32_t d;
 };
 
@@ -113,18 +119,22 @@ __device__ __forceinline__ void store_slice(void* o, int64_t off, f32x4 v) {
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  // this block's group (uniform: a scalar walk over at most kMaxGroups entries)
+  int g = 0;
+  while (g + 1 < a.n_groups && a.block_begin[g + 1] <= (int)blockIdx.x) ++g;
   const int tpp = a.d >> 2;  // threads per (row, head) pair
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t gid = (int64_t)(blockIdx.x - a.block_begin[g]) * kThreads + threadIdx.x;
   const int64_t pair = gid / tpp;
   const int c = (int)(gid - pair * tpp);
-  if (pair >= a.pairs) return;
+  if (pair >= a.pairs[g]) return;
   const int64_t off = pair * a.d + 4 * c;
+  const int p0 = a.part_begin[g];
   float lse;
   const f32x4 v = merge_slice<false, 4, false>(
-      a.n, [&](int j) { return a.lse[j][pair]; },
-      [&](int j) { return *reinterpret_cast<const f32x4*>(a.o[j] + off); }, lse);
-  store_slice<OUT_BF16>(a.o_out, off, v);
-  if (c == 0) a.lse_out[pair] = lse;
+      a.n[g], [&](int j) { return a.lse[p0 + j][pair]; },
+      [&](int j) { return *reinterpret_cast<const f32x4*>(a.o[p0 + j] + off); }, lse);
+  store_slice<OUT_BF16>(a.o_out[g], off, v);
+  if (c == 0) a.lse_out[g][pair] = lse;
 }
 
 // Merge of the KV-split partial states of several forward jobs in one launch: job j
@@ -200,27 +210,54 @@ hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipSt
   return hipGetLastError();
 }
 
+hipError_t launch_merge_groups(int n_groups, const int32_t* n_parts, const float* const* o_parts,
+                               const float* const* lse_parts, const int64_t* rows, int hq, int d, int out_dtype,
+                               void* const* o_out, float* const* lse_out, hipStream_t stream) {
+  // groups go into launches in order, at most kMaxGroups groups and kMaxParts parts each
+  int g0 = 0, p0 = 0;
+  while (g0 < n_groups) {
+    MergeArgs a{};
+    int ng = 0, np = 0, blocks = 0;
+    while (g0 + ng < n_groups && ng < kMaxGroups && np + n_parts[g0 + ng] <= kMaxParts) {
+      const int g = g0 + ng;
+      for (int j = 0; j < n_parts[g]; ++j) {
+        a.o[np + j] = o_parts[p0 + np + j];
+        a.lse[np + j] = lse_parts[p0 + np + j];
+      }
+      a.o_out[ng] = o_out[g];
+      a.lse_out[ng] = lse_out[g];
+      a.pairs[ng] = rows[g] * hq;
+      a.part_begin[ng] = np;
+      a.n[ng] = n_parts[g];
+      a.block_begin[ng] = blocks;
+      blocks += (int)((a.pairs[ng] * (d / 4) + kThreads - 1) / kThreads);
+      np += n_parts[g];
+      ++ng;
+    }
+    a.block_begin[ng] = blocks;
+    a.n_groups = ng;
+    a.d = d;
+    if (blocks > 0) {
+      if (out_dtype == 0)
+        hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    g0 += ng;
+    p0 += np;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                         int64_t rows, int hq, int d, int out_dtype, void* o_out, float* lse_out,
                         hipStream_t stream) {
-  MergeArgs a{};
-  for (int j = 0; j < n_parts; ++j) {
-    a.o[j] = o_parts[j];
-    a.lse[j] = lse_parts[j];
-  }
-  a.o_out = o_out;
-  a.lse_out = lse_out;
-  a.pairs = rows * hq;
-  a.n = n_parts;
-  a.d = d;
-  const int64_t threads = a.pairs * (d / 4);
-  if (threads == 0) return hipSuccess;
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  if (out_dtype == 0)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  const int32_t np = n_parts;
+  void* oo = o_out;
+  float* lo = lse_out;
+  return launch_merge_groups(1, &np, o_parts, lse_parts, &rows, hq, d, out_dtype, &oo, &lo, stream);
 }
 
 }  // namespace cpattn

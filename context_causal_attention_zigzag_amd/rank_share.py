@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 import torch
 
 from . import (PART_STRIPED, PART_THD, PART_ZIGZAG, MASK_CAUSAL, MASK_CAUSAL_DOC, attn_desc, cpattn_bwd,
-               cpattn_bwd_workspace_bytes, cpattn_merge, cpattn_partition, cpattn_stream_fwd,
+               cpattn_bwd_workspace_bytes, cpattn_merge_groups, cpattn_partition, cpattn_stream_fwd,
                cpattn_stream_fwd_workspace_bytes, cpattn_tile_fwd, cpattn_tile_fwd_workspace_bytes,
                cpattn_zigzag_edge_visible, kv_seg, q_block)
 
@@ -142,11 +142,14 @@ class RankShare:
         n = self.q.shape[0]
         o = torch.empty_like(self.q) if o is None else o
         lse = torch.empty((n, self.hq), dtype=torch.float32, device=self.q.device) if lse is None else lse
+        groups = []
         for (a, b) in self.q_chunks():
             mine = [p for e, p in zip(edges, parts) if e[0] == (a, b)]
             if not mine:  # every query chunk sees at least its own diagonal block
                 raise ValueError("query chunk without any edge")
-            cpattn_merge([p[0] for p in mine], [p[1] for p in mine], o[a:b], lse[a:b])
+            groups.append(([p[0] for p in mine], [p[1] for p in mine], o[a:b], lse[a:b]))
+        # every query chunk's merge in one launch
+        cpattn_merge_groups(groups)
         return o, lse
 
     def alloc_bwd_buffers(self, granularity="owner"):

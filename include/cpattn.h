@@ -264,6 +264,28 @@ int cpattn_merge(int32_t n_parts, const float* const* o_parts, const float* cons
                  float* lse_out, void* stream);
 
 /*
+ * cpattn_merge_groups — several independent cpattn_merge calls in one launch (or as
+ * few as the launch arguments allow), for example the merges of all query chunks of a
+ * rank after a batch of tile edges.  Same source and arithmetic as cpattn_merge: each
+ * group's result is bit-identical to cpattn_merge on that group alone.
+ *
+ *  n_groups         number of groups (0 is a no-op).
+ *  n_parts          host array [n_groups], each 1..64.
+ *  o_parts          host array [sum of n_parts] of device fp32 [rows[g], hq, d]: group
+ *                   g's parts follow those of groups 0 .. g-1.
+ *  lse_parts        host array [sum of n_parts] of device fp32 [rows[g], hq], same order.
+ *  rows             host array [n_groups] (a group with 0 rows is skipped; its buffers
+ *                   are not read and may be NULL).
+ *  out_dtype        CPATTN_BF16 or CPATTN_F32 for every o_out[g].
+ *  o_out, lse_out   host arrays [n_groups] of device [rows[g], hq, d] and fp32
+ *                   [rows[g], hq] outputs.
+ * Errors: ARG, ALIGN (16-byte aligned O buffers), UNSUPPORTED (as cpattn_merge), HIP.
+ */
+int cpattn_merge_groups(int32_t n_groups, const int32_t* n_parts, const float* const* o_parts,
+                        const float* const* lse_parts, const int64_t* rows, int32_t hq, int32_t d,
+                        int32_t out_dtype, void* const* o_out, float* const* lse_out, void* stream);
+
+/*
  * cpattn_stream_fwd — the streaming online-softmax form over KV segments in
  * arrival order (the ring loop of one rank, with the other ranks' segments given
  * as local buffers).

@@ -111,6 +111,21 @@ int main() {
   EXPECT(cpattn_merge(65, cparts, cparts, 16, 8, 128, CPATTN_BF16, F, static_cast<float*>(F), nullptr), CPATTN_ERR_ARG);
   EXPECT(cpattn_merge(4, cparts, cparts, 16, 8, 130, CPATTN_BF16, F, static_cast<float*>(F), nullptr),
          CPATTN_ERR_UNSUPPORTED);
+  {
+    // grouped merges: 12 groups of 6 parts (more than one launch's worth of groups and parts)
+    std::vector<const float*> gp(72, static_cast<const float*>(F));
+    std::vector<int32_t> gparts(12, 6);
+    std::vector<int64_t> grows(12, 16);
+    std::vector<void*> gout(12, F);
+    std::vector<float*> glse(12, static_cast<float*>(F));
+    EXPECT_ANY(cpattn_merge_groups(12, gparts.data(), gp.data(), gp.data(), grows.data(), 8, 128, CPATTN_BF16,
+                                   gout.data(), glse.data(), nullptr),
+               CPATTN_ERR_HIP, CPATTN_OK);
+    gparts[5] = 0;
+    EXPECT(cpattn_merge_groups(12, gparts.data(), gp.data(), gp.data(), grows.data(), 8, 128, CPATTN_BF16,
+                               gout.data(), glse.data(), nullptr),
+           CPATTN_ERR_ARG);
+  }
 
   // backward
   float* Ff = static_cast<float*>(F);

@@ -123,6 +123,31 @@ def test_tile_and_merge_validation():
     assert C.lib.cpattn_merge(1, p, p, 0, 8, 128, C.BF16, FAKE, FAKE, None) == C.OK   # no-op
 
 
+def test_merge_groups_validation():
+    def call(n_groups, n_parts, rows, d=128, dtype=C.BF16, parts=None, outs=None, hq=8):
+        np_ = (ctypes.c_int32 * max(1, len(n_parts)))(*n_parts)
+        rw = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        total = sum(max(0, x) for x in n_parts)
+        pp = parts if parts is not None else (ctypes.c_void_p * max(1, total))(*([FAKE] * max(1, total)))
+        oo = outs if outs is not None else (ctypes.c_void_p * max(1, len(rows)))(*([FAKE] * max(1, len(rows))))
+        return C.lib.cpattn_merge_groups(n_groups, np_, pp, pp, rw, hq, d, dtype, oo, oo, None)
+    assert call(-1, [], []) == C.ERR_ARG
+    assert call(0, [], []) == C.OK                                   # no-op
+    assert call(2, [1, 2], [10, 10], hq=0) == C.ERR_ARG
+    assert call(2, [1, 2], [10, 10], d=6) == C.ERR_UNSUPPORTED
+    assert call(2, [1, 2], [10, 10], dtype=9) == C.ERR_UNSUPPORTED
+    assert call(2, [1, 0], [10, 10]) == C.ERR_ARG                    # a group without parts
+    assert call(2, [1, 65], [10, 10]) == C.ERR_ARG
+    assert call(2, [1, 2], [10, -1]) == C.ERR_ARG
+    nul = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert call(2, [1, 2], [10, 10], parts=nul) == C.ERR_ARG         # a null part
+    mis = (ctypes.c_void_p * 3)(FAKE, FAKE + 8, FAKE)
+    assert call(2, [1, 2], [10, 10], parts=mis) == C.ERR_ALIGN       # a misaligned part
+    out_nul = (ctypes.c_void_p * 2)(FAKE, None)
+    assert call(2, [1, 2], [10, 10], outs=out_nul) == C.ERR_ARG      # a null output
+    assert call(2, [1, 2], [0, 0], outs=out_nul) == C.OK             # groups of 0 rows: outputs not read
+
+
 def test_forward_workspace_plan():
     # a small share (2048 rows x 8 heads, 4 segments of 2048 keys) cannot fill 256 CUs
     # with query tiles alone: a split is planned; a large one (64 query tiles x 64 heads) not

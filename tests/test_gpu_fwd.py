@@ -230,6 +230,43 @@ def test_many_segments_and_edges():
     assert_close(l2, l_ref, TOL_LSE_BF16, "30-edge LSE")
 
 
+def test_merge_groups_match_single_merges():
+    # groups of different row counts and part counts, one empty; 11 groups of up to 7 parts
+    # take more than one launch (8 groups / 64 parts per launch).  Each group's result must
+    # be bit-identical to cpattn_merge on that group alone, and match the oracle's merge.
+    rng = np.random.default_rng(9)
+    hq, d = 3, 128
+    shapes = [(77, 5), (0, 2), (33, 1), (64, 7), (5, 3), (40, 6), (1, 1), (90, 7), (12, 4), (50, 7), (7, 2)]
+    for dt in (torch.float32, torch.bfloat16):
+        say(f"merge groups {dt}")
+        groups, single, refs = [], [], []
+        for rows, n in shapes:
+            os_ = [rng.standard_normal((rows, hq, d)).astype(np.float32) for _ in range(n)]
+            ls_ = [(rng.standard_normal((rows, hq)) * 4).astype(np.float32) for _ in range(n)]
+            if rows > 3:
+                ls_[0][2, :] = -np.inf
+                for j in range(n):
+                    ls_[j][3, 1] = -np.inf    # a row empty in every part
+            op = [torch.from_numpy(x).to(DEV) for x in os_]
+            lp = [torch.from_numpy(x).to(DEV) for x in ls_]
+            o = torch.empty((rows, hq, d), dtype=dt, device=DEV)
+            lse = torch.empty((rows, hq), dtype=torch.float32, device=DEV)
+            groups.append((op, lp, o, lse))
+            o1, l1 = torch.empty_like(o), torch.empty_like(lse)
+            if rows:
+                C.cpattn_merge(op, lp, o1, l1)
+            single.append((o1, l1))
+            refs.append(OA.merge(list(zip(os_, ls_))) if rows else None)
+        C.cpattn_merge_groups(groups)
+        torch.cuda.synchronize()
+        for (op, lp, o, lse), (o1, l1), ref in zip(groups, single, refs):
+            if ref is None:
+                continue
+            assert torch.equal(o, o1) and torch.equal(lse, l1)
+            assert_close(o, ref[0], 1e-5 if dt == torch.float32 else TOL_BF16, f"grouped merge O {dt}")
+            assert_close(lse, ref[1], 1e-5, f"grouped merge LSE {dt}")
+
+
 def test_merge_kernel_against_oracle_merge():
     rng = np.random.default_rng(5)
     n, rows, hq, d = 5, 77, 3, 128
