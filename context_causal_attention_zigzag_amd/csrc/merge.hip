@@ -144,7 +144,8 @@ struct MergeJobsArgs {
   const float* ws_lse[kMaxJobs];
   void* o[kMaxJobs];
   float* lse[kMaxJobs];
-  int64_t pair_begin[kMaxJobs + 1];  // prefix of len*hq over the jobs
+  int64_t pairs[kMaxJobs];             // len * hq of each job
+  int32_t block_begin[kMaxJobs + 1];   // first block of each job (every block in one job)
   int32_t n[kMaxJobs];
   int32_t n_jobs;
   int32_t d;
@@ -154,15 +155,15 @@ struct MergeJobsArgs {
 // gradient partials; otherwise the log-sum-exp merge.
 template <bool OUT_BF16, bool SUM>
 __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
-  const int tpp = a.d >> 2;
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t gpair = gid / tpp;
-  const int c = (int)(gid - gpair * tpp);
-  if (gpair >= a.pair_begin[a.n_jobs]) return;
+  // this block's job (uniform: a scalar walk), so the job's pointers are scalar loads
   int j = 0;
-  while (j + 1 < a.n_jobs && a.pair_begin[j + 1] <= gpair) ++j;
-  const int64_t pair = gpair - a.pair_begin[j];
-  const int64_t stride = a.pair_begin[j + 1] - a.pair_begin[j];  // len * hq
+  while (j + 1 < a.n_jobs && a.block_begin[j + 1] <= (int)blockIdx.x) ++j;
+  const int tpp = a.d >> 2;
+  const int64_t gid = (int64_t)(blockIdx.x - a.block_begin[j]) * kThreads + threadIdx.x;
+  const int64_t pair = gid / tpp;
+  const int c = (int)(gid - pair * tpp);
+  const int64_t stride = a.pairs[j];  // len * hq
+  if (pair >= stride) return;
   const int n = a.n[j];
   const float* lp = a.ws_lse[j] + pair;
   const float* op = a.ws_o[j] + pair * a.d + 4 * c;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void merge_jobs_kernel(MergeJobsArgs a) {
 
 hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream, bool sum) {
   MergeJobsArgs a{};
-  int64_t pairs = 0;
+  int64_t blocks = 0;
   for (int j = 0; j < f.n_jobs; ++j) {
     const JobDesc& jb = f.jobs[j];
     if (jb.n_split <= 1) continue;
@@ -194,13 +195,13 @@ hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipSt
     a.o[k] = jb.o;
     a.lse[k] = jb.lse;
     a.n[k] = jb.n_split;
-    a.pair_begin[k] = pairs;
-    pairs += (int64_t)jb.len * f.hq;
+    a.pairs[k] = (int64_t)jb.len * f.hq;
+    a.block_begin[k] = (int32_t)blocks;
+    blocks += (a.pairs[k] * (d / 4) + kThreads - 1) / kThreads;
   }
-  a.pair_begin[a.n_jobs] = pairs;
+  a.block_begin[a.n_jobs] = (int32_t)blocks;
   a.d = d;
-  if (pairs == 0) return hipSuccess;
-  const int64_t blocks = (pairs * (d / 4) + kThreads - 1) / kThreads;
+  if (blocks == 0) return hipSuccess;
   if (sum)
     hipLaunchKernelGGL((merge_jobs_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else if (out_dtype == 0)
