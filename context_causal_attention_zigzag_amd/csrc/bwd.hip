@@ -269,8 +269,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
 
   using Sm = DqSmem<D>;
   const uint32_t rstride = (uint32_t)a.hkv * D;  // elements between consecutive keys
-  FillOffs<D, Sm, NW> fo;
-  fo.init(wave, lane);
+  FillOffs<D, Sm, NW, true> fo;
+  fo.init(wave, lane, rstride);
   const bool doc = mask == kMaskCausalDoc;
   TileRef cur = iter_next(it, job, TileRef{-1, 0});
   if (cur.seg >= 0) {

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * kWave, wg_per_cu(NW)) void fwd_bf16_kernel(Fwd
 
   const uint32_t rs = (uint32_t)a.hkv * D;  // elements between consecutive keys
   FillOffs<D, Sm, NW> fo;
-  fo.init(wave, lane);
+  fo.init(wave, lane, rs);
   TileRef cur = iter_next(it, job, TileRef{-1, 0});
   if (cur.seg >= 0) {
     KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);

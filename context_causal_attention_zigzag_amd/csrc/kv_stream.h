@@ -347,11 +347,19 @@ __device__ __forceinline__ void mask_half(f32x16& x, const int32_t* kp, const in
 // The image is a sequence of 16-byte slots (row-major, kKS / 8 or kVS / 8 slots per
 // key row, the last ones padding); fill instruction jj of the work-group writes slots
 // 64 jj .. 64 jj + 63, lane l slot 64 jj + l.  Per fill instruction each lane's source
-// is a fixed element offset (key row * row stride + column; padding slots load a valid
-// dummy chunk), clamped to last * stride + D - 8: rows up to the tile's last key stay
-// exact, rows after it (ragged tile) read the last chunk of key `last` (finite data;
-// those keys are masked).
-template <int D, class Smem, int kWaves = 4>
+// is a fixed offset from the tile's first key (key row * row stride + column; padding
+// slots load a valid dummy chunk), clamped to that of key `last`'s last chunk: rows up
+// to the tile's last key stay exact, rows after it (ragged tile) read the last chunk
+// of key `last` (finite data; those keys are masked).
+//
+// Two forms of the per-lane offsets.  Full (kCompact false): the byte offsets, one
+// register per fill instruction of the wave, computed once and hidden from the
+// compiler, which otherwise recomputes their divisions at every tile to save the
+// registers (about a dozen vector instructions per fill, in the forward kernel).
+// Compact: 16-bit (row, column) entries, two per register, the offset formed at fill
+// time -- for the dQ kernel, which holds them without recomputing and has no registers
+// to spare (the full form made its 8K pass 3-5% slower).
+template <int D, class Smem, int kWaves = 4, bool kCompact = false>
 struct FillOffs {
   static constexpr int kKSlots = Smem::kKS / 8;
   static constexpr int kVSlots = Smem::kVS / 8;
@@ -361,45 +369,101 @@ struct FillOffs {
   static constexpr int kVPer = (kVInst + kWaves - 1) / kWaves;
   static_assert(kBK * kKSlots % kWave == 0 && kBK * kVSlots % kWave == 0, "whole instructions");
   static_assert(D <= 256, "column offsets fit a byte");
-  // per fill instruction, 16 bits: key row (bits 8..13) and element column (bits 0..7);
-  // two per register (the offset is formed at fill time: row * stride + column)
-  uint32_t kp[(kKPer + 1) / 2], vp[(kVPer + 1) / 2];
+  static constexpr int kKReg = kCompact ? (kKPer + 1) / 2 : kKPer;
+  static constexpr int kVReg = kCompact ? (kVPer + 1) / 2 : kVPer;
+  uint32_t ko[kKReg], vo[kVReg];
 
+  // (row, column) of a slot: row in bits 8..13, element column in bits 0..7
   static __device__ __forceinline__ uint32_t entry(int slot, int slots) {
     const int c = slot % slots;
     return (uint32_t)min(slot / slots, kBK - 1) << 8 | (uint32_t)(c < D / 8 ? c * 8 : 0);
   }
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // element offset of an entry, rs: elements between consecutive keys
+  static __device__ __forceinline__ uint32_t elems(uint32_t e, uint32_t rs) { return __umul24(e >> 8, rs) + (e & 0xffu); }
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t rs) {
+    if (kCompact) {
 #pragma unroll
-    for (int j = 0; j < (kKPer + 1) / 2; ++j) kp[j] = 0;
+      for (int j = 0; j < kKReg; ++j) ko[j] = 0;
 #pragma unroll
-    for (int j = 0; j < (kVPer + 1) / 2; ++j) vp[j] = 0;
+      for (int j = 0; j < kVReg; ++j) vo[j] = 0;
 #pragma unroll
-    for (int j = 0; j < kKPer; ++j) kp[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kKSlots) << (16 * (j & 1));
+      for (int j = 0; j < kKPer; ++j) ko[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kKSlots) << (16 * (j & 1));
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) vp[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kVSlots) << (16 * (j & 1));
+      for (int j = 0; j < kVPer; ++j) vo[j >> 1] |= entry(kWave * (wave + kWaves * j) + lane, kVSlots) << (16 * (j & 1));
+    } else {
+#pragma unroll
+      for (int j = 0; j < kKReg; ++j) {
+        ko[j] = elems(entry(kWave * (wave + kWaves * j) + lane, kKSlots), rs) * 2;
+        asm volatile("" : "+v"(ko[j]));
+      }
+#pragma unroll
+      for (int j = 0; j < kVReg; ++j) {
+        vo[j] = elems(entry(kWave * (wave + kWaves * j) + lane, kVSlots), rs) * 2;
+        asm volatile("" : "+v"(vo[j]));
+      }
+    }
   }
-  static __device__ __forceinline__ uint32_t offset(const uint32_t* packed, int j, uint32_t rs) {
-    const uint32_t e = (packed[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-    return __umul24(e >> 8, rs) + (e & 0xffu);
+  // offset of fill j of the K (or V) image: elements (compact), bytes (full)
+  __device__ __forceinline__ uint32_t koff(int j, uint32_t rs) const {
+    return kCompact ? elems((ko[j >> 1] >> (16 * (j & 1))) & 0xffffu, rs) : ko[j];
+  }
+  __device__ __forceinline__ uint32_t voff(int j, uint32_t rs) const {
+    return kCompact ? elems((vo[j >> 1] >> (16 * (j & 1))) & 0xffffu, rs) : vo[j];
   }
 };
 
-template <int D, class Smem, int kWaves>
+// Full form: every offset is clamped into a register of its own before the burst (an
+// instruction that overwrites the address register of a fill still waiting for the
+// memory pipeline stalls until that fill has read it, so a burst that reuses one
+// register would be serialised).  Compact form: each fill's address is formed as it
+// is issued.
+template <int D, class Smem, int kWaves, bool kCompact>
 __device__ __forceinline__ void fill_tile(Smem& sm, int buf, const KvTile& t, uint32_t rs, bool doc, int wave,
-                                          int lane, const FillOffs<D, Smem, kWaves>& fo) {
-  using FO = FillOffs<D, Smem, kWaves>;
-  const uint32_t cap = (uint32_t)t.last * rs + D - 8;
+                                          int lane, const FillOffs<D, Smem, kWaves, kCompact>& fo) {
+  using FO = FillOffs<D, Smem, kWaves, kCompact>;
   const uint32_t kl = lds_offset(sm.k[buf]), vl = lds_offset(sm.v[buf]);
+  if constexpr (kCompact) {
+    const uint32_t cap = (uint32_t)t.last * rs + D - 8;  // elements
 #pragma unroll
-  for (int j = 0; j < FO::kKPer; ++j) {
-    const int jj = wave + kWaves * j;
-    if (jj < FO::kKInst) fill16_untracked(t.k + min(FO::offset(fo.kp, j, rs), cap), kl + jj * kWave * 16);
-  }
+    for (int j = 0; j < FO::kKPer; ++j) {
+      const int jj = wave + kWaves * j;
+      if (jj < FO::kKInst) fill16_untracked(t.k + min(fo.koff(j, rs), cap), kl + jj * kWave * 16);
+    }
 #pragma unroll
-  for (int j = 0; j < FO::kVPer; ++j) {
-    const int jj = wave + kWaves * j;
-    if (jj < FO::kVInst) fill16_untracked(t.v + min(FO::offset(fo.vp, j, rs), cap), vl + jj * kWave * 16);
+    for (int j = 0; j < FO::kVPer; ++j) {
+      const int jj = wave + kWaves * j;
+      if (jj < FO::kVInst) fill16_untracked(t.v + min(fo.voff(j, rs), cap), vl + jj * kWave * 16);
+    }
+  } else {
+    __builtin_assume(wave >= 0 && wave < kWaves);
+    const uint32_t cap = ((uint32_t)t.last * rs + D - 8) * 2;  // bytes
+    const bf16* kb = uniform_ptr(t.k);
+    const bf16* vb = uniform_ptr(t.v);
+    uint32_t ko[FO::kKPer], vo[FO::kVPer];
+#pragma unroll
+    for (int j = 0; j < FO::kKPer; ++j) {
+      ko[j] = min(fo.koff(j, rs), cap);
+      asm volatile("" : "+v"(ko[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < FO::kVPer; ++j) {
+      vo[j] = min(fo.voff(j, rs), cap);
+      asm volatile("" : "+v"(vo[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < FO::kKPer; ++j) {
+      const int jj = wave + kWaves * j;
+      if (jj < FO::kKInst) fill16_off(kb, ko[j], kl + jj * kWave * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < FO::kVPer; ++j) {
+      const int jj = wave + kWaves * j;
+      if (jj < FO::kVInst) fill16_off(vb, vo[j], vl + jj * kWave * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < FO::kKPer; ++j) asm volatile("" ::"v"(ko[j]));
+#pragma unroll
+    for (int j = 0; j < FO::kVPer; ++j) asm volatile("" ::"v"(vo[j]));
   }
   if (wave == 0) fill4_untracked(t.pos + min(lane, t.last), lds_offset(sm.kpos[buf]));
   if (wave == 1 && doc) fill4_untracked(t.doc + min(lane, t.last), lds_offset(sm.kdoc[buf]));
