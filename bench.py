@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 CSRC = os.path.join(ROOT, "context_causal_attention_zigzag_amd", "csrc")
 # kernel -> (source files it is built from, counter summary under profiles/)
 # timed call -> the kernel it launches (rocprofv3 names it with its template arguments)
-KERNEL_OF = {"partition": "partition_kernel", "merge": "merge_kernel<true>", "bwd_delta": "bwd_delta_kernel<{d}>",
+KERNEL_OF = {"partition": "partition_kernel", "merge": "merge_kernel<true>",
              "bwd_dkdv": "bwd_dkdv_kernel<{d}, ...>", "tile_fwd": "fwd_bf16_kernel<{d}, ...>",
              "stream_fwd": "fwd_bf16_kernel<{d}, ...>", "bwd_dq": "bwd_dq_kernel<{d}, ...>"}
 TRAFFIC = {"bwd_dkdv": (("bwd.hip", "kv_stream.h", "common.h"), "bwd_dkdv_kernel_{w}_traffic.txt")}
@@ -168,7 +168,7 @@ def main():
     cu_dev = torch.as_tensor(cu, dtype=torch.int32, device=dev) if w.packed else None
     part_mode = C.PART_THD if w.packed else C.PART_ZIGZAG
     n_local = w.seq // w.cp
-    names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+    names = ["partition", "tile_fwd", "merge", "stream_fwd", "bwd_dq", "bwd_dkdv"]
 
     def share_steps(rank, striped=False):
         """Buffers of one rank's share and the function running one step of it."""
@@ -217,12 +217,12 @@ def main():
             mark(3)
             rs.stream_fwd(gran, o_s, l_s, workspace=ws_stream)
             mark(4)
-            C.cpattn_bwd_delta(desc, o_s, g, delta)
+            # the dQ pass forms the per-row values D (rowsum(dO * O)) itself, for the
+            # dK/dV pass too: the backward as cpattn_bwd runs it
+            C.cpattn_bwd_dq_delta(desc, qblk, bsegs, o_s, l_s, g, delta, dq, ws_dq)
             mark(5)
-            C.cpattn_bwd_dq(desc, qblk, bsegs, l_s, delta, g, dq, ws_dq)
-            mark(6)
             C.cpattn_bwd_dkdv(desc, qblk, bsegs, l_s, delta, g, dk, dv)
-            mark(7)
+            mark(6)
             for i, n in enumerate(names):
                 if i in marks and i + 1 in marks:
                     ev[n].append((marks[i], marks[i + 1]))
@@ -267,7 +267,7 @@ def main():
             merge_launches, ng, np_ = merge_launches + 1, 0, 0
         ng, np_ = ng + 1, np_ + n
     launches = {"partition": 1, "tile_fwd": 1 + split_t, "merge": merge_launches, "stream_fwd": 1 + split_s,
-                "bwd_delta": 1, "bwd_dq": 1 + split_q, "bwd_dkdv": 1}
+                "bwd_dq": 1 + split_q, "bwd_dkdv": 1}
     single = [n for n in names if launches[n] == 1]
     dom = max(single, key=lambda n: ms[n])
     ev[dom] = []
@@ -313,7 +313,7 @@ def main():
             st_pairs[rr] = int((inf["rs"].q_idx.cpu().numpy().astype(np.int64) + 1).sum())
             del st, ev_r, inf
         striped_cmp = (st_ms, st_pairs)
-    bwd_ms = ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"]
+    bwd_ms = ms["bwd_dq"] + ms["bwd_dkdv"]
     if w.packed:
         # a row at position p of a document starting at c sees p - c + 1 keys
         pos = rs.q_idx.cpu().numpy().astype(np.int64)
@@ -332,7 +332,6 @@ def main():
     part_bytes = 2 * n_local * (w.hq + 2 * w.hkv) * w.d * elt + 4 * n_local * (1 + w.packed)
     n_parts = [sum(1 for e in edges if e[0] == ch) for ch in rs.q_chunks()]
     merge_bytes = sum(n * (n_local // 2) * w.hq * (w.d * 4 + 4) for n in n_parts) + n_local * w.hq * (w.d * elt + 4)
-    delta_bytes = n_local * w.hq * (2 * w.d * elt + 4)
     # call -> (kernel launches, bound, algorithmic work); the forward calls add a merge
     # launch when their plan splits the KV tiles, the dQ call a sum launch, and the merge
     # call is one grouped launch for the query chunks
@@ -341,8 +340,8 @@ def main():
         "tile_fwd": (launches["tile_fwd"], "mfma", f_fwd),
         "merge": (launches["merge"], "hbm", merge_bytes),
         "stream_fwd": (launches["stream_fwd"], "mfma", f_fwd),
-        "bwd_delta": (launches["bwd_delta"], "hbm", delta_bytes),
-        "bwd_dq": (launches["bwd_dq"], "mfma", 2.0 * unit),  # dQ = dS K; S and dP recomputed, not counted
+        # dQ = dS K, with D formed first; S and dP recomputed, not counted
+        "bwd_dq": (launches["bwd_dq"], "mfma", 2.0 * unit),
         "bwd_dkdv": (launches["bwd_dkdv"], "mfma", 8.0 * unit),  # S, dP, dV = P^T dO, dK = dS^T Q
     }
     per_kernel = {}

@@ -95,6 +95,9 @@ lib.cpattn_bwd_delta.restype = _c_i32
 lib.cpattn_bwd_dq.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
 lib.cpattn_bwd_dq.restype = _c_i32
+lib.cpattn_bwd_dq_delta.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32, _P(cpattn_kv_seg),
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
+lib.cpattn_bwd_dq_delta.restype = _c_i32
 lib.cpattn_bwd_dq_workspace_bytes.argtypes = [_P(cpattn_attn_desc), _P(cpattn_q_block), _c_i32,
                                               _P(cpattn_kv_seg)]
 lib.cpattn_bwd_dq_workspace_bytes.restype = _c_sz
@@ -110,7 +113,7 @@ EXPORTED = ("cpattn_strerror", "cpattn_version", "cpattn_partition", "cpattn_par
             "cpattn_zigzag_edge_visible", "cpattn_tile_fwd",
             "cpattn_tile_fwd_workspace_bytes", "cpattn_merge", "cpattn_merge_groups", "cpattn_stream_fwd",
             "cpattn_stream_fwd_workspace_bytes", "cpattn_bwd", "cpattn_bwd_workspace_bytes",
-            "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
+            "cpattn_bwd_delta", "cpattn_bwd_dq", "cpattn_bwd_dq_delta", "cpattn_bwd_dq_workspace_bytes", "cpattn_bwd_dkdv",
             "cpattn_bwd_noalloc")
 
 
@@ -352,6 +355,16 @@ def cpattn_bwd_dq(desc: cpattn_attn_desc, q: cpattn_q_block, segs, lse, delta, d
     st = lib.cpattn_bwd_dq(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(lse), _ptr(delta),
                            _ptr(dout), _ptr(dq), wp, wb, _stream(stream))
     _check(st, "cpattn_bwd_dq")
+
+
+def cpattn_bwd_dq_delta(desc: cpattn_attn_desc, q: cpattn_q_block, segs, o, lse, dout, delta, dq,
+                        workspace=None, stream=None):
+    """dQ pass that also forms the per-row values D from O and dO and stores them in ``delta``."""
+    sa = (cpattn_kv_seg * max(1, len(segs)))(*segs)
+    wp, wb = _ws_args(workspace)
+    st = lib.cpattn_bwd_dq_delta(ctypes.byref(desc), ctypes.byref(q), len(segs), sa, _ptr(o), _ptr(lse),
+                                 _ptr(dout), _ptr(delta), _ptr(dq), wp, wb, _stream(stream))
+    _check(st, "cpattn_bwd_dq_delta")
 
 
 def cpattn_bwd_dkdv(desc: cpattn_attn_desc, q: cpattn_q_block, segs, lse, delta, dout, dk, dv,

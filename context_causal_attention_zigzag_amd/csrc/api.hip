@@ -483,17 +483,21 @@ int check_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_
 // The dQ pass as one query-major job over the segments; split over KV tiles into the
 // workspace when it holds the plan's partial buffers.  More than kMaxSegs segments run
 // as unsplit launches of kMaxSegs segments, each adding its part to dQ.
+// o not null: the pass forms delta from O and dO and stores it instead of reading it
+// (the first launch of a list of more than kMaxSegs segments; the others read it).
 hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                       const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
-                      float* dq, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      float* dq, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      const void* o = nullptr) {
   if (q->len == 0) return hipSuccess;
+  float* dl = const_cast<float*>(delta);  // written only when o is set
   if (n_segs > kMaxSegs) {
     for (int s0 = 0; s0 < n_segs; s0 += kMaxSegs) {
       FwdArgs f{};
       fill_common(f, desc);
       fill_stream_job(f, q, min(kMaxSegs, n_segs - s0), segs + s0, dq, const_cast<float*>(lse));
       plan_fwd(f, desc->d, CPATTN_BF16, device_cus(), false, 0);
-      const hipError_t e = launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, s0 > 0, stream);
+      const hipError_t e = launch_bwd_dq(f, dout, dl, eff_scale(desc), desc->d, s0 > 0, stream, s0 == 0 ? o : nullptr);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -506,7 +510,7 @@ hipError_t run_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int
   if (need > 0 && (workspace == nullptr || need > workspace_bytes))
     need = plan_fwd(f, desc->d, CPATTN_BF16, cus, false, 0);  // too small: no split
   if (need > 0) assign_fwd_workspace(f, desc->d, workspace);
-  return launch_bwd_dq(f, dout, delta, eff_scale(desc), desc->d, false, stream);
+  return launch_bwd_dq(f, dout, dl, eff_scale(desc), desc->d, false, stream, o);
 }
 
 hipError_t run_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -585,6 +589,18 @@ int cpattn_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t
                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+int cpattn_bwd_dq_delta(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                        const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout,
+                        float* delta, float* dq, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq);
+  if (st != CPATTN_OK) return st;
+  if (q->len > 0 && o == nullptr) return CPATTN_ERR_ARG;
+  if (q->len > 0 && !aligned16(o)) return CPATTN_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CPATTN_ERR_ALIGN;
+  return hip_status(run_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq, workspace, workspace_bytes,
+                               reinterpret_cast<hipStream_t>(stream), o));
+}
+
 int cpattn_bwd_dkdv(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                     const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
                     float* const* dk, float* const* dv, void* stream) {
@@ -617,12 +633,11 @@ int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_
   if ((st = check_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq)) != CPATTN_OK) return st;
   if ((st = check_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv)) != CPATTN_OK) return st;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_bwd_delta(o, dout, delta, q->len * desc->hq, desc->d, hs);
-  if (e == hipSuccess) {
-    char* rest = q->len > 0 ? reinterpret_cast<char*>(workspace) + delta_bytes : nullptr;
-    e = run_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq, rest,
-                   q->len > 0 ? workspace_bytes - delta_bytes : 0, hs);
-  }
+  // the dQ pass forms delta itself (the same bits as the delta pass) and stores it for
+  // the dK/dV pass: two launches instead of three
+  char* rest = q->len > 0 ? reinterpret_cast<char*>(workspace) + delta_bytes : nullptr;
+  hipError_t e = run_bwd_dq(desc, q, n_segs, segs, lse, delta, dout, dq, rest,
+                            q->len > 0 ? workspace_bytes - delta_bytes : 0, hs, o);
   if (e == hipSuccess) e = run_bwd_dkdv(desc, q, n_segs, segs, lse, delta, dout, dk, dv, hs);
   return hip_status(e);
 }

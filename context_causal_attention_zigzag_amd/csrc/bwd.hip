@@ -38,22 +38,31 @@ constexpr int kBQ = 32;    // query rows per dK/dV step
 constexpr int kPosPad = 0x7fffffff;
 
 // ---------------------------------------------------------------------------
+// D_i of one 8-element chunk of a row: O . dO in fp32, one fused multiply-add per
+// element in order.  The delta kernel and the dQ pass that forms D itself share it, and
+// both add a row's chunk values in the same pairs (distance half the chunk count, then
+// halving), so the two give the same bits.
+__device__ __forceinline__ float chunk_dot(const bf16x8& o, const bf16x8& g) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)o[e], (float)g[e], s);
+  return s;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const bf16* __restrict__ o,
                                                               const bf16* __restrict__ dout,
                                                               float* __restrict__ delta, int64_t pairs) {
-  constexpr int kTpp = D / 8;  // threads per (row, head), 8 elements each
+  constexpr int kTpp = D / 8;  // threads per (row, head): chunk c of the row each
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t pair = gid / kTpp;
   const int c = (int)(gid % kTpp);
   float s = 0.0f;
   if (pair < pairs) {
     const int64_t off = pair * D + c * 8;
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + off);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+    s = chunk_dot(*reinterpret_cast<const bf16x8*>(o + off), *reinterpret_cast<const bf16x8*>(dout + off));
   }
+  // chunk c adds chunk c + w, w = kTpp / 2, ..., 1 (thread 0's sum is stored)
 #pragma unroll
   for (int w = kTpp / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, kTpp);
   if (pair < pairs && c == 0) delta[pair] = s;
@@ -70,9 +79,10 @@ using DqSmem = kv::KvSmem<D, D + 24, D + 8>;
 
 struct DqExtra {
   const void* dout;
-  const float* delta;  // [q_len, hq]
+  float* delta;        // [q_len, hq]: read, or written when o is set
   float scale;         // softmax scale (factor of dS)
   int32_t accumulate;  // add to the output instead of overwriting it (unsplit jobs)
+  const void* o;       // forward output: the pass forms D from O and dO (the first split stores it)
 };
 
 // One 64-key tile for one wave of the dQ pass, in four phases over the tile's key
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
     }
   }
 
-  bf16x8 qf[D / 16], of[D / 16];
+  bf16x8 qf[D / 16], of[D / 16], ov[D / 16];
   int qpos = kPosPad, qdoc = 0;
   float lse2 = __builtin_inff(), dl = 0.0f;
   {
@@ -240,9 +250,35 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
       if (mask == kMaskCausalDoc) qdoc = job.doc[myrow];
       const float l = job.lse[(int64_t)myrow * a.hq + head];
       lse2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // a row with no key: P = 0
-      dl = x.delta[(int64_t)myrow * a.hq + head];
+      if (x.o == nullptr) dl = x.delta[(int64_t)myrow * a.hq + head];
+    }
+    // O chunks of the row for forming D (used after the first fill lands, so that their
+    // latency hides behind the set-up instead of holding it up)
+    if (x.o != nullptr) {
+      const bf16* obp = reinterpret_cast<const bf16*>(x.o) + off;
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) ov[ds] = *reinterpret_cast<const bf16x8*>(obp + ds * 16);
     }
   }
+  // D of the row from O and the dO operands held: this lane's chunks are 2 ds + h;
+  // pairs as in the delta kernel (chunk distance D/16, then halving within the lane,
+  // then the other half's sum), so the value equals its bits.  The first split stores
+  // it.  Called at work-group-uniform points (the exchange between halves needs every lane).
+  auto form_delta = [&]() {
+    float p[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) p[ds] = chunk_dot(ov[ds], of[ds]);
+#pragma unroll
+    for (int w = D / 32; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) p[i] = p[i] + p[i + w];
+    const float mine = p[0];
+    const float d = mine + __shfl_xor(mine, 32);
+    if (row_ok) {
+      dl = d;
+      if (split == 0 && (lane >> 5) == 0) x.delta[(int64_t)myrow * a.hq + head] = d;
+    }
+  };
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -262,7 +298,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   if (nsplit == 1) {
     iter_walk_all(it, job);
   } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
-    // nothing in this split: mark its partial empty
+    // nothing in this split: mark its partial empty (the first split still stores D)
+    if (x.o != nullptr) form_delta();
     if (row_ok && (lane >> 5) == 0) flag_dst[(int64_t)myrow * a.hq + head] = neg_inf();
     return;
   }
@@ -273,10 +310,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   fo.init(wave, lane, rstride);
   const bool doc = mask == kMaskCausalDoc;
   TileRef cur = iter_next(it, job, TileRef{-1, 0});
+  if (cur.seg < 0 && x.o != nullptr) form_delta();
   if (cur.seg >= 0) {
     KvTile tc = iter_tile(it, cur, job.seg_begin, kvh, a.hkv, D);
     fill_tile<D, Sm>(sm, 0, tc, rstride, doc, wave, lane, fo);
     fill_barrier();
+    if (x.o != nullptr) form_delta();
     int buf = 0;
     while (true) {
       const TileRef nxt = iter_next(it, job, cur);
@@ -920,8 +959,8 @@ void launch_dq(bool ranked, dim3 grid, dim3 block, hipStream_t stream, const Fwd
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), grid, block, 0, stream, f, x);
 }
 
-hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* delta, float scale, int d,
-                         bool accumulate, hipStream_t stream) {
+hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, float* delta, float scale, int d,
+                         bool accumulate, hipStream_t stream, const void* o) {
   FwdArgs f = args;
   // work-groups as in the forward kernel (wave count chosen by the plan)
   const int nw = f.wg_waves == 8 ? 8 : 4;
@@ -934,7 +973,7 @@ hipError_t launch_bwd_dq(const FwdArgs& args, const void* dout, const float* del
   if (total == 0) return hipSuccess;
   f.total_wgs = total;
   f.padded_wgs = (total + 7) & ~7;
-  const DqExtra x{dout, delta, scale, accumulate ? 1 : 0};
+  const DqExtra x{dout, delta, scale, accumulate ? 1 : 0, o};
   const dim3 grid(f.padded_wgs), block(nw * kWave);
   const bool ranked = kv::ranked_plan(f, qt_rows, f.plan != nullptr ? kv::kMaxPlanTiles : kv::kMaxRankedTiles);
   if (!ranked) f.plan = nullptr;

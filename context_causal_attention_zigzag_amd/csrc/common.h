@@ -321,8 +321,10 @@ hipError_t launch_merge_groups(int n_groups, const int32_t* n_parts, const float
 // (query-major, `dq` holds its job, split plan and partial buffers); dK/dV (key-major).
 hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int64_t pairs, int d,
                             hipStream_t stream);
-hipError_t launch_bwd_dq(const FwdArgs& dq, const void* dout, const float* delta, float scale, int d,
-                         bool accumulate, hipStream_t stream);
+// o not null: the dQ pass forms delta from O and dO itself and stores it (same bits as
+// launch_bwd_delta) instead of reading it.
+hipError_t launch_bwd_dq(const FwdArgs& dq, const void* dout, float* delta, float scale, int d,
+                         bool accumulate, hipStream_t stream, const void* o = nullptr);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t stream);
 // One launch merging the KV splits of every split job of a forward launch.
 hipError_t launch_merge_split_jobs(const FwdArgs& f, int d, int out_dtype, hipStream_t stream,

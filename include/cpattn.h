@@ -343,9 +343,9 @@ size_t cpattn_stream_fwd_workspace_bytes(const cpattn_attn_desc* desc, const cpa
  *  workspace        256-byte aligned device buffer, at least q.len * hq * 4 bytes
  *                   (rounded up to 256); cpattn_bwd_workspace_bytes() bytes enable the
  *                   split dQ pass.  Contents on entry are ignored.
- * Computed as three passes without atomics — the calls below, in this order:
- * cpattn_bwd_delta into the start of the workspace, cpattn_bwd_dq with the rest of
- * the workspace, cpattn_bwd_dkdv.
+ * Computed as two passes without atomics — the calls below, in this order:
+ * cpattn_bwd_dq_delta (which forms the per-row values into the start of the
+ * workspace) with the rest of the workspace, then cpattn_bwd_dkdv.
  * Errors: ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 int cpattn_bwd(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
@@ -367,7 +367,8 @@ size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_b
  * around communication: D once per backward, then per arriving KV segment the
  * dK/dV pass (whose result can go back to the segment's owner at once) and the dQ
  * pass.  Running cpattn_bwd_delta, cpattn_bwd_dq and cpattn_bwd_dkdv over the same
- * arguments gives exactly the outputs of cpattn_bwd.  Same source as cpattn_bwd.
+ * arguments gives exactly the outputs of cpattn_bwd, and so does cpattn_bwd_dq_delta
+ * followed by cpattn_bwd_dkdv.  Same source as cpattn_bwd.
  */
 
 /* cpattn_bwd_delta — D_i = sum_d G_i * O_i per (row, head), the term the softmax
@@ -397,6 +398,18 @@ int cpattn_bwd_delta(const cpattn_attn_desc* desc, int64_t rows, const void* o, 
 int cpattn_bwd_dq(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
                   const cpattn_kv_seg* segs, const float* lse, const float* delta, const void* dout,
                   float* dq, void* workspace, size_t workspace_bytes, void* stream);
+
+/* cpattn_bwd_dq_delta — cpattn_bwd_dq that forms D_i = sum_d G_i * O_i itself from
+ * the forward output and the dO rows it loads anyway, and stores it for
+ * cpattn_bwd_dkdv: the values equal cpattn_bwd_delta's bit for bit (same products,
+ * added in the same pairs), and dq equals what cpattn_bwd_dq gives with them.
+ *  o                device [q.len, hq, d] bf16 forward output (16-byte aligned).
+ *  delta            device fp32 [q.len, hq] output.
+ *  the rest         as for cpattn_bwd_dq (lse, dout, dq, workspace, stream).
+ * Errors: ARG, ALIGN, UNSUPPORTED, HIP. */
+int cpattn_bwd_dq_delta(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,
+                        const cpattn_kv_seg* segs, const void* o, const float* lse, const void* dout,
+                        float* delta, float* dq, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that let cpattn_bwd_dq split (0: no split planned or invalid arguments). */
 size_t cpattn_bwd_dq_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_block* q, int32_t n_segs,

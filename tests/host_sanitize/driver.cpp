@@ -135,6 +135,9 @@ int main() {
              CPATTN_ERR_HIP, CPATTN_OK);
   EXPECT_ANY(cpattn_bwd_dkdv(&d, &q, 70, segs.data(), Ff, Ff, F, outs.data(), outs.data(), nullptr), CPATTN_ERR_HIP,
              CPATTN_OK);
+  EXPECT(cpattn_bwd_dq_delta(&d, &q, 4, segs.data(), nullptr, Ff, F, Ff, Ff, nullptr, 0, nullptr), CPATTN_ERR_ARG);
+  EXPECT_ANY(cpattn_bwd_dq_delta(&d, &q, 70, segs.data(), F, Ff, F, Ff, Ff, nullptr, 0, nullptr), CPATTN_ERR_HIP,
+             CPATTN_OK);
   cpattn_attn_desc wide = {CPATTN_BF16, 64, 8, 128, 0.0f, CPATTN_MASK_CAUSAL};
   cpattn_q_block big = {F, Fi, nullptr, 300000};
   EXPECT(cpattn_bwd_noalloc(&wide, &big, 1, segs.data(), F, Ff, F, Ff, outs.data(), outs.data(), nullptr),

@@ -224,6 +224,17 @@ def test_bwd_pass_calls_validation():
                              1 << 20, None) == C.ERR_ALIGN
     assert lib.cpattn_bwd_dq(ctypes.byref(d), ctypes.byref(qb(0)), 4, s4, None, None, None, None, None, 0,
                              None) == C.OK
+    # dQ forming delta: the forward output is needed (and aligned) when there are rows
+    assert lib.cpattn_bwd_dq_delta(ctypes.byref(d), ctypes.byref(q), 4, s4, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                   None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dq_delta(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE + 8, FAKE, FAKE, FAKE, FAKE, None,
+                                   0, None) == C.ERR_ALIGN
+    assert lib.cpattn_bwd_dq_delta(ctypes.byref(d), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, None, FAKE, None, 0,
+                                   None) == C.ERR_ARG
+    assert lib.cpattn_bwd_dq_delta(ctypes.byref(f32), ctypes.byref(q), 4, s4, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   0, None) == C.ERR_UNSUPPORTED
+    assert lib.cpattn_bwd_dq_delta(ctypes.byref(d), ctypes.byref(qb(0)), 4, s4, None, None, None, None, None, None,
+                                   0, None) == C.OK
     # dK/dV: row limit, output tables, alignment
     p = (ctypes.c_void_p * 4)(*[FAKE] * 4)
     nul = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)

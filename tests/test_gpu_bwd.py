@@ -71,7 +71,8 @@ def test_bwd8k_unsplit_dq_pass(bwd8k):
 
 
 def test_bwd8k_pass_calls_match_combined_call(bwd8k):
-    # delta, dQ and dK/dV as separate calls give exactly what cpattn_bwd gives
+    # delta, dQ and dK/dV as separate calls give exactly what cpattn_bwd gives (which
+    # forms delta inside its dQ pass)
     w, q, k, v, g = bwd8k
     import context_causal_attention_zigzag_amd as C
     rs, rows, gr, dq_c, dk_c, dv_c = run_bwd(q, k, v, g, w.cp, 2)
@@ -93,6 +94,15 @@ def test_bwd8k_pass_calls_match_combined_call(bwd8k):
     assert torch.equal(dq, dq_c)
     for a, b in zip(dk + dv, dk_c + dv_c):
         assert torch.equal(a, b)
+    # the dQ pass that forms D itself, split and unsplit: the same D and dQ bit for bit
+    for wsx in (ws, None):
+        delta2 = torch.full_like(delta, float("nan"))
+        dq2 = torch.empty_like(dq)
+        C.cpattn_bwd_dq_delta(desc, qb, segs, o, lse, gd, delta2, dq2, wsx)
+        dq3 = torch.empty_like(dq)
+        C.cpattn_bwd_dq(desc, qb, segs, lse, delta, gd, dq3, wsx)
+        torch.cuda.synchronize()
+        assert torch.equal(delta2, delta) and torch.equal(dq2, dq3)
 
 
 @pytest.mark.parametrize("seq,cp,hq,hkv,d", [(800, 4, 4, 2, 128), (512, 2, 8, 1, 64), (384, 2, 12, 4, 128)])

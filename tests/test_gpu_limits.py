@@ -53,6 +53,12 @@ def test_many_segments_stream_and_backward(n_segs, dtype):
     say(f"{n_segs} segments backward")
     C.cpattn_bwd(desc, qb, segs, o, lse, g, dq, dk, dv, ws)
     torch.cuda.synchronize()
+    # the first of the dQ launches formed D and left it at the start of the workspace:
+    # the delta pass's values bit for bit
+    delta_ref = torch.empty((seq, hq), dtype=torch.float32, device=DEV)
+    C.cpattn_bwd_delta(desc, o, g, delta_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[:seq * hq * 4].view(torch.float32).view(seq, hq), delta_ref)
     dq_r, dk_r, dv_r = OA.attention_bwd(q, k, v, g.cpu())
     assert_close(dq, dq_r, TOL_BF16, f"{n_segs}-seg dQ")
     dk_all = torch.empty((seq, hkv, d), dtype=torch.float32)
@@ -132,7 +138,12 @@ def test_split_numbering_beyond_one_wave():
     dq = torch.empty((seq // cp, hq, d), dtype=torch.float32, device=DEV)
     say("split numbering over 128 query tiles: dQ")
     C.cpattn_bwd_dq(desc, qblk, segs, lse, delta, g, dq, torch.empty(n_ws, dtype=torch.uint8, device=DEV))
+    # the dQ pass that forms D itself: the same D and dQ bit for bit (d = 64, split)
+    delta2 = torch.full_like(delta, float("nan"))
+    dq2 = torch.empty_like(dq)
+    C.cpattn_bwd_dq_delta(desc, qblk, segs, o, lse, g, delta2, dq2, torch.empty(n_ws, dtype=torch.uint8, device=DEV))
     torch.cuda.synchronize()
+    assert torch.equal(delta2, delta) and torch.equal(dq2, dq)
     local = rs.q_idx.cpu().numpy().astype(np.int64)
     pick = np.unique(np.linspace(0, len(local) - 1, 40).astype(np.int64))
     rows = local[pick]
