@@ -233,6 +233,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   }
 
   bf16x8 qf[D / 16], of[D / 16], ov[D / 16];
+  const bf16* obp = nullptr;  // the row's O (forming D)
   int qpos = kPosPad, qdoc = 0;
   float lse2 = __builtin_inff(), dl = 0.0f;
   {
@@ -252,14 +253,15 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
       lse2 = l == neg_inf() ? __builtin_inff() : l * kLog2e;  // a row with no key: P = 0
       if (x.o == nullptr) dl = x.delta[(int64_t)myrow * a.hq + head];
     }
-    // O chunks of the row for forming D (used after the first fill lands, so that their
-    // latency hides behind the set-up instead of holding it up)
-    if (x.o != nullptr) {
-      const bf16* obp = reinterpret_cast<const bf16*>(x.o) + off;
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) ov[ds] = *reinterpret_cast<const bf16x8*>(obp + ds * 16);
-    }
+    if (x.o != nullptr) obp = reinterpret_cast<const bf16*>(x.o) + off;
   }
+  // the row's O chunks for forming D: loaded beside the first tile fill, whose barrier
+  // waits for them, so that no earlier wait of the set-up (loads complete in issue
+  // order) includes them
+  auto load_o = [&]() {
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) ov[ds] = *reinterpret_cast<const bf16x8*>(obp + ds * 16);
+  };
   // D of the row from O and the dO operands held: this lane's chunks are 2 ds + h;
   // pairs as in the delta kernel (chunk distance D/16, then halving within the lane,
   // then the other half's sum), so the value equals its bits.  The first split stores
@@ -299,7 +301,10 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
     iter_walk_all(it, job);
   } else if (!iter_walk_split(it, job, split * job.tiles_per_split, job.tiles_per_split)) {
     // nothing in this split: mark its partial empty (the first split still stores D)
-    if (x.o != nullptr) form_delta();
+    if (x.o != nullptr && split == 0) {
+      load_o();
+      form_delta();
+    }
     if (row_ok && (lane >> 5) == 0) flag_dst[(int64_t)myrow * a.hq + head] = neg_inf();
     return;
   }
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 8 ? 1 : 2) void bwd_dq_kernel(Fwd
   FillOffs<D, Sm, NW, true> fo;
   fo.init(wave, lane, rstride);
   const bool doc = mask == kMaskCausalDoc;
+  if (x.o != nullptr) load_o();
   TileRef cur = iter_next(it, job, TileRef{-1, 0});
   if (cur.seg < 0 && x.o != nullptr) form_delta();
   if (cur.seg >= 0) {
