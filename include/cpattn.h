@@ -363,7 +363,7 @@ size_t cpattn_bwd_workspace_bytes(const cpattn_attn_desc* desc, const cpattn_q_b
                                   const cpattn_kv_seg* segs);
 
 /*
- * The three passes of cpattn_bwd as separate calls, for callers that schedule them
+ * The passes of cpattn_bwd as separate calls, for callers that schedule them
  * around communication: D once per backward, then per arriving KV segment the
  * dK/dV pass (whose result can go back to the segment's owner at once) and the dQ
  * pass.  Running cpattn_bwd_delta, cpattn_bwd_dq and cpattn_bwd_dkdv over the same
