@@ -558,7 +558,7 @@ size_t plan_fwd(FwdArgs& a, int d, int dtype, int num_cu, bool allow_split, int 
     for (int j = 0; j < a.n_jobs; ++j) n += (int64_t)((a.jobs[j].len + qt_rows - 1) / qt_rows) * (a.hq / hpw);
     return n;
   };
-  if (waves == 0) waves = query_wgs(8) >= num_cu ? 8 : 4;
+  if (waves == 0) waves = query_wgs(8) > num_cu ? 8 : 4;
   a.wg_waves = waves;
   a.plan_tiles = 0;
   a.plan = nullptr;
