@@ -112,10 +112,7 @@ __device__ __forceinline__ int map_rows(const PartArgs& a, int g, int64_t u0, in
 // consecutive destination bytes (and of source bytes within a row).
 constexpr int kPerBlock = kThreads * kVecPerThread;
 
-__global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
-  __shared__ int64_t rows[kPerBlock + 1];
-  const int g = blockIdx.y;
-  if (a.n_gather > 0 && ((a.rope.mask >> g) & 1u)) return;
+__device__ __forceinline__ void plain_gather(const PartArgs& a, int g, int64_t* rows) {
   const int vpr = a.n_gather > 0 ? a.vpr[g] : 1;
   const int64_t nvec = a.local * vpr;
   const int64_t v0 = (int64_t)blockIdx.x * kPerBlock;
@@ -144,6 +141,11 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
     const int64_t v = v0 + threadIdx.x + (int64_t)i * kThreads;
     if (v <= vlast) dst[v] = buf[i];
   }
+}
+
+__global__ __launch_bounds__(kThreads) void partition_kernel(PartArgs a) {
+  __shared__ int64_t rows[kPerBlock + 1];
+  plain_gather(a, blockIdx.y, rows);
 }
 
 // Rotated gather.  A block takes kPerBlock vectors too, as units that hold whole
@@ -243,12 +245,8 @@ __device__ __forceinline__ void rope_block(const PartArgs& a, int g, int64_t u0,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rope_kernel(PartArgs a) {
-  __shared__ int64_t rows[kPerBlock + 1];
-  __shared__ int32_t rpos[kPerBlock + 1];
-  __shared__ float cs[kRopeTab], sn[kRopeTab];
-  const int g = blockIdx.y;
-  if (!((a.rope.mask >> g) & 1u)) return;
+__device__ __forceinline__ void rope_gather(const PartArgs& a, int g, int64_t* rows, int32_t* rpos, float* cs,
+                                            float* sn) {
   const bool half = a.rope.interleaved == 0;
   const int vpr = a.vpr[g];
   const int upr = half ? vpr / 2 : vpr;  // units per row
@@ -283,6 +281,19 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(PartArgs a) {
     else
       rope_block<false, false>(a, g, u0, ulast, t0, upr, rows, cs, sn);
   }
+}
+
+// A gather with rotated tensors: one launch for every tensor, blockIdx.y choosing the
+// tensor and with it the rotated or the plain path (uniform per block).
+__global__ __launch_bounds__(kThreads) void rope_kernel(PartArgs a) {
+  __shared__ int64_t rows[kPerBlock + 1];
+  __shared__ int32_t rpos[kPerBlock + 1];
+  __shared__ float cs[kRopeTab], sn[kRopeTab];
+  const int g = blockIdx.y;
+  if ((a.rope.mask >> g) & 1u)
+    rope_gather(a, g, rows, rpos, cs, sn);
+  else
+    plain_gather(a, g, rows);
 }
 
 }  // namespace
@@ -322,12 +333,12 @@ hipError_t launch_partition(int mode, int64_t total, int cp, int rank, const int
   a.mode = mode;
   if (a.local == 0) return hipSuccess;
   const unsigned gy = n_gather > 0 ? n_gather : 1;
-  if (plain_blocks > 0)
-    hipLaunchKernelGGL(partition_kernel, dim3((unsigned)plain_blocks, gy), dim3(kThreads), 0, stream, a);
   if (rope_blocks > 0) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)rope_blocks, gy), dim3(kThreads), 0, stream, a);
+    // rotated and plain tensors in one launch
+    const int64_t blocks = rope_blocks > plain_blocks ? rope_blocks : plain_blocks;
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)blocks, gy), dim3(kThreads), 0, stream, a);
+  } else if (plain_blocks > 0) {
+    hipLaunchKernelGGL(partition_kernel, dim3((unsigned)plain_blocks, gy), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
