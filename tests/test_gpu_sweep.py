@@ -6,7 +6,13 @@ oracle element by element.  The fixed cases elsewhere pin each feature on its ow
 this one crosses them (a striped share with grouped heads at d = 64, a packed share
 whose documents end inside a tile at cp = 3, ...).  Lengths reach a few thousand
 tokens, so the longer cases take the KV-split plans, and every fourth case is planned
-for two compute units, which gives the forward and dQ launches eight-wave work-groups."""
+for two compute units, which gives the forward and dQ launches eight-wave work-groups.
+
+CPATTN_SWEEP_CASES, CPATTN_SWEEP_SEED and CPATTN_SWEEP_LONG=1 (lengths up to about
+1.75x longer, oracle work per case up to 8e7 pairs) widen the sweep; the defaults
+keep it to seconds."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,11 +25,14 @@ from gpu_common import DEV, TOL_BF16, TOL_F32, TOL_LSE_BF16, assert_close, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
-MAX_PAIRS = 3e7    # local rows x keys x query heads: keeps each oracle pass to seconds
+N_CASES = int(os.environ.get("CPATTN_SWEEP_CASES", "48"))
+SEED = int(os.environ.get("CPATTN_SWEEP_SEED", "20261202"))
+LONG = os.environ.get("CPATTN_SWEEP_LONG", "0") == "1"
+# local rows x keys x query heads: keeps each oracle pass to seconds
+MAX_PAIRS = 8e7 if LONG else 3e7
 
 
-def draw_cases(seed=20261202):
+def draw_cases(seed=SEED):
     rng = np.random.default_rng(seed)
     cases = []
     layouts = ("zigzag", "striped", "packed")
@@ -37,13 +46,13 @@ def draw_cases(seed=20261202):
         dtype = "f32" if i % 6 == 5 else "bf16"
         lengths = None
         if layout == "zigzag":
-            seq = 2 * cp * int(rng.integers(3, 800))
+            seq = 2 * cp * int(rng.integers(3, 1400 if LONG else 800))
         elif layout == "striped":
-            seq = cp * int(rng.integers(5, 1500))
+            seq = cp * int(rng.integers(5, 2600 if LONG else 1500))
         else:
             n_docs = int(rng.integers(1, 9))
             # a zero-length document now and then; otherwise lengths with ragged tails
-            lengths = [2 * cp * (0 if rng.random() < 0.1 else int(rng.integers(1, 300)))
+            lengths = [2 * cp * (0 if rng.random() < 0.1 else int(rng.integers(1, 500 if LONG else 300)))
                        for _ in range(n_docs)]
             seq = sum(lengths)
             if seq == 0:
