@@ -11,10 +11,13 @@ One step = the whole hot path for that share:
 Useful FLOPs count visible (query, key) pairs only: S(S+1)/(2cp) per head for every
 zigzag rank; forward 4*d per pair per head (QK^T and PV), backward 10*d (five
 contractions).  value = useful FLOPs of the step (two forwards + one backward) / time.
-The backward runs as its three calls (delta, dQ, dK/dV) so each is timed on its own.
+The backward runs as its two calls (dQ forming the per-row values D, then dK/dV) so
+each is timed on its own.
 
-Prints one JSON line (rank 0); for the 8K share the other three ranks are timed the
-same way after it and reported as ``per_rank_tflops`` (min and mean over the ranks).
+Prints one JSON line (rank 0).  For the 8K share every rank, on the zigzag and on the
+striped split, is then timed in interleaved rounds after a common warm-up (median of
+three rounds per share), reported as ``per_rank_tflops`` (min and mean over the ranks)
+and ``striped_vs_zigzag``.
 ``--workload s128k`` runs the 128K share instead; ``--workload thd64k`` a packed stream
 of 65536 tokens in documents of lognormal lengths, split per document (zigzag inside
 each document, cp=4, rank 1 by default),
@@ -250,6 +253,22 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
 
+    def interleaved_ms(shares, rounds=3, warm_s=1.0):
+        """GPU ms per step of every share: warm-up passes over all shares (W steps each)
+        for at least ``warm_s`` seconds, then ``rounds`` rounds, each timing K steps of
+        every share in turn (as ``timed_run``); the median of the rounds per share."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            for st in shares.values():
+                for _ in range(max(args.warmup, 1)):
+                    st()
+            torch.cuda.synchronize()
+        got = {key: [] for key in shares}
+        for _ in range(rounds):
+            for key, st in shares.items():
+                got[key].append(timed_run(st, None, warmup=False)[0])
+        return {key: float(np.median(v)) for key, v in got.items()}
+
     step, ev, info = share_steps(r)
     # the per-call breakdown: an event pair around every call (the events cost GPU time
     # of their own, so this loop is not the headline)
@@ -273,19 +292,30 @@ def main():
     ev[dom] = []
     step_ms, wall_ms = timed_run(step, dom, warmup=False)
     dom_ms = mean_ms(ev[dom])
-    # the same step with no event inside the loop, as the other ranks are timed
+    # the same step with no event inside the loop (reported beside the headline)
     plain_ms, _ = timed_run(step, None, warmup=False)
     rs, edges = info["rs"], info["edges"]
-    # the workload's other ranks (every rank of the 8K share) carry the same visible
-    # pairs; each is timed the same way after the headline rank
-    other_ranks = {}
+    # every rank of the 8K share, zigzag and striped (they carry the same or nearly the
+    # same visible pairs), timed in interleaved rounds: all shares are built first, then
+    # warmed up together, so that no share is timed while the GPU clock climbs back from
+    # the idle time of building it (a share timed right after it was built measured
+    # ~6 % slower than the same step timed again later)
+    other_ranks, striped_cmp = {}, None
     if not w.packed and args.rank is None:
+        shares, st_pairs = {("zigzag", r): step}, {}
         for rr in w.ranks:
-            if rr == r:
-                continue
-            st, ev_r, _ = share_steps(rr)
-            other_ranks[rr], _ = timed_run(st)
-            del st, ev_r
+            if rr != r:
+                shares[("zigzag", rr)] = share_steps(rr)[0]
+        if len(w.ranks) == w.cp:
+            for rr in w.ranks:
+                st, _, inf = share_steps(rr, striped=True)
+                shares[("striped", rr)] = st
+                st_pairs[rr] = int((inf["rs"].q_idx.cpu().numpy().astype(np.int64) + 1).sum())
+        share_ms = interleaved_ms(shares)
+        other_ranks = {rr: t for (lay, rr), t in share_ms.items() if lay == "zigzag"}
+        if st_pairs:
+            striped_cmp = ({rr: t for (lay, rr), t in share_ms.items() if lay == "striped"}, st_pairs)
+        del shares
 
     # Rotary embedding fused into the gather (Q and K rotated at the rows' positions, V
     # copied), timed like the plain partition, after the step loop
@@ -302,17 +332,6 @@ def main():
     torch.cuda.synchronize()
     rope_ms = mean_ms(rope_ev)
 
-    # the striped split against the zigzag split on every rank of the 8K share: visible
-    # pairs per rank and the time of the same step
-    striped_cmp = None
-    if not w.packed and args.rank is None and len(w.ranks) == w.cp:
-        st_ms, st_pairs = {}, {}
-        for rr in w.ranks:
-            st, ev_r, inf = share_steps(rr, striped=True)
-            st_ms[rr], _ = timed_run(st)
-            st_pairs[rr] = int((inf["rs"].q_idx.cpu().numpy().astype(np.int64) + 1).sum())
-            del st, ev_r, inf
-        striped_cmp = (st_ms, st_pairs)
     bwd_ms = ms["bwd_dq"] + ms["bwd_dkdv"]
     if w.packed:
         # a row at position p of a document starting at c sees p - c + 1 keys
@@ -371,7 +390,8 @@ def main():
                                "and around the dominant kernel's call",
                    "per_kernel": "a separate loop of K steps with an event pair around every call",
                    "instrumented_ms_per_step": round(inst_ms, 4),
-                   "sum_of_call_intervals_ms": round(inst_step_ms, 4)},
+                   "sum_of_call_intervals_ms": round(inst_step_ms, 4),
+                   "no_event_ms_per_step": round(plain_ms, 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -397,8 +417,7 @@ def main():
     }
     if striped_cmp is not None:
         st_ms, st_pairs = striped_cmp
-        zz_ms = {r: plain_ms}
-        zz_ms.update(other_ranks)
+        zz_ms = dict(other_ranks)
         zz_pairs = pairs
         sp = [st_pairs[x] for x in sorted(st_pairs)]
         out["striped_vs_zigzag"] = {
@@ -408,8 +427,7 @@ def main():
                         "striped": [round(st_ms[x] * 1e3, 2) for x in sorted(st_ms)]},
             "note": "same step (partition, tile + merge, stream, backward) per rank; FLOPs differ by the pairs"}
     if other_ranks:
-        per_rank = {r: round(tflops(step_flops, plain_ms), 3)}
-        per_rank.update({rr: round(tflops(step_flops, t), 3) for rr, t in other_ranks.items()})
+        per_rank = {rr: round(tflops(step_flops, t), 3) for rr, t in other_ranks.items()}
         vals = [per_rank[x] for x in sorted(per_rank)]
         out["per_rank_tflops"] = {"ranks": {str(x): per_rank[x] for x in sorted(per_rank)},
                                   "min": min(vals), "mean": round(sum(vals) / len(vals), 3)}
