@@ -301,7 +301,7 @@ def main():
     # the idle time of building it (a share timed right after it was built measured
     # ~6 % slower than the same step timed again later)
     other_ranks, striped_cmp = {}, None
-    if not w.packed and args.rank is None:
+    if not w.packed and args.rank is None and len(w.ranks) > 1:
         shares, st_pairs = {("zigzag", r): step}, {}
         for rr in w.ranks:
             if rr != r:
